@@ -1,0 +1,238 @@
+"""Plain float64 oracle of the Sparse Delta Memory (SDM) layer forward.
+
+TEST INFRASTRUCTURE. This module is the checker, not the product: only ``tests/``,
+``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg import it. It shares
+no code with the HIP path (``sparse_memory_linear_amd``) and imports nothing from it; the
+only common module is the seeded input generator ``sdm_inputs`` (no method arithmetic).
+
+Sources. "PL" is the paperlayer.ai source-linked summary of arXiv:2607.07386v1,
+*Sparse Delta Memory: Scaling the State of Linear RNNs through Sparsity*; "Atlas" is the
+atlas.scime.ai summary of the same paper. Citations give the page and its section:
+
+* PL §2 Background, "Gated DeltaNet": a gated delta rule reads the value currently stored
+  for a key, subtracts it from the new value, and writes the difference, with a decay gate
+  alpha in (0, 1) and an input gate beta in [0, 1].
+* PL §2 Background, "Product Key Memory": k slots out of N are found with sub-linear work,
+  without forming all N scores.
+* PL §3 Method, "Sparse memory updates" / "Sparse addressing" / "Sparse retrieval": an
+  N-slot table; the gated delta update touches only the W slots selected from the key;
+  R slots selected from the query are read as a weighted sum.
+* PL §3 Method, "Connection to GDN": with N = d_qk, W = R = d_qk and dense key values the
+  update is exactly Gated DeltaNet's.
+* PL §3 Method, "Learned initial state": the table starts from a learned M0.
+* PL §4 Experimental Setup, "SDM Configuration": read and write activations are
+  softmax-normalised.
+* PL App. B, "Gate dynamics": slots that are overwritten can be fully decayed (alpha -> 0).
+* Atlas, "Approach": the W write and R read slots come from product-key top-k selection.
+
+The pages give no equation, listing or worked example. The steps below are the plainest
+reading of that prose; each point the pages leave open is marked READING and is listed,
+with the same labels, in the design notes of the repository.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
+brute force, closed forms and an independent dense Gated DeltaNet; absolute output
+values on realistic inputs have no pin beyond those (the pages print none).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Tuple
+
+import numpy as np
+
+__all__ = [
+    "round_bf16",
+    "round_mem",
+    "decision_f32",
+    "half_scores",
+    "top_order",
+    "product_key_select",
+    "softmax",
+    "address",
+    "recurrence",
+    "forward_unit",
+    "forward",
+    "decode_step_unit",
+]
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+# ----------------------------------------------------------------------------- rounding
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even, directly from
+    float64 (no intermediate float32). bfloat16 keeps 8 significant bits and float32's
+    exponent range; its smallest subnormal is 2**-133."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # x = m * 2**e with 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)              # exponent of one unit in the last place
+    y = np.ldexp(np.rint(np.ldexp(x, -q)), q)  # np.rint: round half to even
+    y = np.where(np.abs(y) > _BF16_MAX, np.copysign(np.inf, x), y)
+    return y
+
+
+def round_mem(x: np.ndarray, mem_dtype: str) -> np.ndarray:
+    """READING R10: the table is stored in its dtype, so every value written to it is
+    rounded (nearest-even) to that dtype when it is written, i.e. after every token.
+    "f64" (no rounding) exists for the closed-form pins only."""
+    if mem_dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    if mem_dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if mem_dtype == "bf16":
+        return round_bf16(x)
+    raise ValueError(mem_dtype)
+
+
+def decision_f32(x: np.ndarray) -> np.ndarray:
+    """Scores on which slot selection is decided: float32, the precision the device takes
+    the same integer decision in (READING R18). Weights still use the float64 scores."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------- addressing
+def half_scores(x: np.ndarray, C1: np.ndarray, C2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Product-key scores of the two halves of x (PL §2 "Product Key Memory"; Atlas
+    "Approach"). x: [..., d_k]; C1, C2: [s, h] with h = d_k/2.
+
+    READING R5: the first half x[:h] is scored against C1 and the second half x[h:]
+    against C2 (plain dot products, no scale: READING R6)."""
+    h = C1.shape[1]
+    x = np.asarray(x, dtype=np.float64)
+    s1 = x[..., :h] @ np.asarray(C1, dtype=np.float64).T
+    s2 = x[..., h:] @ np.asarray(C2, dtype=np.float64).T
+    return s1, s2
+
+
+def top_order(scores: np.ndarray, ids: np.ndarray, count: int) -> np.ndarray:
+    """Positions of the first ``count`` entries of each row ordered by (score descending,
+    id ascending) -- READING R7, the tie rule used at every selection step."""
+    order = np.lexsort((ids, -scores), axis=-1)
+    return order[..., :count]
+
+
+def product_key_select(x: np.ndarray, C1: np.ndarray, C2: np.ndarray, kappa: int, n_sel: int):
+    """Select n_sel slots for each row of x by product keys.
+
+    1. score each half against its sub-key set (``half_scores``);
+    2. keep the top ``kappa`` sub-keys of each half (READING R7 order);
+    3. form the kappa*kappa candidate slots n = i*s + j (READING R5) with score
+       sigma1[i] + sigma2[j];
+    4. keep the first n_sel candidates by (score desc, slot asc).
+
+    Returns (slots [.., n_sel] int64, exact scores [.., n_sel] float64) in rank order.
+    Decisions (steps 2 and 4) compare float32-rounded scores (READING R18)."""
+    x2 = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    s = C1.shape[0]
+    s1, s2 = half_scores(x2, C1, C2)
+    d1, d2 = decision_f32(s1), decision_f32(s2)
+    sub = np.broadcast_to(np.arange(s), d1.shape)
+    I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)   # [T, kappa]
+    I2 = np.take_along_axis(sub, top_order(d2, sub, kappa), axis=-1)
+    T = x2.shape[0]
+    slots = (I1[:, :, None] * s + I2[:, None, :]).reshape(T, kappa * kappa)
+    exact = (np.take_along_axis(s1, I1, -1)[:, :, None] + np.take_along_axis(s2, I2, -1)[:, None, :]).reshape(T, -1)
+    dec = decision_f32(np.take_along_axis(d1, I1, -1)[:, :, None] + np.take_along_axis(d2, I2, -1)[:, None, :])
+    dec = dec.reshape(T, -1)
+    pick = top_order(dec, slots, n_sel)
+    sel = np.take_along_axis(slots, pick, -1)
+    sc = np.take_along_axis(exact, pick, -1)
+    if np.ndim(x) == 1:
+        return sel[0], sc[0]
+    return sel, sc
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis, max-subtracted, temperature 1 (PL §4 "SDM
+    Configuration": normalised read and write activations; READING R6)."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - np.max(z, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def address(x, C1, C2, kappa: int, n_sel: int, block: int = 4096):
+    """(slots, weights, scores) for every row of x: product-key selection followed by a
+    softmax over the selected scores (PL §3 "Sparse addressing", PL §4). Rows are
+    processed in blocks only to bound memory; rows are independent."""
+    x2 = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    outs_i, outs_s = [], []
+    for lo in range(0, x2.shape[0], block):
+        i, sc = product_key_select(x2[lo:lo + block], C1, C2, kappa, n_sel)
+        outs_i.append(i)
+        outs_s.append(sc)
+    idx = np.concatenate(outs_i, 0) if outs_i else np.zeros((0, n_sel), np.int64)
+    sc = np.concatenate(outs_s, 0) if outs_s else np.zeros((0, n_sel))
+    return idx, softmax(sc) if sc.size else sc, sc
+
+
+# ----------------------------------------------------------------------------- recurrence
+def recurrence(M0: np.ndarray, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype: str):
+    """Sparse gated delta write and weighted read, token by token, for one (batch, head).
+
+    For token t with write slots n (weights a) and read slots m (weights u):
+
+    * rho   = alpha_t * sum_j a_j M[n_j]        (READING R2: the read of the write slots
+                                               is decayed, as in Gated DeltaNet, PL §2)
+    * delta = beta_t * (v_t - rho)
+    * M[n_j] <- round(alpha_t * M[n_j] + a_j * delta)   for the W slots only, from the
+      values before this token's write (PL §3 "Sparse memory updates"; READING R1: no
+      other row is decayed; READING R10: rounding to the table dtype)
+    * o_t   = sum_r u_r M[m_r]                  after the write (READING R3; PL §3
+                                               "Sparse retrieval", before the output norm)
+
+    M0: [N, d_v] values of the initial table (PL §3 "Learned initial state").
+    Returns o [T, d_v] float64 and the final table [N, d_v] float64."""
+    M = np.array(M0, dtype=np.float64, copy=True)
+    T = len(widx)
+    d_v = M.shape[1]
+    o = np.zeros((T, d_v))
+    for t in range(T):
+        n = np.asarray(widx[t])
+        a = np.asarray(wgt[t], dtype=np.float64)
+        old = M[n]
+        rho = alpha[t] * (a @ old)
+        delta = beta[t] * (v[t] - rho)
+        M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)
+        m = np.asarray(ridx[t])
+        o[t] = np.asarray(rgt[t], dtype=np.float64) @ M[m]
+    return o, M
+
+
+def forward_unit(q, k, v, alpha, beta, C1, C2, M0, kappa: int, W: int, R: int, mem_dtype: str) -> Dict:
+    """One (batch, head) of the SDM layer forward: addresses from keys (writes) and
+    queries (reads) (PL §3 "Sparse addressing"; READING R4: one sub-key pair per head
+    serves both), then the recurrence from M0. All arguments are float64 values."""
+    widx, wgt, wsc = address(k, C1, C2, kappa, W)
+    ridx, rgt, rsc = address(q, C1, C2, kappa, R)
+    o, M = recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype)
+    return {"o": o, "M": M, "widx": widx, "wgt": wgt, "wscore": wsc, "ridx": ridx, "rgt": rgt, "rscore": rsc}
+
+
+def forward(inputs: Dict[str, np.ndarray], shape, units=None, columns=None) -> Dict:
+    """Run ``forward_unit`` over the (b, h) units of a generated workload (``sdm_inputs``).
+
+    ``units``: optional list of (b, h); ``columns``: optional slice of d_v columns (the
+    columns of the table evolve independently, so a column subset is exact)."""
+    from sdm_inputs import widen
+
+    ind, md = shape.in_dtype, shape.mem_dtype
+    if units is None:
+        units = [(b, h) for b in range(shape.B) for h in range(shape.H)]
+    cols = slice(None) if columns is None else columns
+    out = {}
+    for (b, h) in units:
+        sk = widen(inputs["subkeys"][h], ind)
+        M0 = widen(inputs["M0"][h][:, cols], md)
+        out[(b, h)] = forward_unit(
+            widen(inputs["q"][b, h], ind), widen(inputs["k"][b, h], ind), widen(inputs["v"][b, h][:, cols], ind),
+            inputs["alpha"][b, h].astype(np.float64), inputs["beta"][b, h].astype(np.float64),
+            sk[0], sk[1], M0, shape.kappa, shape.W, shape.R, md)
+    return out
+
+
+def decode_step_unit(M, q, k, v, alpha, beta, C1, C2, kappa: int, W: int, R: int, mem_dtype: str):
+    """One token of one unit on a table M that already holds earlier tokens' writes: the
+    same rule as ``forward_unit`` with T = 1. Returns (o [d_v], new M)."""
+    r = forward_unit(q[None], k[None], v[None], np.array([alpha]), np.array([beta]), C1, C2, M,
+                     kappa, W, R, mem_dtype)
+    return r["o"][0], r["M"], r

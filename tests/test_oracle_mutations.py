@@ -1,0 +1,76 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by at least one pin.
+
+Each mutant is a copy of the oracle's source with one plausible error (a dropped term, a
+wrong sign or index, a transposed operand, a wrong order of steps), loaded as a separate
+module; the real oracle is never modified.
+"""
+import importlib.util
+import os
+import types
+
+import pytest
+
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "sdm_oracle.py")
+
+MUTANTS = {
+    # residual against the undecayed read
+    "raw_residual": ("rho = alpha[t] * (a @ old)", "rho = (a @ old)"),
+    # input gate dropped
+    "no_beta": ("delta = beta[t] * (v[t] - rho)", "delta = (v[t] - rho)"),
+    # sign of the residual flipped
+    "sign_flip": ("delta = beta[t] * (v[t] - rho)", "delta = beta[t] * (rho - v[t])"),
+    # written rows not decayed
+    "no_decay_on_write": ("round_mem(alpha[t] * old + a[:, None] * delta[None, :]", "round_mem(old + a[:, None] * delta[None, :]"),
+    # every row of the table decays, not only the written ones
+    "decay_all_rows": ("        old = M[n]\n", "        old = M[n].copy()\n        M *= alpha[t]\n"),
+    # read taken before the write
+    "read_before_write": (
+        "        M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)\n        m = np.asarray(ridx[t])\n        o[t] = np.asarray(rgt[t], dtype=np.float64) @ M[m]\n",
+        "        m = np.asarray(ridx[t])\n        o[t] = np.asarray(rgt[t], dtype=np.float64) @ M[m]\n        M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)\n"),
+    # halves scored against the wrong sub-key sets
+    "swapped_halves": ("s1 = x[..., :h] @ np.asarray(C1", "s1 = x[..., h:] @ np.asarray(C1"),
+    # slot number transposed
+    "slot_transposed": ("slots = (I1[:, :, None] * s + I2[:, None, :])", "slots = (I1[:, :, None] + I2[:, None, :] * s)"),
+    # ties broken by descending index
+    "tie_desc": ("order = np.lexsort((ids, -scores), axis=-1)", "order = np.lexsort((-ids, -scores), axis=-1)"),
+    # ascending instead of descending scores
+    "min_instead_of_max": ("order = np.lexsort((ids, -scores), axis=-1)", "order = np.lexsort((ids, scores), axis=-1)"),
+    # weights not normalised
+    "unnormalised_weights": ("return e / np.sum(e, axis=-1, keepdims=True)", "return e"),
+    # softmax with a temperature
+    "temperature": ("e = np.exp(z - np.max(z, axis=-1, keepdims=True))", "e = np.exp(0.5 * (z - np.max(z, axis=-1, keepdims=True)))"),
+    # table not rounded to bf16 on write
+    "no_bf16_rounding": ("    if mem_dtype == \"bf16\":\n        return round_bf16(x)", "    if mem_dtype == \"bf16\":\n        return np.asarray(x, dtype=np.float64)"),
+    # bf16 rounding by truncation
+    "bf16_truncate": ("y = np.ldexp(np.rint(np.ldexp(x, -q)), q)", "y = np.ldexp(np.trunc(np.ldexp(x, -q)), q)"),
+    # read weights taken from the write weights
+    "read_uses_write_weights": ("o[t] = np.asarray(rgt[t], dtype=np.float64) @ M[m]", "o[t] = np.asarray(wgt[t], dtype=np.float64)[:len(m)] @ M[m]"),
+    # reads addressed by keys
+    "reads_from_keys": ("ridx, rgt, rsc = address(q, C1, C2, kappa, R)", "ridx, rgt, rsc = address(k, C1, C2, kappa, R)"),
+    # per-half top-k keeps too few sub-keys
+    "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
+}
+
+
+def load_mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = SRC
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = load_mutant(name)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError, FloatingPointError, ZeroDivisionError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"

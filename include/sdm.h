@@ -1,0 +1,148 @@
+/*
+ * sdm.h -- C ABI of the Sparse Delta Memory (SDM) layer forward on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method: a Gated DeltaNet whose dense key-value state is replaced by an N-slot table
+ * per head that starts from a learned M0. For each token, product-key addressing picks W
+ * write slots from the key and R read slots from the query (softmax weights); a gated
+ * delta write updates only the W write slots, and a weighted read of the R read slots
+ * gives the token's output.
+ *
+ * Sources ("PL" = the paperlayer.ai summary of arXiv:2607.07386v1, "Sparse Delta Memory:
+ * Scaling the State of Linear RNNs through Sparsity"; "Atlas" = the atlas.scime.ai
+ * summary of the same paper):
+ *   PL §2 "Gated DeltaNet" and "Product Key Memory"; PL §3 "Sparse memory updates",
+ *   "Sparse addressing", "Sparse retrieval", "Learned initial state"; PL §4 "SDM
+ *   Configuration" (softmax-normalised activations); Atlas "Approach" (product-key top-k).
+ *
+ * Conventions (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer to a contiguous, row-major buffer owned by
+ *     the caller; the library never frees or keeps it. Pointers must be 16-byte aligned.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream). Each call only
+ *     enqueues work on that stream and returns; results are ready when the stream is.
+ *   - Arguments are validated on the host before any HIP call. A failed validation returns
+ *     a negative sdm_status and enqueues nothing, so every argument error can be observed
+ *     without a GPU. Launch failures return SDM_ERR_HIP.
+ *   - Calls keep no state between them; calls on different streams with disjoint outputs
+ *     may run concurrently.
+ *   - Units: a unit is one (batch b, head h) pair; unit u = b*H + h. Units are independent.
+ *
+ * Dtypes: q, k, v and the sub-keys share `in_dtype` (SDM_F32 or SDM_BF16); M0 and the
+ * table share `mem_dtype`. Gates alpha, beta, weights and the output o are float32.
+ */
+#ifndef SDM_H_
+#define SDM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDM_ABI_VERSION 1
+
+typedef enum {
+  SDM_OK = 0,
+  SDM_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned or aliasing buffers   */
+  SDM_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement (see limits) */
+  SDM_ERR_WORKSPACE = -3,   /* workspace missing or smaller than sdm_workspace_bytes()   */
+  SDM_ERR_HIP = -4,         /* a HIP launch or runtime call failed                       */
+  SDM_ERR_INTERNAL = -5
+} sdm_status;
+
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+/* Problem shape. Limits checked by every call:
+ *   B, H >= 1; T >= 1 (T may be 0 only where stated); N = s*s a perfect square with
+ *   4 <= N <= 2^24; d_k even, 2 <= d_k <= 256; 1 <= d_v <= 512 with d_v*sizeof(mem) a
+ *   multiple of 16 bytes; 1 <= kappa <= min(s, 64); 1 <= W, R <= min(kappa*kappa, 64). */
+typedef struct {
+  int32_t B, H, T;      /* batch, heads, tokens in this call                            */
+  int64_t N;            /* slots per head (perfect square; s = sqrt(N) sub-keys/half)   */
+  int32_t d_k, d_v;     /* key/query width (two halves of d_k/2), value width           */
+  int32_t kappa;        /* sub-keys kept per half before the kappa x kappa merge        */
+  int32_t W, R;         /* write slots per token (from k), read slots per token (from q)*/
+  int32_t in_dtype;     /* sdm_dtype of q, k, v, sub-keys                               */
+  int32_t mem_dtype;    /* sdm_dtype of M0 and the table                                */
+} sdm_shape;
+
+/* Human-readable name of a status code (static string). */
+const char* sdm_status_string(int status);
+
+/* SDM_ABI_VERSION of the loaded library. */
+int sdm_abi_version(void);
+
+/* Checks a shape against the limits above without touching any buffer: SDM_OK or the
+ * error code any call would return for it. */
+sdm_status sdm_check_shape(const sdm_shape* shape);
+
+/* Bytes of workspace sdm_forward (and sdm_recurrent) need for this shape: the per-token
+ * slot lists and weights, the token dependency lists and the scheduler's counters. 0 if
+ * the shape is invalid. */
+size_t sdm_workspace_bytes(const sdm_shape* shape);
+
+/* M0 copy-on-init (PL §3 "Learned initial state": the table starts from M0).
+ *   M0 [H, N, d_v] mem_dtype (read); M [B, H, N, d_v] mem_dtype (written): M[b,h] = M0[h]
+ *   bit for bit, for every b. M must not overlap M0. */
+sdm_status sdm_init_from_M0(const sdm_shape* shape, const void* M0, void* M, void* stream);
+
+/* Product-key addressing of every token (PL §2 "Product Key Memory", PL §3 "Sparse
+ * addressing", PL §4 softmax activations, Atlas "Approach").
+ *   x       [B, H, T, d_k] in_dtype: keys (for write slots) or queries (for read slots)
+ *   subkeys [H, 2, s, d_k/2] in_dtype: half p of x is scored against subkeys[h, p]
+ *   n_sel   slots to select per token (W for keys, R for queries), 1..min(kappa^2, 64)
+ *   idx     [B, H, T, n_sel] int32 out: slot n = i*s + j, in rank order
+ *   weight  [B, H, T, n_sel] float32 out: softmax of the selected scores
+ *   score   [B, H, T, n_sel] float32 out, may be NULL: the selected scores
+ * Per half the kappa best sub-keys are kept, the kappa*kappa sums are ranked, and the
+ * first n_sel are returned. Every ranking orders by float32 score descending, then by
+ * index ascending. Scores are float32 sums of exact products (bf16) or float32 products. */
+sdm_status sdm_address(const sdm_shape* shape, const void* x, const void* subkeys, int32_t n_sel,
+                       int32_t* idx, float* weight, float* score, void* stream);
+
+/* The sparse gated-delta recurrence with caller-supplied slots and weights (PL §2 "Gated
+ * DeltaNet", PL §3 "Sparse memory updates" / "Sparse retrieval"). For each unit, tokens
+ * t = 0..T-1 in order:
+ *   rho   = alpha_t * sum_j wgt_j * M[widx_j]
+ *   delta = beta_t * (v_t - rho)
+ *   M[widx_j] = round_mem(alpha_t * M[widx_j] + wgt_j * delta)      (only these W rows)
+ *   o_t   = sum_r rgt_r * M[ridx_r]                                  (after the write)
+ * with float32 arithmetic and one rounding to mem_dtype per written value.
+ *   widx [B,H,T,W] int32, wgt [B,H,T,W] f32, ridx [B,H,T,R] int32, rgt [B,H,T,R] f32
+ *   v [B,H,T,d_v] in_dtype, alpha/beta [B,H,T] f32, M [B,H,N,d_v] in/out, o [B,H,T,d_v] out
+ * The W slots of one token must be distinct. A slot index outside [0, N) is skipped (its
+ * weight contributes nothing and no row is touched) and counted in the workspace's error
+ * word (sdm_workspace_error). ws: at least sdm_workspace_bytes(shape) bytes. */
+sdm_status sdm_recurrent(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                         const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* One SDM layer forward over a [B, H, T] token block: addressing of k (W write slots) and
+ * q (R read slots) followed by the recurrence above, continuing from the table in M (call
+ * sdm_init_from_M0 first for a fresh sequence; calling again with the carried M continues
+ * the sequence).
+ *   q, k [B,H,T,d_k] in_dtype; v [B,H,T,d_v] in_dtype; alpha, beta [B,H,T] f32
+ *   subkeys [H,2,s,d_k/2] in_dtype; M [B,H,N,d_v] mem_dtype in/out; o [B,H,T,d_v] f32 out
+ *   widx_out [B,H,T,W] int32 and ridx_out [B,H,T,R] int32: optional (NULL) copies of the
+ *   selected slots, in rank order.
+ * ws: at least sdm_workspace_bytes(shape) bytes of device memory. */
+sdm_status sdm_forward(const sdm_shape* shape, const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const void* subkeys, void* M, float* o, int32_t* widx_out,
+                       int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step: T must be 1. Same result as sdm_forward with T = 1, fused into one
+ * launch; needs no workspace.
+ *   q, k [B,H,1,d_k]; v [B,H,1,d_v]; alpha, beta [B,H,1]; M in/out; o [B,H,1,d_v] f32. */
+sdm_status sdm_decode_step(const sdm_shape* shape, const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const void* subkeys, void* M, float* o, void* stream);
+
+/* Copies the workspace's error word (number of out-of-range slot indices met by the last
+ * sdm_recurrent on this workspace) to *host_count after synchronising `stream`. */
+sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H_ */

@@ -1,0 +1,167 @@
+"""Python binding of ``libsdm.so``, the MI355X (gfx950) Sparse Delta Memory layer forward.
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels. Tensors are ``torch`` device tensors (contiguous); the call is enqueued on
+``torch.cuda.current_stream()`` unless a stream is given. The names follow the C ABI in
+``include/sdm.h`` (``sdm_init_from_M0`` -> :func:`init_from_M0`, ...).
+
+If ``libsdm.so`` has not been built (``python -m sparse_memory_linear_amd.build``), every
+call raises :class:`SdmLibraryMissing`; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "SDM_F32", "SDM_BF16", "SdmError", "SdmLibraryMissing", "Shape", "lib", "lib_path",
+    "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
+    "forward", "decode_step", "workspace_error", "status_string", "abi_version",
+]
+
+SDM_F32 = 0
+SDM_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libsdm.so")
+
+
+class SdmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+
+
+class SdmLibraryMissing(RuntimeError):
+    pass
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("N", ctypes.c_int64),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("kappa", ctypes.c_int32), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("mem_dtype", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(Shape)
+_SIGS = {
+    "sdm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sdm_abi_version": (ctypes.c_int, []),
+    "sdm_check_shape": (ctypes.c_int, [_SP]),
+    "sdm_workspace_bytes": (ctypes.c_size_t, [_SP]),
+    "sdm_init_from_M0": (ctypes.c_int, [_SP, _P, _P, _P]),
+    "sdm_address": (ctypes.c_int, [_SP, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "sdm_recurrent": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sdm_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sdm_decode_step": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sdm_workspace_error": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P]),
+}
+
+
+def lib():
+    """The loaded ``libsdm.so`` (ctypes CDLL). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise SdmLibraryMissing(
+                f"{lib_path} is not built; run `python -m sparse_memory_linear_amd.build` "
+                "(no fallback implementation exists)")
+        L = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    try:
+        return lib().sdm_status_string(int(code)).decode()
+    except SdmLibraryMissing:
+        return str(code)
+
+
+def abi_version() -> int:
+    return lib().sdm_abi_version()
+
+
+def make_shape(B, H, T, N, d_k, d_v, kappa, W, R, in_dtype=SDM_BF16, mem_dtype=SDM_BF16) -> Shape:
+    def dt(x):
+        if isinstance(x, str):
+            return {"f32": SDM_F32, "bf16": SDM_BF16}[x]
+        return int(x)
+    return Shape(int(B), int(H), int(T), int(N), int(d_k), int(d_v), int(kappa), int(W), int(R), dt(in_dtype),
+                 dt(mem_dtype))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libsdm must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise SdmError(code, where)
+
+
+def check_shape(shape: Shape) -> int:
+    return lib().sdm_check_shape(ctypes.byref(shape))
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return lib().sdm_workspace_bytes(ctypes.byref(shape))
+
+
+def init_from_M0(shape: Shape, M0, M, stream=None):
+    _check(lib().sdm_init_from_M0(ctypes.byref(shape), _ptr(M0), _ptr(M), _stream(stream)), "sdm_init_from_M0")
+
+
+def address(shape: Shape, x, subkeys, n_sel: int, idx, weight, score=None, stream=None):
+    _check(lib().sdm_address(ctypes.byref(shape), _ptr(x), _ptr(subkeys), int(n_sel), _ptr(idx), _ptr(weight),
+                             _ptr(score), _stream(stream)), "sdm_address")
+
+
+def recurrent(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, stream=None):
+    _check(lib().sdm_recurrent(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
+                               _ptr(alpha), _ptr(beta), _ptr(M), _ptr(o), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)), "sdm_recurrent")
+
+
+def forward(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, ws, widx_out=None, ridx_out=None, stream=None):
+    _check(lib().sdm_forward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                             _ptr(subkeys), _ptr(M), _ptr(o), _ptr(widx_out), _ptr(ridx_out), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)), "sdm_forward")
+
+
+def decode_step(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, stream=None):
+    _check(lib().sdm_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(subkeys), _ptr(M), _ptr(o), _stream(stream)), "sdm_decode_step")
+
+
+def workspace_error(ws, stream=None) -> int:
+    out = ctypes.c_int64(0)
+    _check(lib().sdm_workspace_error(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(out), _stream(stream)),
+           "sdm_workspace_error")
+    return out.value

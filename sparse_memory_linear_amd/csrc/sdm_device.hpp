@@ -1,0 +1,170 @@
+// Device helpers shared by the SDM kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16 / float32 values
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ------------------------------------------------------------------ ordered keys
+// Maps float32 to uint32 so that unsigned comparison follows the float order.
+__device__ __forceinline__ uint32_t ordered_u32(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_u32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+// 64-bit rank key: larger key = earlier rank. Orders by score descending, then index
+// ascending (the complement of the index in the low word). Key 0 marks "no element".
+__device__ __forceinline__ uint64_t rank_key(float score, uint32_t index) {
+  return ((uint64_t)ordered_u32(score) << 32) | (uint64_t)(~index);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
+__device__ __forceinline__ float key_score(uint64_t k) { return from_ordered_u32((uint32_t)(k >> 32)); }
+
+// ------------------------------------------------------------------ wave primitives
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = shfl_xor_u32((uint32_t)v, mask);
+  uint32_t hi = shfl_xor_u32((uint32_t)(v >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f32(v, m);
+  return v;
+}
+
+// Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
+__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t key) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t other = shfl_xor_u64(key, j);
+      bool desc_block = (lane & k) == 0;
+      bool lower = (lane & j) == 0;
+      bool take_max = (lower == desc_block);
+      uint64_t mx = key > other ? key : other;
+      uint64_t mn = key > other ? other : key;
+      key = take_max ? mx : mn;
+    }
+  }
+  return key;
+}
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t key) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint32_t other = shfl_xor_u32(key, j);
+      bool desc_block = (lane & k) == 0;
+      bool lower = (lane & j) == 0;
+      bool take_max = (lower == desc_block);
+      uint32_t mx = key > other ? key : other;
+      uint32_t mn = key > other ? other : key;
+      key = take_max ? mx : mn;
+    }
+  }
+  return key;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+// number of set bits of m in lanes below this lane
+__device__ __forceinline__ int mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Exact top-`count` (count <= 64) of E keys per lane (E*64 candidates; key 0 = empty),
+// returned one per lane in rank order: lane i < count holds the i-th largest key, lanes
+// >= count hold 0. `buf` is 64 words of LDS private to the calling wave.
+//
+// Fast path: the count-th largest lane maximum (score word only) is a lower bound of the
+// count-th largest key; if at most 64 keys reach it they are compacted and sorted.
+// Otherwise the keys are extracted one by one (exact, slower).
+template <int E>
+__device__ uint64_t wave_topk(const uint64_t (&keys)[E], int count, uint64_t* buf) {
+  const int lane = lane_id();
+  uint64_t lmax = keys[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) lmax = keys[e] > lmax ? keys[e] : lmax;
+  uint32_t sorted_hi = wave_sort_desc_u32((uint32_t)(lmax >> 32));
+  uint32_t tau = __shfl(sorted_hi, count - 1, kWave);
+  uint64_t masks[E];
+  int total = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bool p = keys[e] != 0 && (uint32_t)(keys[e] >> 32) >= tau;
+    masks[e] = ballot(p);
+    total += popc64(masks[e]);
+  }
+  if (total <= kWave) {
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((masks[e] >> lane) & 1ull) buf[base + mbcnt(masks[e])] = keys[e];
+      base += popc64(masks[e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    uint64_t mine = lane < total ? buf[lane] : 0ull;
+    __builtin_amdgcn_wave_barrier();
+    uint64_t s = wave_sort_desc_u64(mine);
+    return lane < count ? s : 0ull;
+  }
+  // exact slow path: repeated wave-wide maximum extraction
+  uint64_t work[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) work[e] = keys[e];
+  uint64_t out = 0;
+  for (int i = 0; i < count; ++i) {
+    uint64_t m = work[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) m = work[e] > m ? work[e] : m;
+    uint64_t g = wave_max_u64(m);
+    if (lane == i) out = g;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (work[e] == g) work[e] = 0;  // keys are unique (index in the low word)
+  }
+  return out;
+}
+
+}  // namespace sdm

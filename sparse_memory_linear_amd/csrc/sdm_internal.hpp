@@ -1,0 +1,42 @@
+// Host-side declarations shared by the launch wrappers and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sdm.h"
+
+namespace sdm {
+
+inline int64_t isqrt64(int64_t n) {
+  if (n <= 0) return 0;
+  int64_t r = 0;
+  while ((r + 1) * (r + 1) <= n) ++r;
+  return r;
+}
+inline size_t dtype_size(int dt) { return dt == SDM_BF16 ? 2 : 4; }
+
+// Workspace layout of sdm_forward / sdm_recurrent (all offsets 256-byte aligned).
+struct WsLayout {
+  size_t widx, wgt, ridx, rgt;  // per-token slot lists and weights (forward only)
+  size_t err;                   // int64 error counter
+  size_t deps;                  // dependency lists (dataflow scheduler)
+  size_t sched;                 // scheduler counters and done flags
+  size_t total;
+};
+WsLayout workspace_layout(const sdm_shape& S);
+
+hipError_t launch_zero(void* p, size_t n_words, hipStream_t stream);
+size_t address_lds_bytes(int s, int kappa);
+hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys, int n_sel, int32_t* idx,
+                          float* weight, float* score, hipStream_t stream);
+hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t stream);
+hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
+                            void* ws, const WsLayout& L, hipStream_t stream);
+hipError_t launch_decode(const sdm_shape& S, const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const void* subkeys, void* M, float* o, hipStream_t stream);
+size_t decode_lds_bytes(const sdm_shape& S);
+
+}  // namespace sdm

@@ -1,0 +1,90 @@
+// Wave-level product-key selection shared by the addressing and decode kernels.
+//
+// Method (paperlayer.ai summary of arXiv:2607.07386v1, §2 "Product Key Memory"; atlas.scime.ai
+// summary, "Approach"): the best kappa sub-keys of each half are kept, and the best n_sel of
+// the kappa x kappa sums are the token's slots. Every ranking orders by float32 score
+// descending, then by index ascending.
+#pragma once
+
+#include "sdm_device.hpp"
+
+namespace sdm {
+
+// ---------------------------------------------------------------- per-half selection
+// Top-kappa sub-keys of one token-half: lanes < kappa receive (index, score) in rank order.
+template <int E>
+__device__ void select_half(const float* row, int s, int kappa, uint64_t* wbuf, int32_t* out_idx, float* out_sc) {
+  const int lane = lane_id();
+  uint64_t keys[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    int i = lane + kWave * e;
+    keys[e] = i < s ? rank_key(row[i], (uint32_t)i) : 0ull;
+  }
+  uint64_t k = wave_topk<E>(keys, kappa, wbuf);
+  if (lane < kappa) {
+    out_idx[lane] = (int32_t)key_index(k);
+    out_sc[lane] = key_score(k);
+  }
+}
+
+// ---------------------------------------------------------------- merge
+// (a, b) for the p-th pair of the staircase {(a, b): (a+1)(b+1) <= n_sel, a, b < kappa},
+// enumerated row by row.
+__device__ __forceinline__ bool stair_pair(int p, int kappa, int n_sel, int& a, int& b) {
+  for (a = 0; a < kappa; ++a) {
+    int cnt = n_sel / (a + 1);
+    if (cnt > kappa) cnt = kappa;
+    if (cnt <= 0) return false;
+    if (p < cnt) { b = p; return true; }
+    p -= cnt;
+  }
+  return false;
+}
+
+__device__ __forceinline__ uint64_t cand_key(const int32_t* i1, const float* s1, const int32_t* i2, const float* s2,
+                                             int a, int b, int s) {
+  float sc = s1[a] + s2[b];
+  uint32_t slot = (uint32_t)i1[a] * (uint32_t)s + (uint32_t)i2[b];
+  return rank_key(sc, slot);
+}
+
+// Top n_sel of the kappa x kappa candidates for one token: lanes < n_sel get their key.
+template <int EM>
+__device__ uint64_t merge_token(const int32_t* i1, const float* s1, const int32_t* i2, const float* s2, int s,
+                                int kappa, int n_sel, int stair_count, uint64_t* wbuf) {
+  const int lane = lane_id();
+  // 1. exact top n_sel of the staircase pairs (every pair outside it is dominated by at
+  //    least n_sel pairs inside it up to float32 rounding ties, which step 2 catches)
+  uint64_t keys[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    int p = lane + kWave * e, a, b;
+    keys[e] = (p < stair_count && stair_pair(p, kappa, n_sel, a, b)) ? cand_key(i1, s1, i2, s2, a, b, s) : 0ull;
+  }
+  uint64_t top = wave_topk<EM>(keys, n_sel, wbuf);
+  uint64_t tau = __shfl(top, n_sel - 1, kWave);
+  // 2. any pair outside the staircase ranking above the n_sel-th? (float32 rounding ties)
+  bool viol = false;
+  const int all = kappa * kappa;
+  for (int p = lane; p < all; p += kWave) {
+    int a = p / kappa, b = p % kappa;
+    if ((a + 1) * (b + 1) > n_sel && cand_key(i1, s1, i2, s2, a, b, s) > tau) viol = true;
+  }
+  if (ballot(viol) == 0ull) return top;
+  // 3. exact extraction over all kappa^2 pairs, largest first
+  uint64_t out = 0ull, prev = ~0ull;
+  for (int i = 0; i < n_sel; ++i) {
+    uint64_t m = 0ull;
+    for (int p = lane; p < all; p += kWave) {
+      uint64_t k = cand_key(i1, s1, i2, s2, p / kappa, p % kappa, s);
+      if (k < prev && k > m) m = k;
+    }
+    uint64_t g = wave_max_u64(m);
+    if (lane == i) out = g;
+    prev = g;
+  }
+  return out;
+}
+
+}  // namespace sdm

@@ -1,0 +1,145 @@
+"""The C-ABI library on the host: it loads, exports every entry point the header declares,
+and rejects bad arguments before any HIP call (no GPU needed; no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+
+@pytest.fixture(scope="module")
+def sdm():
+    import sparse_memory_linear_amd as S
+    if not os.path.exists(S.lib_path):
+        from sparse_memory_linear_amd import build
+        build.build(verbose=False)
+    return S
+
+
+@pytest.fixture(scope="module")
+def no_gpu():
+    # every call below must fail validation; never hand fake pointers to a real device
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run only where no GPU is visible")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_[A-Za-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(sdm):
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(sdm.lib_path)
+    for n in names:
+        assert hasattr(L, n), f"libsdm.so does not export {n}"
+
+
+def test_abi_version_and_status_strings(sdm):
+    assert sdm.abi_version() == 1
+    assert sdm.status_string(0) == "SDM_OK"
+    assert sdm.status_string(-1) == "SDM_ERR_INVALID_ARG"
+    assert sdm.status_string(-3) == "SDM_ERR_WORKSPACE"
+
+
+def base(**kw):
+    import sparse_memory_linear_amd as S
+    d = dict(B=2, H=2, T=64, N=65536, d_k=128, d_v=128, kappa=16, W=16, R=16, in_dtype=1, mem_dtype=1)
+    d.update(kw)
+    return S.make_shape(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"N": 65535}, -1),          # not a perfect square
+    ({"N": 1}, -1),
+    ({"N": 1024 * 1024}, -2),    # s > 512: outside the kernels' limits
+    ({"d_k": 127}, -1),          # odd key width
+    ({"d_k": 512}, -2),
+    ({"kappa": 0}, -1),
+    ({"kappa": 257}, -1),        # more than s sub-keys
+    ({"kappa": 128}, -2),        # beyond 64
+    ({"W": 0}, -1),
+    ({"W": 257, "kappa": 16}, -1),  # more than kappa^2
+    ({"W": 65, "kappa": 16}, -2),
+    ({"d_v": 3, "mem_dtype": 0}, -2),  # rows must be multiples of 16 bytes
+    ({"in_dtype": 7}, -1),
+    ({"B": 0}, -1),
+    ({"T": 0}, 0),
+])
+def test_check_shape(sdm, kw, code):
+    assert sdm.check_shape(base(**kw)) == code
+
+
+def test_workspace_bytes(sdm):
+    S = base()
+    n = sdm.workspace_bytes(S)
+    tok = 2 * 2 * 64
+    assert n >= tok * (16 + 16) * 8
+    assert sdm.workspace_bytes(base(N=65535)) == 0
+
+
+FAKE = 1 << 40  # 16-byte aligned fake device addresses, never dereferenced
+
+
+def test_null_and_misaligned_pointers(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    assert L.sdm_init_from_M0(sp, None, FAKE, None) == -1
+    assert L.sdm_init_from_M0(sp, FAKE + 4, FAKE + (1 << 36), None) == -1
+    assert L.sdm_address(sp, FAKE, FAKE + 2**30, 16, None, FAKE + 2**31, None, None) == -1
+    assert L.sdm_address(sp, FAKE, FAKE + 2**30, 0, FAKE + 2**32, FAKE + 2**33, None, None) == -1
+    assert L.sdm_address(sp, FAKE, FAKE + 2**30, 300, FAKE + 2**32, FAKE + 2**33, None, None) == -1
+    args = [FAKE + i * (1 << 36) for i in range(9)]
+    args[2] += 8  # misaligned ridx
+    assert L.sdm_recurrent(sp, *args, FAKE + 10 * (1 << 36), 1 << 30, None) == -1
+
+
+def test_workspace_too_small(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    need = sdm.workspace_bytes(S)
+    p = [FAKE + i * (1 << 36) for i in range(12)]
+    assert L.sdm_forward(ctypes.byref(S), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], None, None, p[8], need - 256,
+                         None) == -3
+    assert L.sdm_forward(ctypes.byref(S), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], None, None, None, need,
+                         None) == -3
+    assert L.sdm_recurrent(ctypes.byref(S), *p[:9], p[9], 8, None) == -3
+
+
+def test_overlapping_buffers_rejected(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    # M0 inside M
+    assert L.sdm_init_from_M0(sp, FAKE + 4096, FAKE, None) == -1
+    # o overlapping the table
+    p = [FAKE + i * (1 << 36) for i in range(12)]
+    need = sdm.workspace_bytes(S)
+    assert L.sdm_forward(sp, p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[6] + 1024, None, None, p[8], need, None) == -1
+    # workspace inside the table
+    assert L.sdm_forward(sp, p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], None, None, p[6] + 4096, need, None) == -1
+
+
+def test_decode_requires_single_token(sdm, no_gpu):
+    L = sdm.lib()
+    S = base(T=2)
+    p = [FAKE + i * (1 << 36) for i in range(9)]
+    assert L.sdm_decode_step(ctypes.byref(S), *p, None) == -1
+    S0 = base(T=1)
+    assert L.sdm_decode_step(ctypes.byref(S0), None, *p[1:], None) == -1
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import sparse_memory_linear_amd as S
+    monkeypatch.setattr(S, "lib_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(S, "_lib", None)
+    with pytest.raises(S.SdmLibraryMissing):
+        S.lib()

@@ -1,0 +1,288 @@
+"""Benchmark of the SDM layer forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+copy-on-init of the tables from M0, product-key addressing of the keys (W write slots)
+and queries (R read slots), and the sparse gated-delta recurrence over all tokens. The
+step is issued through the library's C ABI calls in the order sdm_forward issues them
+(init, address k, address q, recurrence), so that the recurrence kernel can be timed on
+its own with HIP events on the stream it runs on.
+
+Prints one JSON line. ``value`` is layer tokens/s (B*T tokens per step) with all inputs
+resident in HBM before timing starts. ``roofline`` describes the recurrence kernel
+(HBM-bound): algorithmic bytes per launch / its average event-timed duration, against
+MI355X's 8 TB/s. ``cpu_baseline`` times the float64 CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sdm_inputs as SI  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "layer_8b_long"
+METRIC = "SDM layer tokens/s on 1 MI355X; gather/scatter HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def recurrence_bytes_per_token_head(sh: SI.Shape) -> int:
+    """Algorithmic HBM bytes of the recurrence per (batch, head, token): W rows gathered and
+    W rows written back, R rows gathered (d_v values each, table dtype), v_t read, o_t
+    written (float32), alpha_t and beta_t read."""
+    mem = 2 if sh.mem_dtype == "bf16" else 4
+    inb = 2 if sh.in_dtype == "bf16" else 4
+    return (2 * sh.W + sh.R) * sh.d_v * mem + sh.d_v * inb + sh.d_v * 4 + 8
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per recurrence launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_recurrence_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def _oracle_unit(args):
+    """Worker: the oracle on one unit over the first T_s tokens (all columns)."""
+    name, b, h, T_s = args
+    import oracle.sdm_oracle as O
+    sh = SI.WORKLOADS[name]
+    inp = _oracle_unit.inp
+    sk = SI.widen(inp["subkeys"][h], sh.in_dtype)
+    t0 = time.perf_counter()
+    O.forward_unit(SI.widen(inp["q"][b, h, :T_s], sh.in_dtype), SI.widen(inp["k"][b, h, :T_s], sh.in_dtype),
+                   SI.widen(inp["v"][b, h, :T_s], sh.in_dtype), inp["alpha"][b, h, :T_s].astype(np.float64),
+                   inp["beta"][b, h, :T_s].astype(np.float64), sk[0], sk[1], SI.widen(inp["M0"][h], sh.mem_dtype),
+                   sh.kappa, sh.W, sh.R, sh.mem_dtype)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(name: str, inp, budget_s: float = 15.0):
+    import multiprocessing as mp
+    sh = SI.WORKLOADS[name]
+    units = [(b, h) for b in range(sh.B) for h in range(sh.H)]
+    ncpu = len(os.sched_getaffinity(0))
+    P = max(1, min(16, ncpu, len(units)))
+    _oracle_unit.inp = inp
+    # calibrate on a short prefix in this process (one unit)
+    T_cal = min(sh.T, 128)
+    dt = _oracle_unit((name, 0, 0, T_cal))
+    per_tok = dt / T_cal
+    T_s = int(max(64, min(sh.T, budget_s / max(per_tok, 1e-9))))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(P) as pool:
+        pool.map(_oracle_unit, [(name, b, h, T_s) for (b, h) in units[:P]])
+    wall = time.perf_counter() - t0
+    token_heads_per_s = P * T_s / wall
+    return {
+        "value": token_heads_per_s / sh.H,
+        "unit": "tokens/s",
+        "cores": P,
+        "kind": "oracle",
+        "sample": f"{P} (batch, head) units x first {T_s} tokens of {name}, float64 numpy oracle "
+                  f"(addressing + recurrence), one process per unit; layer tokens/s = unit-tokens/s / H",
+    }
+
+
+# ----------------------------------------------------------------------------- GPU run
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(SI.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_memory_linear_amd as S
+
+    sh = SI.WORKLOADS[args.workload]
+    if sh.T == 1:
+        return bench_decode(args, sh)
+    log(f"[bench] generating {sh.name} inputs")
+    t0 = time.time()
+    inp = SI.make_inputs(sh)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is touched: the oracle workers are forked from this process
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(sh.name, inp)
+        log(f"[bench] oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} cores")
+
+    def dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    q, k, v = (dev(inp[n], sh.in_dtype) for n in ("q", "k", "v"))
+    subkeys = dev(inp["subkeys"], sh.in_dtype)
+    alpha, beta = dev(inp["alpha"], "f32"), dev(inp["beta"], "f32")
+    M0 = dev(inp["M0"], sh.mem_dtype)
+    mdt = torch.bfloat16 if sh.mem_dtype == "bf16" else torch.float32
+    M = torch.empty((sh.B, sh.H, sh.N, sh.d_v), dtype=mdt, device="cuda")
+    o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+    shape = S.make_shape(sh.B, sh.H, sh.T, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
+    ws = torch.empty(S.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    widx = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.int32, device="cuda")
+    wgt = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.float32, device="cuda")
+    ridx = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.int32, device="cuda")
+    rgt = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        S.init_from_M0(shape, M0, M)
+        S.address(shape, k, subkeys, sh.W, widx, wgt)
+        S.address(shape, q, subkeys, sh.R, ridx, rgt)
+        if ev is not None:
+            ev[0].record(stream)
+        S.recurrent(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    rec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    tokens = sh.B * sh.T
+    value = tokens / (ms_step / 1e3)
+    per_th = recurrence_bytes_per_token_head(sh)
+    launch_bytes = per_th * sh.B * sh.H * sh.T
+    achieved = launch_bytes / (rec_ms / 1e3) / 1e9
+    log(f"[bench] {ms_step:.3f} ms/step, recurrence {rec_ms:.3f} ms, {achieved:.1f} GB/s")
+
+    traffic = traffic_from_profile(sh.name)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.in_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": sh.T, "N": sh.N, "d_k": sh.d_k, "d_v": sh.d_v,
+                   "kappa": sh.kappa, "W": sh.W, "R": sh.R, "in_dtype": sh.in_dtype, "mem_dtype": sh.mem_dtype,
+                   "arith": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "recurrence",
+                     "ms_per_launch": rec_ms, "bytes_per_launch": launch_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, sh):
+    """Decode workload: latency of one fused decode step over B sequences (tables pre-filled
+    by a prefill through the forward), tokens/s = B / step time."""
+    import torch
+    import sparse_memory_linear_amd as S
+
+    log(f"[bench] decode: building {sh.B}x{sh.H} tables")
+    rng_inp = SI.make_inputs(sh)
+
+    def dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    subkeys = dev(rng_inp["subkeys"], sh.in_dtype)
+    M0 = dev(rng_inp["M0"], sh.mem_dtype)
+    mdt = torch.bfloat16 if sh.mem_dtype == "bf16" else torch.float32
+    M = torch.empty((sh.B, sh.H, sh.N, sh.d_v), dtype=mdt, device="cuda")
+    s1 = S.make_shape(sh.B, sh.H, 1, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
+    S.init_from_M0(s1, M0, M)
+    P = sh.prefill
+    sp = S.make_shape(1, sh.H, P, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
+    ws = torch.empty(S.workspace_bytes(sp), dtype=torch.uint8, device="cuda")
+    o_pre = torch.empty((1, sh.H, P, sh.d_v), dtype=torch.float32, device="cuda")
+    for b in range(sh.B):
+        pre = SI.make_prefill(sh, b)
+        t = {n: dev(pre[n], sh.in_dtype if n in ("q", "k", "v") else "f32") for n in ("q", "k", "v", "alpha", "beta")}
+        S.forward(sp, t["q"], t["k"], t["v"], t["alpha"], t["beta"], subkeys, M[b:b + 1], o_pre, ws)
+    torch.cuda.synchronize()
+    q, k, v = (dev(rng_inp[n], sh.in_dtype) for n in ("q", "k", "v"))
+    alpha, beta = dev(rng_inp["alpha"], "f32"), dev(rng_inp["beta"], "f32")
+    o = torch.empty((sh.B, sh.H, 1, sh.d_v), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        S.decode_step(s1, q, k, v, alpha, beta, subkeys, M, o)
+    torch.cuda.synchronize()
+    n = max(args.steps, 100)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(n):
+        S.decode_step(s1, q, k, v, alpha, beta, subkeys, M, o)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / n
+    per_th = recurrence_bytes_per_token_head(sh) + 2 * sh.d_k * 2
+    launch_bytes = per_th * sh.B * sh.H
+    achieved = launch_bytes / (ms / 1e3) / 1e9
+    out = {
+        "metric": METRIC, "value": sh.B / (wall / n), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / n, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": 1, "N": sh.N, "prefill": P},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "decode", "ms_per_launch": ms},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -84,6 +84,11 @@ WsLayout workspace_layout(const sdm_shape& S) {
   L.rgt = o; o = align_up(o + tok * S.R * 4);
   L.deps = o;
   L.sched = o;
+  if (dataflow_supported(S)) {
+    o = align_up(o + dataflow_deps_bytes(S));
+    L.sched = o;
+    o = align_up(o + dataflow_sched_words(S) * 4);
+  }
   L.total = o;
   return L;
 }

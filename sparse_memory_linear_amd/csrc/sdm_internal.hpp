@@ -39,4 +39,11 @@ hipError_t launch_decode(const sdm_shape& S, const void* q, const void* k, const
                          const float* beta, const void* subkeys, void* M, float* o, hipStream_t stream);
 size_t decode_lds_bytes(const sdm_shape& S);
 
+bool dataflow_supported(const sdm_shape& S);
+size_t dataflow_deps_bytes(const sdm_shape& S);
+size_t dataflow_sched_words(const sdm_shape& S);
+hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                           const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
+                           void* ws, const WsLayout& L, hipStream_t stream);
+
 }  // namespace sdm

@@ -202,6 +202,7 @@ hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float
   A.d_v = S.d_v;
   A.N = S.N;
   if (A.U == 0 || A.T == 0) return hipSuccess;
+  if (dataflow_supported(S)) return launch_dataflow(S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, stream);
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
   if (mb && ib) return launch_seq<uint16_t, uint16_t>(A, stream);
   if (mb && !ib) return launch_seq<uint16_t, float>(A, stream);

@@ -105,9 +105,9 @@ __global__ void __launch_bounds__(kThreads) address_kernel(AddrArgs A) {
   const int s = A.s, kappa = A.kappa;
   const int stride = score_stride(s);
   float* sc = (float*)smem;                                     // [32][s+1]
-  int32_t* sel_i = (int32_t*)(sc + kTok * stride);              // [32][2][kappa]
-  float* sel_s = (float*)(sel_i + kTok * 2 * kappa);            // [32][2][kappa]
-  uint64_t* wbuf_all = (uint64_t*)(((uintptr_t)(sel_s + kTok * 2 * kappa) + 15) & ~(uintptr_t)15);
+  float* sel_s = sc + kTok * stride;                             // [32][2][kappa]
+  int16_t* sel_i = (int16_t*)(sel_s + kTok * 2 * kappa);          // [32][2][kappa]
+  uint64_t* wbuf_all = (uint64_t*)(((uintptr_t)(sel_i + kTok * 2 * kappa) + 15) & ~(uintptr_t)15);
   const int head = blockIdx.y;
   const int r0 = blockIdx.x * kTok;
   const int BT = A.B * A.T;
@@ -126,14 +126,14 @@ __global__ void __launch_bounds__(kThreads) address_kernel(AddrArgs A) {
   for (int n = wave; n < kTok; n += 4) {
     const int r = r0 + n;
     if (r >= BT) continue;
-    const int32_t* i1 = sel_i + (n * 2 + 0) * kappa;
-    const int32_t* i2 = sel_i + (n * 2 + 1) * kappa;
+    const int16_t* i1 = sel_i + (n * 2 + 0) * kappa;
+    const int16_t* i2 = sel_i + (n * 2 + 1) * kappa;
     const float* s1 = sel_s + (n * 2 + 0) * kappa;
     const float* s2 = sel_s + (n * 2 + 1) * kappa;
     uint64_t k = merge_token<EM>(i1, s1, i2, s2, s, kappa, A.n_sel, A.stair_count, wbuf);
     float scv = lane < A.n_sel ? key_score(k) : -INFINITY;
     float mx = __shfl(scv, 0, kWave);
-    float e = lane < A.n_sel ? __expf(scv - mx) : 0.f;
+    float e = lane < A.n_sel ? expf(scv - mx) : 0.f;
     float tot = wave_sum_f32(e);
     const int b = r / A.T, t = r % A.T;
     const size_t o = (((size_t)b * A.H + head) * A.T + t) * A.n_sel;
@@ -177,7 +177,7 @@ hipError_t launch_es(const AddrArgs& A, size_t lds, hipStream_t st) {
 }  // namespace
 
 size_t address_lds_bytes(int s, int kappa) {
-  size_t b = (size_t)kTok * score_stride(s) * 4 + (size_t)kTok * 2 * kappa * 8;
+  size_t b = (size_t)kTok * score_stride(s) * 4 + (size_t)kTok * 2 * kappa * 6;
   b = (b + 15) & ~(size_t)15;
   return b + 4 * kWave * 8;
 }

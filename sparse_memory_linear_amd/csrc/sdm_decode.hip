@@ -59,7 +59,7 @@ __host__ __device__ inline DecLds dec_lds(int s, int kappa, int W, int R, int ro
   DecLds L;
   size_t o = 0;
   L.sc = o; o = al16(o + (size_t)4 * (s + 1) * 4);
-  L.sel_i = o; o = al16(o + (size_t)4 * kappa * 4);
+  L.sel_i = o; o = al16(o + (size_t)4 * kappa * 2);
   L.sel_s = o; o = al16(o + (size_t)4 * kappa * 4);
   L.wbuf = o; o = al16(o + (size_t)4 * 64 * 8);
   L.widx = o; o = al16(o + (size_t)W * 4);
@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
   const int rowdw = A.d_v / CPL;
   const DecLds L = dec_lds(s, kappa, W, R, rowdw, CPL);
   float* sc = (float*)(smem + L.sc);
-  int32_t* sel_i = (int32_t*)(smem + L.sel_i);
+  int16_t* sel_i = (int16_t*)(smem + L.sel_i);
   float* sel_s = (float*)(smem + L.sel_s);
   uint64_t* wbuf = (uint64_t*)(smem + L.wbuf);
   int32_t* swidx = (int32_t*)(smem + L.widx);

@@ -44,15 +44,32 @@ __device__ __forceinline__ float key_score(uint64_t k) { return from_ordered_u32
 // ------------------------------------------------------------------ wave primitives
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Exchange with lane ^ mask, for mask a power of two up to 32, without going through LDS
+// addressing: DPP for masks 1, 2, 4 (half-row mirror then quad reversal), 8 (row rotate),
+// ds_swizzle for 16, v_permlane32_swap for 32. `mask` must fold to a constant.
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
-  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+  switch (mask) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    case 4: return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false), 0x1B,
+                                                      0xF, 0xF, false);                // half mirror, quad reverse
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);              // swap 16
+    case 32: {
+      auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return __lane_id() < 32 ? r[1] : r[0];
+    }
+    default: return (uint32_t)__shfl_xor((int)v, mask, kWave);
+  }
 }
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
   uint32_t lo = shfl_xor_u32((uint32_t)v, mask);
   uint32_t hi = shfl_xor_u32((uint32_t)(v >> 32), mask);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ float shfl_xor_f32(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+  return __uint_as_float(shfl_xor_u32(__float_as_uint(v), mask));
+}
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
@@ -126,7 +143,7 @@ __device__ uint64_t wave_topk(const uint64_t (&keys)[E], int count, uint64_t* bu
 #pragma unroll
   for (int e = 1; e < E; ++e) lmax = keys[e] > lmax ? keys[e] : lmax;
   uint32_t sorted_hi = wave_sort_desc_u32((uint32_t)(lmax >> 32));
-  uint32_t tau = __shfl(sorted_hi, count - 1, kWave);
+  uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)sorted_hi, count - 1);
   uint64_t masks[E];
   int total = 0;
 #pragma unroll

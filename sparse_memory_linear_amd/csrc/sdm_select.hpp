@@ -13,7 +13,7 @@ namespace sdm {
 // ---------------------------------------------------------------- per-half selection
 // Top-kappa sub-keys of one token-half: lanes < kappa receive (index, score) in rank order.
 template <int E>
-__device__ void select_half(const float* row, int s, int kappa, uint64_t* wbuf, int32_t* out_idx, float* out_sc) {
+__device__ void select_half(const float* row, int s, int kappa, uint64_t* wbuf, int16_t* out_idx, float* out_sc) {
   const int lane = lane_id();
   uint64_t keys[E];
 #pragma unroll
@@ -23,7 +23,7 @@ __device__ void select_half(const float* row, int s, int kappa, uint64_t* wbuf, 
   }
   uint64_t k = wave_topk<E>(keys, kappa, wbuf);
   if (lane < kappa) {
-    out_idx[lane] = (int32_t)key_index(k);
+    out_idx[lane] = (int16_t)key_index(k);
     out_sc[lane] = key_score(k);
   }
 }
@@ -42,7 +42,7 @@ __device__ __forceinline__ bool stair_pair(int p, int kappa, int n_sel, int& a, 
   return false;
 }
 
-__device__ __forceinline__ uint64_t cand_key(const int32_t* i1, const float* s1, const int32_t* i2, const float* s2,
+__device__ __forceinline__ uint64_t cand_key(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2,
                                              int a, int b, int s) {
   float sc = s1[a] + s2[b];
   uint32_t slot = (uint32_t)i1[a] * (uint32_t)s + (uint32_t)i2[b];
@@ -51,7 +51,7 @@ __device__ __forceinline__ uint64_t cand_key(const int32_t* i1, const float* s1,
 
 // Top n_sel of the kappa x kappa candidates for one token: lanes < n_sel get their key.
 template <int EM>
-__device__ uint64_t merge_token(const int32_t* i1, const float* s1, const int32_t* i2, const float* s2, int s,
+__device__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2, int s,
                                 int kappa, int n_sel, int stair_count, uint64_t* wbuf) {
   const int lane = lane_id();
   // 1. exact top n_sel of the staircase pairs (every pair outside it is dominated by at
@@ -63,14 +63,20 @@ __device__ uint64_t merge_token(const int32_t* i1, const float* s1, const int32_
     keys[e] = (p < stair_count && stair_pair(p, kappa, n_sel, a, b)) ? cand_key(i1, s1, i2, s2, a, b, s) : 0ull;
   }
   uint64_t top = wave_topk<EM>(keys, n_sel, wbuf);
-  uint64_t tau = __shfl(top, n_sel - 1, kWave);
-  // 2. any pair outside the staircase ranking above the n_sel-th? (float32 rounding ties)
+  const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, n_sel - 1);
+  const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), n_sel - 1);
+  const uint64_t tau = ((uint64_t)thi << 32) | tlo;
+  // 2. a pair (a, b) outside the staircase has b >= n_sel/(a+1), so its score is at most that
+  //    of the boundary pair (a, n_sel/(a+1)) of its row. If no boundary pair reaches the
+  //    n_sel-th score, nothing outside the staircase can rank above it (a float32 rounding
+  //    tie would need an equal score); otherwise fall back to the exact extraction.
+  const float tau_score = key_score(tau);
   bool viol = false;
-  const int all = kappa * kappa;
-  for (int p = lane; p < all; p += kWave) {
-    int a = p / kappa, b = p % kappa;
-    if ((a + 1) * (b + 1) > n_sel && cand_key(i1, s1, i2, s2, a, b, s) > tau) viol = true;
+  if (lane < kappa) {
+    const int b = n_sel / (lane + 1);
+    if (b < kappa && s1[lane] + s2[b] >= tau_score) viol = true;
   }
+  const int all = kappa * kappa;
   if (ballot(viol) == 0ull) return top;
   // 3. exact extraction over all kappa^2 pairs, largest first
   uint64_t out = 0ull, prev = ~0ull;

@@ -1,4 +1,4 @@
-// Dataflow execution of the sparse gated-delta recurrence, one workgroup per (unit, column
+// Pipelined execution of the sparse gated-delta recurrence, one workgroup per (unit, column
 // block).
 //
 // Method (paperlayer.ai summary of arXiv:2607.07386v1, §2 "Gated DeltaNet", §3 "Sparse memory
@@ -8,16 +8,29 @@
 // the result:
 //   * every column of the table evolves on its own given the slots and weights, so a unit's
 //     rows are split into P column blocks handled by P independent workgroups;
-//   * two tokens depend on each other only when they share a slot (a later token touching a
-//     slot an earlier one wrote, or writing a slot an earlier one reads); tokens that share
-//     no slot commute exactly.
-// Inside a workgroup, waves claim tokens in order and run them as soon as their conflicting
-// predecessors among the last kWin tokens have published their written rows in an LDS ring;
-// rows written earlier than that come from the table in HBM. The result is bit-identical to
-// processing the tokens one after another.
+//   * two tokens depend on each other only through a slot they share; a token that finds
+//     the latest writer of each of its slots among the last `win` tokens can take the row
+//     from that writer on chip, and every other row from the table once all tokens older
+//     than the window are stored.
 //
-// deps_kernel precomputes, per token: a kWin-bit mask of conflicting earlier tokens, and per
-// slot the most recent writer inside the window (distance, position) -- or none.
+// Inside a workgroup the tokens stream through an LDS ring of S token slots (S = 2 win):
+//   * wave 0 (meta) copies each token's packed slot list, weights, gates and v columns into
+//     the ring with direct-to-LDS loads, up to S - win tokens ahead of the store wave;
+//   * wave 1 (gather) loads the table rows of each token's slots into the ring, many tokens
+//     in flight, once every token older than the window is in the table;
+//   * waves 3.. (compute) take tokens in order; a token runs when its rows are in the ring
+//     and its writers inside the window have published their new rows. It replaces its
+//     write rows in the ring by their new values and leaves its output block there. It never
+//     touches HBM;
+//   * wave 2 (store) writes new rows and outputs to HBM in token order and advances the
+//     watermark of completed stores. Storing in token order keeps writes to one slot in
+//     order and after every earlier read of it.
+// The result is bit-identical to processing the tokens one after another.
+//
+// deps_kernel precomputes, per token and slot position, a packed word: the slot, and the
+// latest writer inside the window (distance, position) if there is one.
+
+#include <algorithm>
 
 #include "sdm_device.hpp"
 #include "sdm_internal.hpp"
@@ -26,128 +39,130 @@ namespace sdm {
 
 namespace {
 
-constexpr int kWin = 32;            // explicit dependency / forwarding window (tokens)
-constexpr int kRing = 2 * kWin;     // LDS ring of the written row blocks of recent tokens
-constexpr int kDepBlk = 64;         // tokens per deps workgroup
-constexpr int kHashBits = 14;       // deps hash table: 16384 entries, (kDepBlk + kWin) * (W + R) used
+constexpr int kDepBlk = 64;        // tokens per deps workgroup
+constexpr int kHashBits = 15;      // deps hash table: 32768 entries, at most (kDepBlk + kMaxWin) * W = 12224 used
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
-constexpr int kWaves = 16;          // waves per workgroup of the recurrence
-// Longest a wave waits (in units of s_sleep 2): about 3 s. When it runs out the workgroup
-// gives up (abort flag), every wave exits, and the workspace error word records it: the
-// result is then invalid, but the kernel always terminates.
+constexpr int kMaxWin = 127;
+// packed slot word: [31] coded | [30:24] distance | [23:18] writer position | [17:0] slot,
+// or [30] alone for a slot outside [0, N)
+constexpr uint32_t kCoded = 0x80000000u;
+constexpr uint32_t kInvalid = 0x40000000u;
+constexpr uint32_t kSlotMask = 0x3FFFFu;
+constexpr int kWaves = 16;         // meta, gather, store, 13 compute waves
+constexpr int kMetaDepth = 16;     // meta batches in flight (3 loads each)
+constexpr int kGatherGroup = 4;    // tokens per gather step
+constexpr int kStoreBatch = 8;     // tokens per store step (watermark granularity)
+constexpr size_t kLdsBudget = 150 * 1024;
+constexpr size_t kDumpBytes = 1024;  // LDS sink of the gather wave's padding loads
+// Longest a wave waits (in units of s_sleep 2, ~53 ns): about 3.5 s. When it runs out the
+// workgroup gives up (abort flag), every wave exits, and the workspace error word records
+// it: the result is then invalid, but the kernel always terminates.
 constexpr long long kSpinBudget = 1ll << 26;
+
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ dependency pass
 struct DepArgs {
   const int32_t* widx;  // [U][T][W]
   const int32_t* ridx;  // [U][T][R]
-  uint32_t* mask;       // [U][T]: bit d-1 set -> token t-d conflicts with t (1 <= d <= kWin)
-  int16_t* code;        // [U][T][W+R]: (d << 7) | j of the latest writer t-d at position j, or -1
-  int T, W, R;
+  uint32_t* pk;         // [U][T][W+R] packed slot words
+  int T, W, R, win;
+  long long N;
 };
 
 __device__ __forceinline__ uint32_t dep_hash(uint32_t slot) { return (slot * 2654435761u) >> (32 - kHashBits); }
 
-// entry = slot << 14 | window offset << 7 | kind << 6 | position (kind 1 = read slot)
+// hash entry = slot << 14 | window offset << 6 | writer position
 __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
   __shared__ uint32_t table[1 << kHashBits];
   const int u = blockIdx.y;
   const int t0 = blockIdx.x * kDepBlk;
-  const int wlo = t0 - kWin > 0 ? t0 - kWin : 0;
+  const int wlo = t0 - A.win > 0 ? t0 - A.win : 0;
   const int whi = t0 + kDepBlk < A.T ? t0 + kDepBlk : A.T;
-  const int ntok = whi - wlo;
-  const int per = A.W + A.R;
+  const int W = A.W, R = A.R, per = W + R;
   for (int i = threadIdx.x; i < (1 << kHashBits); i += 256) table[i] = kEmpty;
   __syncthreads();
-  const int32_t* wi = A.widx + (size_t)u * A.T * A.W;
-  const int32_t* ri = A.ridx + (size_t)u * A.T * A.R;
-  for (int e = threadIdx.x; e < ntok * per; e += 256) {
-    const int k = e / per, p = e % per;
-    const int t = wlo + k;
-    const bool rd = p >= A.W;
-    const int j = rd ? p - A.W : p;
-    const int32_t slot = rd ? ri[(size_t)t * A.R + j] : wi[(size_t)t * A.W + j];
-    if (slot < 0) continue;
-    const uint32_t ent = ((uint32_t)slot << 14) | ((uint32_t)k << 7) | (rd ? 64u : 0u) | (uint32_t)j;
+  const int32_t* wi = A.widx + (size_t)u * A.T * W;
+  const int32_t* ri = A.ridx + (size_t)u * A.T * R;
+  for (int e = threadIdx.x; e < (whi - wlo) * W; e += 256) {
+    const int k = e / W, j = e - k * W;
+    const int32_t slot = wi[(size_t)(wlo + k) * W + j];
+    if (slot < 0 || slot >= A.N) continue;
+    const uint32_t ent = ((uint32_t)slot << 14) | ((uint32_t)k << 6) | (uint32_t)j;
     uint32_t h = dep_hash((uint32_t)slot);
     while (atomicCAS(&table[h], kEmpty, ent) != kEmpty) h = (h + 1) & ((1u << kHashBits) - 1);
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = t0 + wave; t < whi; t += 4) {
-    const int kt = t - wlo;
-    uint32_t m = 0;
-    for (int p = lane; p < per; p += 64) {
-      const bool rd = p >= A.W;
-      const int32_t slot = rd ? ri[(size_t)t * A.R + (p - A.W)] : wi[(size_t)t * A.W + p];
+  uint32_t* out = A.pk + ((size_t)u * A.T + t0) * per;
+  for (int e = threadIdx.x; e < (whi - t0) * per; e += 256) {
+    const int kk = e / per, p = e - kk * per;
+    const int t = t0 + kk, kt = t - wlo;
+    const bool rd = p >= W;
+    const int32_t slot = rd ? ri[(size_t)t * R + (p - W)] : wi[(size_t)t * W + p];
+    uint32_t word = kInvalid;
+    if (slot >= 0 && slot < A.N) {
       int best = -1, bestj = 0;
-      if (slot >= 0) {
-        uint32_t h = dep_hash((uint32_t)slot);
-        while (true) {
-          const uint32_t ent = table[h];
-          if (ent == kEmpty) break;
-          if ((ent >> 14) == (uint32_t)slot) {
-            const int k = (ent >> 7) & 127;
-            const bool erd = (ent >> 6) & 1u;
-            const int d = kt - k;
-            // conflicts: a write slot with any earlier slot use, a read slot with an earlier write
-            if (d >= 1 && d <= kWin && (!rd || !erd)) m |= 1u << (d - 1);
-            // latest writer: earlier token, or this token itself for a read slot
-            if (!erd && d <= kWin && (d >= 1 || (rd && d == 0)) && k > best) {
-              best = k;
-              bestj = ent & 63;
-            }
+      uint32_t h = dep_hash((uint32_t)slot);
+      while (true) {
+        const uint32_t ent = table[h];
+        if (ent == kEmpty) break;
+        if ((ent >> 14) == (uint32_t)slot) {
+          const int k = (ent >> 6) & 255;
+          const int d = kt - k;
+          // latest writer: an earlier token, or this token itself for a read slot
+          if ((rd ? d >= 0 : d >= 1) && d <= A.win && k > best) {
+            best = k;
+            bestj = ent & 63;
           }
-          h = (h + 1) & ((1u << kHashBits) - 1);
         }
+        h = (h + 1) & ((1u << kHashBits) - 1);
       }
-      A.code[((size_t)u * A.T + t) * per + p] = best < 0 ? (int16_t)-1 : (int16_t)(((kt - best) << 7) | bestj);
+      word = (uint32_t)slot;
+      if (best >= 0) word |= kCoded | ((uint32_t)(kt - best) << 24) | ((uint32_t)bestj << 18);
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m |= shfl_xor_u32(m, s);
-    if (lane == 0) A.mask[(size_t)u * A.T + t] = m;
+    out[e] = word;
   }
 }
 
-// ------------------------------------------------------------------ recurrence
-struct CsArgs {
-  const int32_t* widx;
-  const float* wgt;
-  const int32_t* ridx;
-  const float* rgt;
-  const uint32_t* mask;
-  const int16_t* code;
-  const void* v;
-  const float* alpha;
-  const float* beta;
-  void* M;
-  float* o;
+// ------------------------------------------------------------------ recurrence pipeline
+struct PipeArgs {
+  const uint32_t* pk;  // [U][T][E] packed slot words (E = W + R: write slots, then read slots)
+  const float* wgt;    // [U][T][W]
+  const float* rgt;    // [U][T][R]
+  const void* v;       // [U][T][d_v]
+  const float* alpha;  // [U][T]
+  const float* beta;   // [U][T]
+  void* M;             // [U][N][d_v]
+  float* o;            // [U][T][d_v]
   unsigned long long* err;
-  int U, T, W, R, d_v, P;  // P column blocks per unit
+  int U, T, W, R, E, d_v, P;
+  int S, win, tpb, vw, rowbytes;
   long long N;
 };
 
 template <typename MemT>
-struct Word;  // one 32-bit word of a row: 1 float32 or 2 bf16 columns
+struct Pair;  // 8 bytes of a row: 2 float32 or 4 bf16 columns
 template <>
-struct Word<float> {
-  static constexpr int kCols = 1;
-  __device__ static void unpack(uint32_t w, float* x) { x[0] = __uint_as_float(w); }
-  __device__ static uint32_t pack(const float* x) { return __float_as_uint(x[0]); }
-};
-template <>
-struct Word<uint16_t> {
+struct Pair<float> {
   static constexpr int kCols = 2;
-  __device__ static void unpack(uint32_t w, float* x) { x[0] = bf16lo(w); x[1] = bf16hi(w); }
-  __device__ static uint32_t pack(const float* x) { return pack_bf16x2(x[0], x[1]); }
+  __device__ static void unpack(u2 w, float* x) {
+    x[0] = __uint_as_float(w[0]);
+    x[1] = __uint_as_float(w[1]);
+  }
+  __device__ static u2 pack(const float* x) { return u2{__float_as_uint(x[0]), __float_as_uint(x[1])}; }
 };
-
-template <typename InT>
-__device__ __forceinline__ float in_at(const InT* p, size_t i);
 template <>
-__device__ __forceinline__ float in_at<float>(const float* p, size_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float in_at<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+struct Pair<uint16_t> {
+  static constexpr int kCols = 4;
+  __device__ static void unpack(u2 w, float* x) {
+    x[0] = bf16lo(w[0]);
+    x[1] = bf16hi(w[0]);
+    x[2] = bf16lo(w[1]);
+    x[3] = bf16hi(w[1]);
+  }
+  __device__ static u2 pack(const float* x) { return u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}; }
+};
 
 __device__ __forceinline__ int lds_ld(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -155,23 +170,62 @@ __device__ __forceinline__ int lds_ld(const int* p) {
 __device__ __forceinline__ void lds_st(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+__device__ __forceinline__ void acquire_lds() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); }
+__device__ __forceinline__ void release_lds() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local"); }
 
-// Workgroup = kWaves waves serving one (unit, column block). Lane = (row group g, word l):
-// LPR lanes (one 32-bit word each) cover the block's part of a row, G = 64/LPR rows per
-// instruction, NR row instructions per slot list.
-template <typename MemT, typename InT, int LPR, int NR>
-__global__ void __launch_bounds__(kWaves * 64) recurrence_kernel(CsArgs A) {
-  using WT = Word<MemT>;
-  constexpr int CPW = WT::kCols;  // columns per word
-  constexpr int G = 64 / LPR;
+// The meta and gather waves keep direct-to-LDS loads in flight; the compiler would make every
+// LDS access of those waves wait for all of them. Their LDS accesses are therefore written
+// out: reads that wait for themselves only, and writes.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ int dma_wave_read(const int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ void dma_wave_read2(uint32_t a0, uint32_t a1, uint32_t (&v)[2]) {
+  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(v[0]), "=&v"(v[1])
+               : "v"(a0), "v"(a1)
+               : "memory");
+}
+__device__ __forceinline__ void dma_wave_write(int* p, int v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// Buffer load of SZ bytes per lane straight into LDS at dst + lane * SZ (dst wave-uniform).
+template <int SZ>
+__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t off) {
+  if constexpr (SZ == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, off, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Control words at the start of LDS.
+enum { kClaim = 0, kMetaDone = 1, kWm = 2, kStoreIssued = 3, kAbort = 4, kCtrlWords = 16 };
+
+// Workgroup of kWaves waves serving one (unit, column block) of RB bytes per row. Lane
+// layout of row work: LPC = RB/8 lanes (8 bytes each) per row, G = 64/LPC rows per pass;
+// NP passes cover max(W, R) rows, NG passes cover the E = W + R rows gathered per token.
+template <typename MemT, typename InT, int RB, int NP, int NG>
+__global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
+  using PT = Pair<MemT>;
+  constexpr int CPL = PT::kCols;              // columns per lane
+  constexpr int LPC = RB / 8;
+  constexpr int G = 64 / LPC;
+  constexpr int CPR = RB / (int)sizeof(MemT);  // columns per row block
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int fwd_tok[kRing];   // token whose written rows sit in ring slot i
-  __shared__ int done_tok[kRing];  // token whose table stores are complete
-  __shared__ int claim, wm, abort_wg;
 
-  const int W = A.W, R = A.R, T = A.T;
-  const int lane = threadIdx.x & 63;
-  const int g = lane / LPR, l = lane % LPR;
+  const int T = A.T, W = A.W, R = A.R, E = A.E, S = A.S, smask = A.S - 1, win = A.win;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane / LPC, l = lane % LPC;
   // XCD-aware placement: all column blocks of a unit go to the same XCD (workgroups are
   // dealt to the 8 XCDs round-robin), so they share its L2 for rows and per-token inputs.
   const int xcd = blockIdx.x & 7, kb = blockIdx.x >> 3;
@@ -179,238 +233,484 @@ __global__ void __launch_bounds__(kWaves * 64) recurrence_kernel(CsArgs A) {
   const int cb = kb % A.P;
   if (u >= A.U) return;
 
-  uint32_t* ring = (uint32_t*)smem;  // [kRing][W][LPR] words
-  const int rowdw = A.d_v / CPW;      // words per table row
-  uint32_t* Mu = (uint32_t*)A.M + (size_t)u * (size_t)A.N * rowdw + (size_t)cb * LPR + l;
-  const int col0 = (cb * LPR + l) * CPW;  // first column of this lane
-  const long long N = A.N;
-  const int per = W + R;
+  int* ctrl = (int*)smem;
+  int* g_tok = ctrl + kCtrlWords;  // [S] token whose rows are gathered in ring slot i
+  int* f_tok = g_tok + S;          // [S] token whose new write rows are in slot i
+  int* c_tok = f_tok + S;          // [S] token whose compute is complete in slot i
+  uint32_t* pk_r = (uint32_t*)(c_tok + S);                          // [S][E]
+  float* wt_r = (float*)(pk_r + (size_t)S * E);                     // [S][E]
+  uint32_t* vab_r = (uint32_t*)(wt_r + (size_t)S * E);              // [S][vw]: v columns, alpha, beta
+  unsigned char* rows = (unsigned char*)(vab_r + (size_t)S * A.vw);  // [S][E][RB]
+  float* obuf = (float*)(rows + (size_t)S * E * RB);                // [S][CPR]
+  unsigned char* dump = (unsigned char*)(obuf + (size_t)S * CPR);    // 1 KB sink for padding loads
 
-  for (int i = threadIdx.x; i < kRing; i += blockDim.x) {
-    fwd_tok[i] = -1;
-    done_tok[i] = -1;
-  }
-  if (threadIdx.x == 0) {
-    claim = 0;
-    wm = 0;
-    abort_wg = 0;
-  }
+  for (int i = threadIdx.x; i < kCtrlWords; i += blockDim.x) ctrl[i] = 0;
+  for (int i = threadIdx.x; i < 3 * S; i += blockDim.x) g_tok[i] = -1;
   __syncthreads();
 
-  while (true) {
-    int t = 0;
-    if (lane == 0) t = atomicAdd(&claim, 1);
-    t = __shfl(t, 0, kWave);
-    if (t >= T || lds_ld(&abort_wg)) break;
-    const size_t ut = (size_t)u * T + t;
-    // ---- per-token inputs
-    int nj[NR], mr[NR], cw[NR], cr[NR];
-    float aj[NR], ur[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int j = i * G + g;
-      nj[i] = j < W ? A.widx[ut * W + j] : -1;
-      aj[i] = j < W ? A.wgt[ut * W + j] : 0.f;
-      cw[i] = j < W ? (int)A.code[ut * per + j] : -1;
-      mr[i] = j < R ? A.ridx[ut * R + j] : -1;
-      ur[i] = j < R ? A.rgt[ut * R + j] : 0.f;
-      cr[i] = j < R ? (int)A.code[ut * per + W + j] : -1;
+  const size_t ut0 = (size_t)u * T;
+  const uint32_t oob = 0x7FFFFFF0u;  // buffer offset past the end: loads give 0, stores are dropped
+  const uint32_t colb = (uint32_t)(cb * RB + l * 8);
+  auto row_ptr = [&](int sl, int e) -> u2* { return (u2*)(rows + ((size_t)sl * E + e) * RB + l * 8); };
+  auto give_up = [&]() {
+    if (lane == 0) {
+      lds_st(&ctrl[kAbort], 1);
+      atomicAdd(A.err, 1ull << 40);
     }
-    const float al = A.alpha[ut], be = A.beta[ut];
-    float vv[CPW];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) vv[c] = in_at<InT>((const InT*)A.v, ut * A.d_v + col0 + c);
-    const uint32_t pm = A.mask[ut];
-    // ---- wait 1: every token up to t-kWin has finished (its ring slot may be reused and
-    //      its table stores are visible), and the conflicting tokens of the window have
-    //      published their written rows
-    {
-      long long budget = kSpinBudget;
-      bool ok = true;
-      while (lds_ld(&wm) < t - kWin + 1) {
-        if (--budget <= 0 || lds_ld(&abort_wg)) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      const bool mine = lane < kWin && ((pm >> lane) & 1u);
-      const int pt = t - 1 - lane;
-      while (ok) {
-        const bool wait = mine && lds_ld(&fwd_tok[pt & (kRing - 1)]) != pt;
-        if (ballot(wait) == 0ull) break;
-        if (--budget <= 0 || lds_ld(&abort_wg)) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      if (!ok) {
-        if (lane == 0) {
-          lds_st(&abort_wg, 1);
-          atomicAdd(A.err, 1ull << 40);
-        }
-        break;
-      }
-    }
-    // no ring or table read may move above the waits
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // ---- gather: rows written inside the window come from the ring, others from the table
-    uint32_t wv[NR], rv[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int j = i * G + g;
-      uint32_t x = 0;
-      if (j < W) {
-        if (cw[i] >= 0) {
-          const int d = cw[i] >> 7, jj = cw[i] & 127;
-          x = ring[(((t - d) & (kRing - 1)) * W + jj) * LPR + l];
-        } else if (nj[i] >= 0 && nj[i] < N) {
-          x = Mu[(size_t)nj[i] * rowdw];
+  };
+
+  if (wave == 0) {
+    // ================================================================ meta wave
+    const int tpb = A.tpb, vw = A.vw, vw2 = A.vw - 2;
+    const int nb = (T + tpb - 1) / tpb;
+    const size_t vrow = (size_t)A.d_v * sizeof(InT) / 4;         // words per token of v
+    const size_t vcol = (size_t)cb * CPR * sizeof(InT) / 4;      // first word of this block
+    int published = 0, s_seen = 0;
+    long long budget = kSpinBudget;
+    for (int b = 0; b < nb; ++b) {
+      const int tb = b * tpb;
+      const int need = tb + tpb - S + win;  // ring slots of this batch are free
+      if (s_seen < need) {
+        s_seen = dma_wave_read(&ctrl[kStoreIssued]);
+        if (s_seen < need) {
+          __builtin_amdgcn_s_waitcnt(0);
+          if (tb > published) {
+            published = tb;
+            dma_wave_write(&ctrl[kMetaDone], published);
+          }
+          while ((s_seen = dma_wave_read(&ctrl[kStoreIssued])) < need) {
+            if (--budget <= 0 || dma_wave_read(&ctrl[kAbort])) {
+              give_up();
+              return;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
         }
       }
-      wv[i] = x;
-      uint32_t y = 0;
-      if (j < R && cr[i] < 0 && mr[i] >= 0 && mr[i] < N) y = Mu[(size_t)mr[i] * rowdw];
-      rv[i] = y;
+      const int sl0 = tb & smask;
+      {
+        const int q = lane * 4, tt = q / E;
+        if (q < tpb * E && tb + tt < T)
+          __builtin_amdgcn_global_load_lds(A.pk + (ut0 + tb) * E + q, (void*)(pk_r + (size_t)sl0 * E), 16, 0, 0);
+      }
+      {
+        const int q = lane * 4, tt = q / E, e = q - tt * E;
+        const size_t t = ut0 + tb + tt;
+        const float* src = e < W ? A.wgt + t * W + e : A.rgt + t * R + (e - W);
+        if (q < tpb * E && tb + tt < T)
+          __builtin_amdgcn_global_load_lds(src, (void*)(wt_r + (size_t)sl0 * E), 16, 0, 0);
+      }
+      {
+        const int tt = lane / vw, k = lane - tt * vw;
+        const size_t t = ut0 + tb + tt;
+        const uint32_t* src = k < vw2 ? (const uint32_t*)A.v + t * vrow + vcol + k
+                                      : (const uint32_t*)(k == vw2 ? A.alpha : A.beta) + t;
+        if (lane < tpb * vw && tb + tt < T)
+          __builtin_amdgcn_global_load_lds(src, (void*)(vab_r + (size_t)sl0 * vw), 4, 0, 0);
+      }
+      if (b >= kMetaDepth) {
+        // exactly 3 loads per batch: the batch kMetaDepth back is complete
+        wait_vmcnt<3 * kMetaDepth>();
+        const int done = (b - kMetaDepth + 1) * tpb;
+        if (done > published) {
+          published = done;
+          dma_wave_write(&ctrl[kMetaDone], published);
+        }
+      }
     }
-    // ---- decayed weighted read of the write slots
-    float acc[CPW];
+    __builtin_amdgcn_s_waitcnt(0);
+    dma_wave_write(&ctrl[kMetaDone], T);
+    return;
+  }
+
+  if (wave == 1) {
+    // ================================================================ gather wave
+    // Direct-to-LDS loads of the table rows of each token's slots, GB tokens per step and up
+    // to GD steps in flight. Slots with a writer inside the window come from the ring
+    // instead: their loads (and those of slots outside [0, N)) are out of range and give 0.
+    constexpr int GB = kGatherGroup;
+    constexpr int DSZ = RB == 8 ? 4 : 16;           // bytes per lane per load
+    constexpr int LPD = RB / DSZ;                   // lanes per row
+    constexpr int RPI = 64 / LPD;                   // rows per load instruction
+    constexpr int ND = RB == 8 ? 2 * NG : (NG > 1 ? NG / 2 : 1);  // load instructions per token
+    constexpr int GD = 63 / (GB * ND) < 8 ? 63 / (GB * ND) : 8;   // steps in flight
+    static_assert(GD >= 1 && GD * GB * ND <= 63, "vmcnt range");
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)A.M + (size_t)u * (size_t)A.N * A.rowbytes, (short)0, (int)((size_t)A.N * A.rowbytes), 0x00020000);
+    const int nsteps = (T + GB - 1) / GB;
+    const int ld = lane / LPD;                                  // row of this lane within a load
+    const uint32_t lcol = (uint32_t)(cb * RB + (lane % LPD) * DSZ);
+    int m_seen = 0, wm_seen = 0, published = 0;
+    long long budget = kSpinBudget;
+    auto publish_upto = [&](int k) {  // steps < k are complete: publish their tokens
+      for (; published < k; ++published) {
+        const int t = published * GB + lane;
+        if (lane < GB && t < T) dma_wave_write(&g_tok[t & smask], t);
+      }
+    };
+    for (int k = 0; k < nsteps; ++k) {
+      const int t0 = k * GB;
+      const int tl = t0 + GB < T ? t0 + GB : T;
+      if (m_seen < tl || wm_seen < tl - 1 - win) {
+        m_seen = dma_wave_read(&ctrl[kMetaDone]);
+        wm_seen = dma_wave_read(&ctrl[kWm]);
+        if (m_seen < tl || wm_seen < tl - 1 - win) {
+          // blocked: publish everything in flight first, so that nothing waits on this wave
+          __builtin_amdgcn_s_waitcnt(0);
+          publish_upto(k);
+          while (true) {
+            m_seen = dma_wave_read(&ctrl[kMetaDone]);
+            wm_seen = dma_wave_read(&ctrl[kWm]);
+            if (m_seen >= tl && wm_seen >= tl - 1 - win) break;
+            if (--budget <= 0 || dma_wave_read(&ctrl[kAbort])) {
+              give_up();
+              return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+      // packed slot words of this lane's rows, for the GB tokens
+      uint32_t pkv[GB][ND];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) acc[c] = 0.f;
+      for (int tt = 0; tt < GB; ++tt) {
+        const int sl = (t0 + tt) & smask;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      float x[CPW];
-      WT::unpack(wv[i], x);
+        for (int d = 0; d < ND; d += 2) {
+          const int e0 = d * RPI + ld, e1 = (d + 1) * RPI + ld;
+          uint32_t r[2];
+          dma_wave_read2(lds_addr(pk_r + (size_t)sl * E + (e0 < E ? e0 : 0)),
+                         lds_addr(pk_r + (size_t)sl * E + (e1 < E ? e1 : 0)), r);
+          pkv[tt][d] = r[0];
+          if (d + 1 < ND) pkv[tt][d + 1] = r[1];
+        }
+      }
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) acc[c] = fmaf(aj[i], x[c], acc[c]);
+      for (int tt = 0; tt < GB; ++tt) {
+        const int t = t0 + tt;
+        const int sl = t & smask;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int e = d * RPI + ld;
+          const bool live = t < T && d * RPI < E;  // wave-uniform
+          const uint32_t p = pkv[tt][d];
+          const uint32_t off =
+              (!live || e >= E || (p & (kCoded | kInvalid))) ? oob : (p & kSlotMask) * (uint32_t)A.rowbytes + lcol;
+          if (live) {
+            if (e < E)
+              load_lds<DSZ>(rs, rows + ((size_t)sl * E + d * RPI) * RB, off);
+          } else {
+            load_lds<DSZ>(rs, dump, oob);
+          }
+        }
+      }
+      if (k >= GD) {
+        // exactly GB * ND loads per step: step k - GD is complete
+        wait_vmcnt<GD * GB * ND>();
+        publish_upto(k - GD + 1);
+      }
     }
-#pragma unroll
-    for (int s = LPR; s < 64; s <<= 1)
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) acc[c] += shfl_xor_f32(acc[c], s);
-    float dl[CPW];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) dl[c] = be * (vv[c] - al * acc[c]);
-    // ---- gated delta write: new rows into this token's ring slot
-    uint32_t* mine_ring = ring + (size_t)(t & (kRing - 1)) * W * LPR;
-    uint32_t nwv[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int j = i * G + g;
-      float x[CPW], y[CPW];
-      WT::unpack(wv[i], x);
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) y[c] = fmaf(al, x[c], aj[i] * dl[c]);
-      nwv[i] = WT::pack(y);
-      if (j < W) mine_ring[j * LPR + l] = nwv[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 0) lds_st(&fwd_tok[t & (kRing - 1)], t);
-    // ---- the table stores wait for the conflicting tokens' own stores (write after write)
-    {
-      long long budget = kSpinBudget;
-      const bool mine = lane < kWin && ((pm >> lane) & 1u);
-      const int pt = t - 1 - lane;
-      bool ok = true;
+    __builtin_amdgcn_s_waitcnt(0);
+    publish_upto(nsteps);
+    return;
+  }
+
+  if (wave == 2) {
+    // ================================================================ store wave
+    constexpr int SB = kStoreBatch;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)A.M + (size_t)u * (size_t)A.N * A.rowbytes, (short)0, (int)((size_t)A.N * A.rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        A.o + (size_t)u * T * A.d_v, (short)0, (int)((size_t)T * A.d_v * 4), 0x00020000);
+    long long budget = kSpinBudget;
+    for (int t0 = 0; t0 < T; t0 += SB) {
+      bool drained = false;
       while (true) {
-        const bool wait = mine && lds_ld(&done_tok[pt & (kRing - 1)]) != pt;
+        const int t = t0 + lane;
+        const bool wait = lane < SB && t < T && lds_ld(&c_tok[t & smask]) != t;
         if (ballot(wait) == 0ull) break;
-        if (--budget <= 0 || lds_ld(&abort_wg)) {
-          ok = false;
+        if (!drained) {
+          // blocked: let the watermark cover every store issued so far
+          __builtin_amdgcn_s_waitcnt(0);
+          if (lane == 0) lds_st(&ctrl[kWm], t0);
+          drained = true;
+        }
+        if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+          give_up();
+          return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      acquire_lds();
+      u2 val[SB][NP];
+      uint32_t off[SB][NP];
+      float ov[SB][CPL];
+      uint32_t ooff[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int t = t0 + k;
+        const bool tv = t < T;
+        const int sl = t & smask;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int j = i * G + g;
+          const int jc = j < W ? j : W - 1;
+          const uint32_t p = (tv && j < W) ? pk_r[(size_t)sl * E + j] : kInvalid;
+          const bool ok = (p & kCoded) || !(p & kInvalid);
+          val[k][i] = *row_ptr(sl, jc);
+          off[k][i] = ok ? (p & kSlotMask) * (uint32_t)A.rowbytes + colb : oob;
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ov[k][c] = obuf[(size_t)sl * CPR + l * CPL + c];
+        ooff[k] = (tv && g == 0) ? (uint32_t)(((size_t)t * A.d_v + cb * CPR + l * CPL) * 4) : oob;
+      }
+      // exactly SB * (NP + 1) store instructions per batch, so the wait below is exact
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) __builtin_amdgcn_raw_buffer_store_b64(val[k][i], rs, off[k][i], 0, 0);
+        if constexpr (CPL == 4) {
+          u4 o4 = {__float_as_uint(ov[k][0]), __float_as_uint(ov[k][1]), __float_as_uint(ov[k][2]),
+                   __float_as_uint(ov[k][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(o4, ro, ooff[k], 0, 0);
+        } else {
+          u2 o2 = {__float_as_uint(ov[k][0]), __float_as_uint(ov[k][1])};
+          __builtin_amdgcn_raw_buffer_store_b64(o2, ro, ooff[k], 0, 0);
+        }
+      }
+      release_lds();
+      if (lane == 0) lds_st(&ctrl[kStoreIssued], t0 + SB);
+      // the previous batch's stores are complete: every token before t0 is in the table
+      wait_vmcnt<SB * (NP + 1)>();
+      if (lane == 0) lds_st(&ctrl[kWm], t0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) lds_st(&ctrl[kWm], T);
+    return;
+  }
+
+  // ================================================================== compute waves
+  bool aborted = false;
+  while (!aborted) {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(&ctrl[kClaim], 1);
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t >= T) break;
+    const int sl = t & smask;
+    {
+      long long budget = kSpinBudget;
+      while (lds_ld(&g_tok[sl]) != t) {
+        if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+          aborted = true;
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(1);
       }
-      if (!ok) {
-        if (lane == 0) {
-          lds_st(&abort_wg, 1);
-          atomicAdd(A.err, 1ull << 40);
-        }
-        break;
-      }
+      if (aborted) break;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    acquire_lds();
+    const uint32_t* pks = pk_r + (size_t)sl * E;
+    const float* wts = wt_r + (size_t)sl * E;
+    const uint32_t* vab = vab_r + (size_t)sl * A.vw;
+    uint32_t pw[NP], pr[NP];
+    float aw[NP], ur[NP];
+    u2 xw[NP], xr[NP];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NP; ++i) {
       const int j = i * G + g;
-      if (j < W && nj[i] >= 0 && nj[i] < N) Mu[(size_t)nj[i] * rowdw] = nwv[i];
+      pw[i] = j < W ? pks[j] : kInvalid;
+      pr[i] = j < R ? pks[W + j] : kInvalid;
+      aw[i] = j < W ? wts[j] : 0.f;
+      ur[i] = j < R ? wts[W + j] : 0.f;
+      // slots outside [0, N) carry no weight
+      if ((pw[i] & (kCoded | kInvalid)) == kInvalid) aw[i] = 0.f;
+      if ((pr[i] & (kCoded | kInvalid)) == kInvalid) ur[i] = 0.f;
+      xw[i] = *row_ptr(sl, j < W ? j : 0);
+      xr[i] = *row_ptr(sl, W + (j < R ? j : 0));
     }
-    // ---- weighted read of the R slots after the write
-    float ov[CPW];
+    float vv[CPL];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) ov[c] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      uint32_t x = rv[i];
-      if (cr[i] >= 0) {
-        const int d = cr[i] >> 7, jj = cr[i] & 127;
-        x = ring[(((t - d) & (kRing - 1)) * W + jj) * LPR + l];
+    for (int c = 0; c < CPL; ++c) {
+      if constexpr (sizeof(InT) == 2) {
+        const uint32_t w = vab[(l * CPL + c) >> 1];
+        vv[c] = ((l * CPL + c) & 1) ? bf16hi(w) : bf16lo(w);
+      } else {
+        vv[c] = __uint_as_float(vab[l * CPL + c]);
       }
-      float y[CPW];
-      WT::unpack(x, y);
+    }
+    const float al = __uint_as_float(vab[A.vw - 2]);
+    const float be = __uint_as_float(vab[A.vw - 1]);
+    // wait for the writers inside the window to publish their new rows
+    {
+      long long budget = kSpinBudget;
+      while (true) {
+        bool wait = false;
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) ov[c] = fmaf(ur[i], y[c], ov[c]);
+        for (int i = 0; i < NP; ++i) {
+          if (pw[i] & kCoded) {
+            const int d = (pw[i] >> 24) & 127;
+            wait |= lds_ld(&f_tok[(sl - d) & smask]) != t - d;
+          }
+          if (pr[i] & kCoded) {
+            const int d = (pr[i] >> 24) & 127;
+            if (d > 0) wait |= lds_ld(&f_tok[(sl - d) & smask]) != t - d;
+          }
+        }
+        if (ballot(wait) == 0ull) break;
+        if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+          aborted = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (aborted) break;
+    }
+    acquire_lds();
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (pw[i] & kCoded) {
+        const int d = (pw[i] >> 24) & 127, jj = (pw[i] >> 18) & 63;
+        xw[i] = *row_ptr((sl - d) & smask, jj);
+      }
+    }
+    // decayed weighted read of the write slots
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float x[CPL];
+      PT::unpack(xw[i], x);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(aw[i], x[c], acc[c]);
     }
 #pragma unroll
-    for (int s = LPR; s < 64; s <<= 1)
+    for (int s = LPC; s < 64; s <<= 1)
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) ov[c] += shfl_xor_f32(ov[c], s);
+      for (int c = 0; c < CPL; ++c) acc[c] += shfl_xor_f32(acc[c], s);
+    float dl[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dl[c] = be * (vv[c] - al * acc[c]);
+    // gated delta write: new rows replace the write rows of this token's slot
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int j = i * G + g;
+      float x[CPL], y[CPL];
+      PT::unpack(xw[i], x);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], aw[i] * dl[c]);
+      if (j < W) *row_ptr(sl, j) = PT::pack(y);
+    }
+    release_lds();
+    if (lane == 0) lds_st(&f_tok[sl], t);
+    // weighted read of the R slots after the write
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (pr[i] & kCoded) {
+        const int d = (pr[i] >> 24) & 127, jj = (pr[i] >> 18) & 63;
+        xr[i] = *row_ptr((sl - d) & smask, jj);
+      }
+    }
+    float ov[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) ov[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float y[CPL];
+      PT::unpack(xr[i], y);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ov[c] = fmaf(ur[i], y[c], ov[c]);
+    }
+#pragma unroll
+    for (int s = LPC; s < 64; s <<= 1)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ov[c] += shfl_xor_f32(ov[c], s);
     if (g == 0) {
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) A.o[ut * A.d_v + col0 + c] = ov[c];
+      for (int c = 0; c < CPL; ++c) obuf[(size_t)sl * CPR + l * CPL + c] = ov[c];
     }
     // slot indices outside [0, N) were skipped; the first column block counts them
     if (cb == 0) {
       int bad = 0;
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
+      for (int i = 0; i < NP; ++i) {
         const int j = i * G + g;
-        bad += popc64(ballot(l == 0 && j < W && (nj[i] < 0 || nj[i] >= N)));
-        bad += popc64(ballot(l == 0 && j < R && (mr[i] < 0 || mr[i] >= N)));
+        bad += popc64(ballot(l == 0 && j < W && (pw[i] & (kCoded | kInvalid)) == kInvalid));
+        bad += popc64(ballot(l == 0 && j < R && (pr[i] & (kCoded | kInvalid)) == kInvalid));
       }
       if (bad && lane == 0) atomicAdd(A.err, (unsigned long long)bad);
     }
-    // ---- finished: table stores complete, then publish and advance the watermark
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 0) {
-      lds_st(&done_tok[t & (kRing - 1)], t);
-      int w = lds_ld(&wm);
-      while (w < T && lds_ld(&done_tok[w & (kRing - 1)]) == w) {
-        const int seen = atomicCAS(&wm, w, w + 1);
-        w = seen == w ? w + 1 : seen;
-      }
+    release_lds();
+    if (lane == 0) lds_st(&c_tok[sl], t);
+  }
+  if (aborted) give_up();
+}
+
+// ------------------------------------------------------------------ configuration
+struct PipeCfg {
+  int rb, P, S, win, tpb, vw, np, ng;
+  size_t lds;
+};
+
+int pow2_floor(int x) {
+  int p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+// Ring and batch sizes for a block width of rb bytes per row; false if it does not fit.
+bool pipe_fits(const sdm_shape& S, int rb, PipeCfg* c) {
+  const int msz = (int)dtype_size(S.mem_dtype), isz = (int)dtype_size(S.in_dtype);
+  const int rowbytes = S.d_v * msz;
+  if (rowbytes % rb) return false;
+  const int E = S.W + S.R;
+  const int lpc = rb / 8, G = 64 / lpc;
+  const int np = (std::max(S.W, S.R) + G - 1) / G;
+  int ng = (E + G - 1) / G;
+  if (ng == 3) ng = 4;
+  if (np > 2 || ng > 4 || np > ng) return false;
+  const int cpr = rb / msz;
+  if ((cpr * isz) % 4) return false;
+  const int vw = cpr * isz / 4 + 2;
+  if (vw > 64) return false;
+  const int tpb = std::min(pow2_floor(std::max(1, 256 / E)), pow2_floor(64 / vw));
+  const size_t slot = 12 + (size_t)E * 8 + (size_t)vw * 4 + (size_t)E * rb + (size_t)cpr * 4;
+  const size_t fixed = kCtrlWords * 4 + kDumpBytes;
+  int ring = 256;
+  while (ring >= 64 && fixed + ring * slot > kLdsBudget) ring /= 2;
+  if (ring < 64) return false;
+  // progress: a blocked gather step and a meta batch fit between the store wave and the window
+  if (kGatherGroup + kStoreBatch > ring / 2 || kGatherGroup + tpb + kStoreBatch > ring - ring / 2) return false;
+  c->rb = rb;
+  c->P = rowbytes / rb;
+  c->S = ring;
+  c->win = std::min(kMaxWin, ring / 2);
+  c->tpb = tpb;
+  c->vw = vw;
+  c->np = np;
+  c->ng = ng;
+  c->lds = fixed + ring * slot;
+  return true;
+}
+
+// Every workgroup issues about the same number of row requests per token whatever its block
+// width, and one CU serves a bounded rate of them; so pick the width that needs the fewest
+// rounds of workgroups over the CUs, and the narrowest among those (more CUs, longer ring).
+bool pipe_config(const sdm_shape& S, int cus, PipeCfg* out) {
+  bool any = false;
+  long long best = 0;
+  const long long U = (long long)S.B * S.H;
+  for (int rb = 8; rb <= 32; rb *= 2) {
+    PipeCfg c;
+    if (!pipe_fits(S, rb, &c) || c.S < 64) continue;
+    const long long rounds = (U * c.P + cus - 1) / cus;  // one 16-wave workgroup per CU
+    if (!any || rounds < best) {
+      *out = c;
+      best = rounds;
+      any = true;
     }
   }
-}
-
-template <typename MemT, typename InT, int LPR>
-hipError_t cs_launch_nr(const CsArgs& A, int nr, hipStream_t st) {
-  const size_t lds = (size_t)kRing * A.W * LPR * 4;
-  const int groups = (A.U + 7) / 8;
-  dim3 grid(8 * groups * A.P);
-  dim3 block(kWaves * 64);
-  if (nr <= 1) hipLaunchKernelGGL((recurrence_kernel<MemT, InT, LPR, 1>), grid, block, lds, st, A);
-  else if (nr <= 2) hipLaunchKernelGGL((recurrence_kernel<MemT, InT, LPR, 2>), grid, block, lds, st, A);
-  else if (nr <= 4) hipLaunchKernelGGL((recurrence_kernel<MemT, InT, LPR, 4>), grid, block, lds, st, A);
-  else hipLaunchKernelGGL((recurrence_kernel<MemT, InT, LPR, 8>), grid, block, lds, st, A);
-  return hipGetLastError();
-}
-
-template <typename MemT, typename InT>
-hipError_t cs_launch_lpr(const CsArgs& A, int lpr, hipStream_t st) {
-  const int G = 64 / lpr;
-  const int mx = A.W > A.R ? A.W : A.R;
-  const int nr = (mx + G - 1) / G;
-  switch (lpr) {
-    case 2: return cs_launch_nr<MemT, InT, 2>(A, nr, st);
-    case 4: return cs_launch_nr<MemT, InT, 4>(A, nr, st);
-    case 8: return cs_launch_nr<MemT, InT, 8>(A, nr, st);
-    case 16: return cs_launch_nr<MemT, InT, 16>(A, nr, st);
-    default: return hipErrorInvalidValue;
-  }
+  return any;
 }
 
 int device_cus() {
@@ -423,35 +723,43 @@ int device_cus() {
   return cus;
 }
 
-}  // namespace
-
-// Words per column block: split each row into P blocks of LPR 32-bit words (LPR in 2..16),
-// aiming at about one workgroup per CU over all units.
-int dataflow_lanes_per_row(const sdm_shape& S, int cus) {
-  const int rowdw = S.d_v * (int)dtype_size(S.mem_dtype) / 4;
-  const int U = S.B * S.H;
-  int best = -1;
-  for (int lpr = 16; lpr >= 2; lpr >>= 1) {
-    if (rowdw % lpr) continue;
-    const int G = 64 / lpr;
-    const int mx = S.W > S.R ? S.W : S.R;
-    if ((mx + G - 1) / G > 8) continue;
-    if ((size_t)kRing * S.W * lpr * 4 > 64 * 1024) continue;
-    best = lpr;
-    if ((long long)U * (rowdw / lpr) >= cus) break;  // enough workgroups: keep blocks wide
-  }
-  return best;
+template <typename MemT, typename InT, int RB>
+hipError_t pipe_launch_rb(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
+  const int groups = (A.U + 7) / 8;
+  dim3 grid(8 * groups * A.P);
+  dim3 block(kWaves * 64);
+  if (c.np == 1 && c.ng == 1) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 1, 1>), grid, block, c.lds, st, A);
+  else if (c.np == 1 && c.ng == 2) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 1, 2>), grid, block, c.lds, st, A);
+  else if (c.np == 2 && c.ng == 2) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 2, 2>), grid, block, c.lds, st, A);
+  else if (c.np == 2 && c.ng == 4) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 2, 4>), grid, block, c.lds, st, A);
+  else if (c.np == 1 && c.ng == 4) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 1, 4>), grid, block, c.lds, st, A);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
+template <typename MemT, typename InT>
+hipError_t pipe_launch(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
+  switch (c.rb) {
+    case 8: return pipe_launch_rb<MemT, InT, 8>(A, c, st);
+    case 16: return pipe_launch_rb<MemT, InT, 16>(A, c, st);
+    case 32: return pipe_launch_rb<MemT, InT, 32>(A, c, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
 bool dataflow_supported(const sdm_shape& S) {
-  if (S.W + S.R > 128) return false;
-  if (S.N > (1 << 18)) return false;  // deps table packs slots in 18 bits
-  return dataflow_lanes_per_row(S, 256) > 0;
+  if (S.W % 4 || S.R % 4) return false;  // weight lists move in 16-byte pieces
+  if (S.N > (1 << 18)) return false;     // packed slot words hold 18-bit slots
+  if ((size_t)S.N * S.d_v * dtype_size(S.mem_dtype) > 0x7FFFFFFFull) return false;  // buffer offsets
+  if ((size_t)S.T * S.d_v * 4 > 0x7FFFFFFFull) return false;
+  PipeCfg c;
+  return pipe_config(S, 256, &c);
 }
 
 size_t dataflow_deps_bytes(const sdm_shape& S) {
-  const size_t tok = (size_t)S.B * S.H * S.T;
-  return tok * 4 + ((tok * (size_t)(S.W + S.R) * 2 + 255) & ~(size_t)255);
+  return (size_t)S.B * S.H * (size_t)S.T * (size_t)(S.W + S.R) * 4;
 }
 
 size_t dataflow_sched_words(const sdm_shape& S) {
@@ -462,30 +770,27 @@ size_t dataflow_sched_words(const sdm_shape& S) {
 hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                            void* ws, const WsLayout& L, hipStream_t stream) {
+  PipeCfg c;
+  if (!pipe_config(S, device_cus(), &c)) return hipErrorInvalidValue;
   const int U = S.B * S.H;
   char* w = (char*)ws;
-  const size_t tok = (size_t)U * S.T;
-  int16_t* code = (int16_t*)(w + L.deps);
-  uint32_t* mask = (uint32_t*)(w + L.deps + ((tok * (size_t)(S.W + S.R) * 2 + 255) & ~(size_t)255));
+  uint32_t* pk = (uint32_t*)(w + L.deps);
   DepArgs D;
   D.widx = widx;
   D.ridx = ridx;
-  D.mask = mask;
-  D.code = code;
+  D.pk = pk;
   D.T = S.T;
   D.W = S.W;
   D.R = S.R;
+  D.win = c.win;
+  D.N = S.N;
   hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), 0, stream, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int lpr = dataflow_lanes_per_row(S, device_cus());
-  CsArgs A;
-  A.widx = widx;
+  PipeArgs A;
+  A.pk = pk;
   A.wgt = wgt;
-  A.ridx = ridx;
   A.rgt = rgt;
-  A.mask = mask;
-  A.code = code;
   A.v = v;
   A.alpha = alpha;
   A.beta = beta;
@@ -496,15 +801,20 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   A.T = S.T;
   A.W = S.W;
   A.R = S.R;
+  A.E = S.W + S.R;
   A.d_v = S.d_v;
+  A.P = c.P;
+  A.S = c.S;
+  A.win = c.win;
+  A.tpb = c.tpb;
+  A.vw = c.vw;
+  A.rowbytes = S.d_v * (int)dtype_size(S.mem_dtype);
   A.N = S.N;
-  const int rowdw = S.d_v * (int)dtype_size(S.mem_dtype) / 4;
-  A.P = rowdw / lpr;
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
-  if (mb && ib) return cs_launch_lpr<uint16_t, uint16_t>(A, lpr, stream);
-  if (mb && !ib) return cs_launch_lpr<uint16_t, float>(A, lpr, stream);
-  if (!mb && ib) return cs_launch_lpr<float, uint16_t>(A, lpr, stream);
-  return cs_launch_lpr<float, float>(A, lpr, stream);
+  if (mb && ib) return pipe_launch<uint16_t, uint16_t>(A, c, stream);
+  if (mb && !ib) return pipe_launch<uint16_t, float>(A, c, stream);
+  if (!mb && ib) return pipe_launch<float, uint16_t>(A, c, stream);
+  return pipe_launch<float, float>(A, c, stream);
 }
 
 }  // namespace sdm

@@ -20,7 +20,8 @@ namespace sdm {
 namespace {
 
 constexpr int kTok = 32;      // tokens per workgroup
-constexpr int kThreads = 256; // 4 waves
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
@@ -35,9 +36,11 @@ struct AddrArgs {
   int stair_count;      // number of (a, b) rank pairs with (a+1)(b+1) <= n_sel, a,b < kappa
 };
 
-// Rows of the score tile are padded by one float so that the MFMA-layout writes (one token
-// per lane, stride = row length) fall into different LDS banks.
-__host__ __device__ __forceinline__ int score_stride(int s) { return s + 1; }
+// Score tile [32 tokens][s]. The MFMA layout writes one token per lane; to keep those writes
+// in different LDS banks, score m of token n sits at n * s + (m ^ n) when s is a multiple of
+// 32 (the MFMA path); otherwise rows are padded by one float.
+__host__ __device__ __forceinline__ int score_stride(int s) { return s % 32 == 0 ? s : s + 1; }
+__host__ __device__ __forceinline__ int score_swz(int s, int n) { return s % 32 == 0 ? (n & 31) : 0; }
 
 template <bool BF16>
 __device__ __forceinline__ float load_in(const void* p, size_t i) {
@@ -63,7 +66,7 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
     const int b = r / A.T, t = r % A.T;
     const uint16_t* xrow = X + (((size_t)b * A.H + head) * A.T + t) * d_k + (size_t)half * h;
     const int kq = (lane >> 5) * 4;
-    for (int st = wave; st < s / 32; st += 4) {
+    for (int st = wave; st < s / 32; st += kWaves) {
       float16_t acc = {};
       const uint16_t* crow = C + (size_t)(st * 32 + (lane & 31)) * h;
       for (int k0 = 0; k0 < h; k0 += 8) {
@@ -79,7 +82,7 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         int row = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        sc[col * stride + st * 32 + row] = acc[i];
+        sc[col * stride + ((st * 32 + row) ^ col)] = acc[i];
       }
     }
   } else {
@@ -93,7 +96,7 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
       float acc = 0.f;
       for (int c = 0; c < h; ++c)
         acc = fmaf(load_in<BF16>(A.x, xoff + c), load_in<BF16>(A.subkeys, coff + (size_t)m * h + c), acc);
-      sc[n * stride + m] = acc;
+      sc[n * stride + (m ^ score_swz(s, n))] = acc;
     }
   }
 }
@@ -113,24 +116,27 @@ __global__ void __launch_bounds__(kThreads) address_kernel(AddrArgs A) {
   const int BT = A.B * A.T;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint64_t* wbuf = wbuf_all + wave * kWave;
+  int pr[EM];
+  stair_pairs<EM>(kappa, A.n_sel, pr);
 
   for (int half = 0; half < 2; ++half) {
     score_half<BF16>(A, head, r0, half, sc);
     __syncthreads();
-    for (int n = wave; n < kTok; n += 4) {
+    for (int n = wave; n < kTok; n += kWaves) {
       if (r0 + n >= BT) continue;
-      select_half<ES>(sc + n * stride, s, kappa, wbuf, sel_i + (n * 2 + half) * kappa, sel_s + (n * 2 + half) * kappa);
+      select_half<ES>(sc + n * stride, score_swz(s, n), s, kappa, wbuf, sel_i + (n * 2 + half) * kappa,
+                      sel_s + (n * 2 + half) * kappa);
     }
     __syncthreads();
   }
-  for (int n = wave; n < kTok; n += 4) {
+  for (int n = wave; n < kTok; n += kWaves) {
     const int r = r0 + n;
     if (r >= BT) continue;
     const int16_t* i1 = sel_i + (n * 2 + 0) * kappa;
     const int16_t* i2 = sel_i + (n * 2 + 1) * kappa;
     const float* s1 = sel_s + (n * 2 + 0) * kappa;
     const float* s2 = sel_s + (n * 2 + 1) * kappa;
-    uint64_t k = merge_token<EM>(i1, s1, i2, s2, s, kappa, A.n_sel, A.stair_count, wbuf);
+    uint64_t k = merge_token<EM>(i1, s1, i2, s2, s, kappa, A.n_sel, pr, wbuf);
     float scv = lane < A.n_sel ? key_score(k) : -INFINITY;
     float mx = __shfl(scv, 0, kWave);
     float e = lane < A.n_sel ? expf(scv - mx) : 0.f;
@@ -179,7 +185,7 @@ hipError_t launch_es(const AddrArgs& A, size_t lds, hipStream_t st) {
 size_t address_lds_bytes(int s, int kappa) {
   size_t b = (size_t)kTok * score_stride(s) * 4 + (size_t)kTok * 2 * kappa * 6;
   b = (b + 15) & ~(size_t)15;
-  return b + 4 * kWave * 8;
+  return b + kWaves * kWave * 8;
 }
 
 hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys, int n_sel, int32_t* idx,

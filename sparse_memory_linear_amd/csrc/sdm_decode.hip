@@ -112,17 +112,24 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
   }
   __syncthreads();
   // 2. per-half top-kappa, one wave per (vector, half)
-  select_half<ES>(sc + wave * (s + 1), s, kappa, wbuf + wave * 64, sel_i + wave * kappa, sel_s + wave * kappa);
+  select_half<ES>(sc + wave * (s + 1), 0, s, kappa, wbuf + wave * 64, sel_i + wave * kappa, sel_s + wave * kappa);
   __syncthreads();
   // 3. kappa x kappa merge and softmax: wave 0 for the key (W), wave 1 for the query (R)
   if (wave < 2) {
     const int n_sel = wave == 0 ? W : R;
     const int base = wave * 2;
-    uint64_t key = wave == 0
-        ? merge_token<EMW>(sel_i + base * kappa, sel_s + base * kappa, sel_i + (base + 1) * kappa,
-                           sel_s + (base + 1) * kappa, s, kappa, n_sel, A.stairW, wbuf + wave * 64)
-        : merge_token<EMR>(sel_i + base * kappa, sel_s + base * kappa, sel_i + (base + 1) * kappa,
-                           sel_s + (base + 1) * kappa, s, kappa, n_sel, A.stairR, wbuf + wave * 64);
+    uint64_t key;
+    if (wave == 0) {
+      int pr[EMW];
+      stair_pairs<EMW>(kappa, n_sel, pr);
+      key = merge_token<EMW>(sel_i + base * kappa, sel_s + base * kappa, sel_i + (base + 1) * kappa,
+                             sel_s + (base + 1) * kappa, s, kappa, n_sel, pr, wbuf + wave * 64);
+    } else {
+      int pr[EMR];
+      stair_pairs<EMR>(kappa, n_sel, pr);
+      key = merge_token<EMR>(sel_i + base * kappa, sel_s + base * kappa, sel_i + (base + 1) * kappa,
+                             sel_s + (base + 1) * kappa, s, kappa, n_sel, pr, wbuf + wave * 64);
+    }
     float scv = lane < n_sel ? key_score(key) : -INFINITY;
     float mx = __shfl(scv, 0, kWave);
     float e = lane < n_sel ? expf(scv - mx) : 0.f;

@@ -12,14 +12,16 @@ namespace sdm {
 
 // ---------------------------------------------------------------- per-half selection
 // Top-kappa sub-keys of one token-half: lanes < kappa receive (index, score) in rank order.
+// Score i of the row sits at row[i ^ swz] (swz < 32 permutes within aligned groups of 32).
 template <int E>
-__device__ void select_half(const float* row, int s, int kappa, uint64_t* wbuf, int16_t* out_idx, float* out_sc) {
+__device__ void select_half(const float* row, int swz, int s, int kappa, uint64_t* wbuf, int16_t* out_idx,
+                            float* out_sc) {
   const int lane = lane_id();
   uint64_t keys[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     int i = lane + kWave * e;
-    keys[e] = i < s ? rank_key(row[i], (uint32_t)i) : 0ull;
+    keys[e] = i < s ? rank_key(row[i ^ swz], (uint32_t)i) : 0ull;
   }
   uint64_t k = wave_topk<E>(keys, kappa, wbuf);
   if (lane < kappa) {
@@ -29,17 +31,26 @@ __device__ void select_half(const float* row, int s, int kappa, uint64_t* wbuf, 
 }
 
 // ---------------------------------------------------------------- merge
-// (a, b) for the p-th pair of the staircase {(a, b): (a+1)(b+1) <= n_sel, a, b < kappa},
-// enumerated row by row.
-__device__ __forceinline__ bool stair_pair(int p, int kappa, int n_sel, int& a, int& b) {
-  for (a = 0; a < kappa; ++a) {
+// Rank pairs (a, b) of the staircase {(a, b): (a+1)(b+1) <= n_sel, a, b < kappa}, enumerated
+// row by row: this lane's pairs p = lane + 64 e, packed a << 8 | b, or -1 past the end.
+// Depends only on (kappa, n_sel): computed once per wave, outside the token loop.
+template <int EM>
+__device__ __forceinline__ void stair_pairs(int kappa, int n_sel, int (&pr)[EM]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int e = 0; e < EM; ++e) pr[e] = -1;
+  int base = 0;
+  for (int a = 0; a < kappa; ++a) {
     int cnt = n_sel / (a + 1);
     if (cnt > kappa) cnt = kappa;
-    if (cnt <= 0) return false;
-    if (p < cnt) { b = p; return true; }
-    p -= cnt;
+    if (cnt <= 0) break;
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      const int p = lane + kWave * e;
+      if (p >= base && p < base + cnt) pr[e] = (a << 8) | (p - base);
+    }
+    base += cnt;
   }
-  return false;
 }
 
 __device__ __forceinline__ uint64_t cand_key(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2,
@@ -52,16 +63,14 @@ __device__ __forceinline__ uint64_t cand_key(const int16_t* i1, const float* s1,
 // Top n_sel of the kappa x kappa candidates for one token: lanes < n_sel get their key.
 template <int EM>
 __device__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2, int s,
-                                int kappa, int n_sel, int stair_count, uint64_t* wbuf) {
+                                int kappa, int n_sel, const int (&pr)[EM], uint64_t* wbuf) {
   const int lane = lane_id();
   // 1. exact top n_sel of the staircase pairs (every pair outside it is dominated by at
   //    least n_sel pairs inside it up to float32 rounding ties, which step 2 catches)
   uint64_t keys[EM];
 #pragma unroll
-  for (int e = 0; e < EM; ++e) {
-    int p = lane + kWave * e, a, b;
-    keys[e] = (p < stair_count && stair_pair(p, kappa, n_sel, a, b)) ? cand_key(i1, s1, i2, s2, a, b, s) : 0ull;
-  }
+  for (int e = 0; e < EM; ++e)
+    keys[e] = pr[e] >= 0 ? cand_key(i1, s1, i2, s2, pr[e] >> 8, pr[e] & 255, s) : 0ull;
   uint64_t top = wave_topk<EM>(keys, n_sel, wbuf);
   const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, n_sel - 1);
   const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), n_sel - 1);

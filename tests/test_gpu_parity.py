@@ -16,6 +16,8 @@ W_ = SI.WORKLOADS
 CASES = {
     # full tiny workload: fp32 everywhere
     "tiny_fp32": W_["tiny_fp32"],
+    # fp32 inputs with s = 64: vector-ALU scoring into the swizzled score tile
+    "fp32_s64_T100": W_["tiny_fp32"].replace(B=1, H=2, T=100, N=4096, kappa=8, W=8, R=8),
     # the small layer's shape with fewer tokens (8 tiles of 32 tokens per head)
     "small_T256": W_["small"].replace(B=1, H=2, T=256),
     # 1.4B-scale layer shape (s = 512, d_v = 64, bf16 table), ragged token count

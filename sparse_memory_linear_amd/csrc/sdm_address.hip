@@ -22,6 +22,7 @@ namespace {
 constexpr int kTok = 32;      // tokens per workgroup
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kMaxK8 = 8;     // MFMA scoring for half widths up to 64 (8 steps of 8)
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
@@ -57,7 +58,7 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
   const int stride = score_stride(s);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const bool use_mfma = BF16 && (s % 32 == 0) && (h % 8 == 0);
+  const bool use_mfma = BF16 && (s % 32 == 0) && (h % 8 == 0) && h <= 8 * kMaxK8;
   if (use_mfma) {
     const uint16_t* X = (const uint16_t*)A.x;
     const uint16_t* C = (const uint16_t*)A.subkeys + ((size_t)head * 2 + half) * (size_t)s * h;
@@ -66,22 +67,30 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
     const int b = r / A.T, t = r % A.T;
     const uint16_t* xrow = X + (((size_t)b * A.H + head) * A.T + t) * d_k + (size_t)half * h;
     const int kq = (lane >> 5) * 4;
+    const int nk = h / 8;
+    // this lane's token fragments for every k step, loaded once for all sub-key tiles
+    uint2 xf[kMaxK8];
+#pragma unroll
+    for (int k = 0; k < kMaxK8; ++k)
+      if (k < nk) xf[k] = *(const uint2*)(xrow + 8 * k + kq);
     for (int st = wave; st < s / 32; st += kWaves) {
-      float16_t acc = {};
       const uint16_t* crow = C + (size_t)(st * 32 + (lane & 31)) * h;
-      for (int k0 = 0; k0 < h; k0 += 8) {
-        uint2 av = *(const uint2*)(crow + k0 + kq);
-        uint2 bv = *(const uint2*)(xrow + k0 + kq);
-        short4_t a = __builtin_bit_cast(short4_t, av);
-        short4_t bb = __builtin_bit_cast(short4_t, bv);
-        acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bb, acc, 0, 0, 0);
-      }
+      uint2 cf[kMaxK8];
+#pragma unroll
+      for (int k = 0; k < kMaxK8; ++k)
+        if (k < nk) cf[k] = *(const uint2*)(crow + 8 * k + kq);
+      float16_t acc = {};
+#pragma unroll
+      for (int k = 0; k < kMaxK8; ++k)
+        if (k < nk)
+          acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4_t, cf[k]),
+                                                         __builtin_bit_cast(short4_t, xf[k]), acc, 0, 0, 0);
       // D[row = sub-key][col = token]; lane holds col = lane%32,
       // rows 8*(i/4) + 4*(lane/32) + i%4.
       const int col = lane & 31;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int row = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int row = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         sc[col * stride + ((st * 32 + row) ^ col)] = acc[i];
       }
     }
@@ -103,7 +112,7 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
 
 // ---------------------------------------------------------------- kernel
 template <bool BF16, int ES, int EM>
-__global__ void __launch_bounds__(kThreads) address_kernel(AddrArgs A) {
+__global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int s = A.s, kappa = A.kappa;
   const int stride = score_stride(s);

@@ -13,18 +13,24 @@
 //     from that writer on chip, and every other row from the table once all tokens older
 //     than the window are stored.
 //
-// Inside a workgroup the tokens stream through an LDS ring of S token slots (S = 2 win):
-//   * wave 0 (meta) copies each token's packed slot list, weights, gates and v columns into
-//     the ring with direct-to-LDS loads, up to S - win tokens ahead of the store wave;
-//   * wave 1 (gather) loads the table rows of each token's slots into the ring, many tokens
-//     in flight, once every token older than the window is in the table;
-//   * waves 3.. (compute) take tokens in order; a token runs when its rows are in the ring
+// Inside a workgroup the tokens stream through two LDS rings: a token ring of S slots
+// (S = 2 win: gathered rows, new write rows, output block) and a metadata ring of SM slots
+// (packed slot words, weights, gates, v columns).
+//   * wave 0 (meta) copies the metadata of each token into its ring with direct-to-LDS
+//     loads, up to SM tokens ahead of the store wave;
+//   * waves 1 and 3 (gather) load the table rows of each token's slots into registers, a
+//     few 4-token steps in flight, and write them to the token ring; a token is gathered
+//     once every token older than the window is in the table and its ring slot is free;
+//   * waves 4.. (compute) take tokens in order; a token runs when its rows are in the ring
 //     and its writers inside the window have published their new rows. It replaces its
-//     write rows in the ring by their new values and leaves its output block there. It never
-//     touches HBM;
-//   * wave 2 (store) writes new rows and outputs to HBM in token order and advances the
-//     watermark of completed stores. Storing in token order keeps writes to one slot in
-//     order and after every earlier read of it.
+//     write rows in the ring by their new values and leaves its output block there. It
+//     never touches HBM;
+//   * wave 2 (store) writes new rows and outputs to HBM in token order, several tokens per
+//     instruction, and advances the watermark of completed stores. Storing in token order
+//     keeps writes to one slot in order and after every earlier read of it.
+// Each CU serves a bounded rate of vector-memory instructions; the gather and store paths
+// are laid out to move each row block with one 8-byte lane and as few instructions as
+// possible.
 // The result is bit-identical to processing the tokens one after another.
 //
 // deps_kernel precomputes, per token and slot position, a packed word: the slot, and the
@@ -48,12 +54,13 @@ constexpr int kMaxWin = 127;
 constexpr uint32_t kCoded = 0x80000000u;
 constexpr uint32_t kInvalid = 0x40000000u;
 constexpr uint32_t kSlotMask = 0x3FFFFu;
-constexpr int kWaves = 16;         // meta, gather, store, 13 compute waves
+constexpr int kWaves = 16;         // meta, 2 gather, store, 12 compute waves
+constexpr int kGatherWaves = 2;    // waves 1 and 3
+constexpr int kGatherDepth = 3;    // own gather steps in flight per gather wave
 constexpr int kMetaDepth = 16;     // meta batches in flight (3 loads each)
 constexpr int kGatherGroup = 4;    // tokens per gather step
 constexpr int kStoreBatch = 8;     // tokens per store step (watermark granularity)
-constexpr size_t kLdsBudget = 150 * 1024;
-constexpr size_t kDumpBytes = 1024;  // LDS sink of the gather wave's padding loads
+constexpr size_t kLdsBudget = 156 * 1024;
 // Longest a wave waits (in units of s_sleep 2, ~53 ns): about 3.5 s. When it runs out the
 // workgroup gives up (abort flag), every wave exits, and the workspace error word records
 // it: the result is then invalid, but the kernel always terminates.
@@ -137,7 +144,8 @@ struct PipeArgs {
   float* o;            // [U][T][d_v]
   unsigned long long* err;
   int U, T, W, R, E, d_v, P;
-  int S, win, tpb, vw, rowbytes;
+  int S, SM, win, tpb, vw, rowbytes;
+  int pack2;  // two tokens' write rows per store instruction
   long long N;
 };
 
@@ -184,21 +192,8 @@ __device__ __forceinline__ int dma_wave_read(const int* p) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
   return __builtin_amdgcn_readfirstlane(v);
 }
-__device__ __forceinline__ void dma_wave_read2(uint32_t a0, uint32_t a1, uint32_t (&v)[2]) {
-  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(v[0]), "=&v"(v[1])
-               : "v"(a0), "v"(a1)
-               : "memory");
-}
 __device__ __forceinline__ void dma_wave_write(int* p, int v) {
   asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
-}
-
-// Buffer load of SZ bytes per lane straight into LDS at dst + lane * SZ (dst wave-uniform).
-template <int SZ>
-__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t off) {
-  if constexpr (SZ == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, off, 0, 0, 0);
-  else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -224,6 +219,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int T = A.T, W = A.W, R = A.R, E = A.E, S = A.S, smask = A.S - 1, win = A.win;
+  const int SM = A.SM, mmask = A.SM - 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane / LPC, l = lane % LPC;
   // XCD-aware placement: all column blocks of a unit go to the same XCD (workgroups are
@@ -237,12 +233,14 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
   int* g_tok = ctrl + kCtrlWords;  // [S] token whose rows are gathered in ring slot i
   int* f_tok = g_tok + S;          // [S] token whose new write rows are in slot i
   int* c_tok = f_tok + S;          // [S] token whose compute is complete in slot i
-  uint32_t* pk_r = (uint32_t*)(c_tok + S);                          // [S][E]
-  float* wt_r = (float*)(pk_r + (size_t)S * E);                     // [S][E]
-  uint32_t* vab_r = (uint32_t*)(wt_r + (size_t)S * E);              // [S][vw]: v columns, alpha, beta
-  unsigned char* rows = (unsigned char*)(vab_r + (size_t)S * A.vw);  // [S][E][RB]
-  float* obuf = (float*)(rows + (size_t)S * E * RB);                // [S][CPR]
-  unsigned char* dump = (unsigned char*)(obuf + (size_t)S * CPR);    // 1 KB sink for padding loads
+  // token ring (S slots): gathered rows, new write rows, write slots, output block
+  unsigned char* rows = (unsigned char*)(c_tok + S);                 // [S][E][RB]
+  int32_t* slot_w = (int32_t*)(rows + (size_t)S * E * RB);           // [S][W] slot of each write row, -1 = skip
+  float* obuf = (float*)(slot_w + (size_t)S * W);                    // [S][CPR]
+  // metadata ring (SM slots): packed slot words, weights, v columns and gates
+  uint32_t* pk_r = (uint32_t*)(obuf + (size_t)S * CPR);             // [SM][E]
+  float* wt_r = (float*)(pk_r + (size_t)SM * E);                    // [SM][E]
+  uint32_t* vab_r = (uint32_t*)(wt_r + (size_t)SM * E);             // [SM][vw]
 
   for (int i = threadIdx.x; i < kCtrlWords; i += blockDim.x) ctrl[i] = 0;
   for (int i = threadIdx.x; i < 3 * S; i += blockDim.x) g_tok[i] = -1;
@@ -269,7 +267,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     long long budget = kSpinBudget;
     for (int b = 0; b < nb; ++b) {
       const int tb = b * tpb;
-      const int need = tb + tpb - S + win;  // ring slots of this batch are free
+      const int need = tb + tpb - SM;  // metadata slots of this batch are free (older tokens stored)
       if (s_seen < need) {
         s_seen = dma_wave_read(&ctrl[kStoreIssued]);
         if (s_seen < need) {
@@ -287,7 +285,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
           }
         }
       }
-      const int sl0 = tb & smask;
+      const int sl0 = tb & mmask;
       {
         const int q = lane * 4, tt = q / E;
         if (q < tpb * E && tb + tt < T)
@@ -323,95 +321,102 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     return;
   }
 
-  if (wave == 1) {
-    // ================================================================ gather wave
-    // Direct-to-LDS loads of the table rows of each token's slots, GB tokens per step and up
-    // to GD steps in flight. Slots with a writer inside the window come from the ring
+  if (wave == 1 || wave == 3) {
+    // ================================================================ gather waves
+    // Table rows of each token's slots, GB tokens per step, loaded into registers (8 bytes a
+    // lane, one lane per row block) and written to the ring GD own steps later. The two
+    // waves take alternate steps. Slots with a writer inside the window come from the ring
     // instead: their loads (and those of slots outside [0, N)) are out of range and give 0.
     constexpr int GB = kGatherGroup;
-    constexpr int DSZ = RB == 8 ? 4 : 16;           // bytes per lane per load
-    constexpr int LPD = RB / DSZ;                   // lanes per row
-    constexpr int RPI = 64 / LPD;                   // rows per load instruction
-    constexpr int ND = RB == 8 ? 2 * NG : (NG > 1 ? NG / 2 : 1);  // load instructions per token
-    constexpr int GD = 63 / (GB * ND) < 8 ? 63 / (GB * ND) : 8;   // steps in flight
-    static_assert(GD >= 1 && GD * GB * ND <= 63, "vmcnt range");
+    constexpr int GD = kGatherDepth;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (char*)A.M + (size_t)u * (size_t)A.N * A.rowbytes, (short)0, (int)((size_t)A.N * A.rowbytes), 0x00020000);
     const int nsteps = (T + GB - 1) / GB;
-    const int ld = lane / LPD;                                  // row of this lane within a load
-    const uint32_t lcol = (uint32_t)(cb * RB + (lane % LPD) * DSZ);
-    int m_seen = 0, wm_seen = 0, published = 0;
+    const int gw = wave == 1 ? 0 : 1;  // own steps gw, gw + kGatherWaves, ...
+    const int nown = nsteps > gw ? (nsteps - gw + kGatherWaves - 1) / kGatherWaves : 0;
+    int m_seen = 0, wm_seen = 0, s_seen = 0;
+    int done = -1;  // own step index last written to the ring
+    bool aborted = false;
     long long budget = kSpinBudget;
-    auto publish_upto = [&](int k) {  // steps < k are complete: publish their tokens
-      for (; published < k; ++published) {
-        const int t = published * GB + lane;
-        if (lane < GB && t < T) dma_wave_write(&g_tok[t & smask], t);
-      }
-    };
-    for (int k = 0; k < nsteps; ++k) {
-      const int t0 = k * GB;
-      const int tl = t0 + GB < T ? t0 + GB : T;
-      if (m_seen < tl || wm_seen < tl - 1 - win) {
-        m_seen = dma_wave_read(&ctrl[kMetaDone]);
-        wm_seen = dma_wave_read(&ctrl[kWm]);
-        if (m_seen < tl || wm_seen < tl - 1 - win) {
-          // blocked: publish everything in flight first, so that nothing waits on this wave
-          __builtin_amdgcn_s_waitcnt(0);
-          publish_upto(k);
-          while (true) {
-            m_seen = dma_wave_read(&ctrl[kMetaDone]);
-            wm_seen = dma_wave_read(&ctrl[kWm]);
-            if (m_seen >= tl && wm_seen >= tl - 1 - win) break;
-            if (--budget <= 0 || dma_wave_read(&ctrl[kAbort])) {
-              give_up();
-              return;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-        }
-      }
-      // packed slot words of this lane's rows, for the GB tokens
-      uint32_t pkv[GB][ND];
-#pragma unroll
-      for (int tt = 0; tt < GB; ++tt) {
-        const int sl = (t0 + tt) & smask;
-#pragma unroll
-        for (int d = 0; d < ND; d += 2) {
-          const int e0 = d * RPI + ld, e1 = (d + 1) * RPI + ld;
-          uint32_t r[2];
-          dma_wave_read2(lds_addr(pk_r + (size_t)sl * E + (e0 < E ? e0 : 0)),
-                         lds_addr(pk_r + (size_t)sl * E + (e1 < E ? e1 : 0)), r);
-          pkv[tt][d] = r[0];
-          if (d + 1 < ND) pkv[tt][d + 1] = r[1];
-        }
-      }
+    u2 data[GD][GB][NG];
+    auto ready = [&](int tl) { return m_seen >= tl && wm_seen >= tl - 1 - win && s_seen >= tl - S + win; };
+    // own step i (held in d) into the ring, unless already written
+    auto complete = [&](int i, const u2 (&d)[GB][NG]) {
+      if (i <= done) return;
+      const int t0 = (gw + i * kGatherWaves) * GB;
 #pragma unroll
       for (int tt = 0; tt < GB; ++tt) {
         const int t = t0 + tt;
-        const int sl = t & smask;
+        if (t < T) {
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int e = d * RPI + ld;
-          const bool live = t < T && d * RPI < E;  // wave-uniform
-          const uint32_t p = pkv[tt][d];
-          const uint32_t off =
-              (!live || e >= E || (p & (kCoded | kInvalid))) ? oob : (p & kSlotMask) * (uint32_t)A.rowbytes + lcol;
-          if (live) {
-            if (e < E)
-              load_lds<DSZ>(rs, rows + ((size_t)sl * E + d * RPI) * RB, off);
-          } else {
-            load_lds<DSZ>(rs, dump, oob);
+          for (int n = 0; n < NG; ++n) {
+            const int e = n * G + g;
+            if (e < E) *row_ptr(t & smask, e) = d[tt][n];
           }
         }
       }
-      if (k >= GD) {
-        // exactly GB * ND loads per step: step k - GD is complete
-        wait_vmcnt<GD * GB * ND>();
-        publish_upto(k - GD + 1);
+      release_lds();
+      if (lane < GB && t0 + lane < T) lds_st(&g_tok[(t0 + lane) & smask], t0 + lane);
+      done = i;
+    };
+    auto issue = [&](int i, u2 (&d)[GB][NG]) {
+      const int t0 = (gw + i * kGatherWaves) * GB;
+#pragma unroll
+      for (int tt = 0; tt < GB; ++tt) {
+        const int t = t0 + tt;
+        const bool tv = t < T && !aborted;
+        const int ml = t & mmask;
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+          const int e = n * G + g;
+          const uint32_t p = (tv && e < E) ? pk_r[(size_t)ml * E + e] : kInvalid;
+          const uint32_t off = (p & (kCoded | kInvalid)) ? oob : (p & kSlotMask) * (uint32_t)A.rowbytes + colb;
+          d[tt][n] = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        }
+      }
+    };
+    for (int base = 0; base < nown + GD; base += GD) {
+#pragma unroll
+      for (int sidx = 0; sidx < GD; ++sidx) {
+        const int i = base + sidx;
+        // register set sidx holds own step i - GD: write it out
+        if (i >= GD && i - GD < nown) complete(i - GD, data[sidx]);
+        if (i < nown) {
+          const int t0 = (gw + i * kGatherWaves) * GB;
+          const int tl = t0 + GB < T ? t0 + GB : T;
+          if (!ready(tl) && !aborted) {
+            m_seen = lds_ld(&ctrl[kMetaDone]);
+            wm_seen = lds_ld(&ctrl[kWm]);
+            s_seen = lds_ld(&ctrl[kStoreIssued]);
+            if (!ready(tl)) {
+              // blocked: first write out every own step still in flight, oldest first
+#pragma unroll
+              for (int j = 1; j < GD; ++j)
+                if (i - GD + j >= 0) complete(i - GD + j, data[(sidx + j) % GD]);
+              while (true) {
+                m_seen = lds_ld(&ctrl[kMetaDone]);
+                wm_seen = lds_ld(&ctrl[kWm]);
+                s_seen = lds_ld(&ctrl[kStoreIssued]);
+                if (ready(tl)) break;
+                if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+                  aborted = true;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+              }
+            }
+            acquire_lds();
+          }
+        }
+        // every position issues its loads (past the end: out of range), so the number of
+        // loads in flight is the same on every path and the waits above stay exact
+        issue(i, data[sidx]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    publish_upto(nsteps);
+    if (wave == 1) {
+    }
+    if (aborted) give_up();
     return;
   }
 
@@ -442,46 +447,67 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
         __builtin_amdgcn_s_sleep(1);
       }
       acquire_lds();
-      u2 val[SB][NP];
-      uint32_t off[SB][NP];
-      float ov[SB][CPL];
-      uint32_t ooff[SB];
-#pragma unroll
-      for (int k = 0; k < SB; ++k) {
+      // outputs of the whole batch in one instruction: lane k * LPC + l carries token k
+      float ov[CPL];
+      uint32_t ooff;
+      {
+        const int k = lane / LPC, lo = lane % LPC;
         const int t = t0 + k;
-        const bool tv = t < T;
+        const bool live = k < SB && t < T;
         const int sl = t & smask;
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const int j = i * G + g;
-          const int jc = j < W ? j : W - 1;
-          const uint32_t p = (tv && j < W) ? pk_r[(size_t)sl * E + j] : kInvalid;
-          const bool ok = (p & kCoded) || !(p & kInvalid);
-          val[k][i] = *row_ptr(sl, jc);
-          off[k][i] = ok ? (p & kSlotMask) * (uint32_t)A.rowbytes + colb : oob;
-        }
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) ov[k][c] = obuf[(size_t)sl * CPR + l * CPL + c];
-        ooff[k] = (tv && g == 0) ? (uint32_t)(((size_t)t * A.d_v + cb * CPR + l * CPL) * 4) : oob;
+        for (int c = 0; c < CPL; ++c) ov[c] = live ? obuf[(size_t)sl * CPR + lo * CPL + c] : 0.f;
+        ooff = live ? (uint32_t)(((size_t)t * A.d_v + cb * CPR + lo * CPL) * 4) : oob;
       }
-      // exactly SB * (NP + 1) store instructions per batch, so the wait below is exact
+      if (A.pack2) {
+        // two tokens per row instruction (the write rows of a token fill at most half a wave)
+        constexpr int HG = G / 2;
+        const int h = g / HG, j = g % HG;
+        u2 val[SB / 2];
+        uint32_t off[SB / 2];
 #pragma unroll
-      for (int k = 0; k < SB; ++k) {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) __builtin_amdgcn_raw_buffer_store_b64(val[k][i], rs, off[k][i], 0, 0);
-        if constexpr (CPL == 4) {
-          u4 o4 = {__float_as_uint(ov[k][0]), __float_as_uint(ov[k][1]), __float_as_uint(ov[k][2]),
-                   __float_as_uint(ov[k][3])};
-          __builtin_amdgcn_raw_buffer_store_b128(o4, ro, ooff[k], 0, 0);
-        } else {
-          u2 o2 = {__float_as_uint(ov[k][0]), __float_as_uint(ov[k][1])};
-          __builtin_amdgcn_raw_buffer_store_b64(o2, ro, ooff[k], 0, 0);
+        for (int m = 0; m < SB / 2; ++m) {
+          const int t = t0 + 2 * m + h;
+          const int sl = t & smask;
+          const int n = (t < T && j < W) ? slot_w[(size_t)sl * W + j] : -1;
+          val[m] = *row_ptr(sl, j < W ? j : 0);
+          off[m] = n >= 0 ? (uint32_t)n * (uint32_t)A.rowbytes + colb : oob;
         }
+#pragma unroll
+        for (int m = 0; m < SB / 2; ++m) __builtin_amdgcn_raw_buffer_store_b64(val[m], rs, off[m], 0, 0);
+      } else {
+        u2 val[SB][NP];
+        uint32_t off[SB][NP];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          const int t = t0 + k;
+          const int sl = t & smask;
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const int j = i * G + g;
+            const int n = (t < T && j < W) ? slot_w[(size_t)sl * W + j] : -1;
+            val[k][i] = *row_ptr(sl, j < W ? j : W - 1);
+            off[k][i] = n >= 0 ? (uint32_t)n * (uint32_t)A.rowbytes + colb : oob;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < SB; ++k)
+#pragma unroll
+          for (int i = 0; i < NP; ++i) __builtin_amdgcn_raw_buffer_store_b64(val[k][i], rs, off[k][i], 0, 0);
+      }
+      if constexpr (CPL == 4) {
+        u4 o4 = {__float_as_uint(ov[0]), __float_as_uint(ov[1]), __float_as_uint(ov[2]), __float_as_uint(ov[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(o4, ro, ooff, 0, 0);
+      } else {
+        u2 o2 = {__float_as_uint(ov[0]), __float_as_uint(ov[1])};
+        __builtin_amdgcn_raw_buffer_store_b64(o2, ro, ooff, 0, 0);
       }
       release_lds();
       if (lane == 0) lds_st(&ctrl[kStoreIssued], t0 + SB);
       // the previous batch's stores are complete: every token before t0 is in the table
-      wait_vmcnt<SB * (NP + 1)>();
+      // (a batch issues exactly SB/2 + 1 or SB * NP + 1 store instructions)
+      if (A.pack2) wait_vmcnt<SB / 2 + 1>();
+      else wait_vmcnt<SB * NP + 1>();
       if (lane == 0) lds_st(&ctrl[kWm], t0);
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -509,9 +535,10 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       if (aborted) break;
     }
     acquire_lds();
-    const uint32_t* pks = pk_r + (size_t)sl * E;
-    const float* wts = wt_r + (size_t)sl * E;
-    const uint32_t* vab = vab_r + (size_t)sl * A.vw;
+    const int ml = t & mmask;
+    const uint32_t* pks = pk_r + (size_t)ml * E;
+    const float* wts = wt_r + (size_t)ml * E;
+    const uint32_t* vab = vab_r + (size_t)ml * A.vw;
     uint32_t pw[NP], pr[NP];
     float aw[NP], ur[NP];
     u2 xw[NP], xr[NP];
@@ -599,7 +626,14 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       PT::unpack(xw[i], x);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], aw[i] * dl[c]);
-      if (j < W) *row_ptr(sl, j) = PT::pack(y);
+      if (j < W) {
+        *row_ptr(sl, j) = PT::pack(y);
+        if (l == 0) slot_w[(size_t)sl * W + j] = (pw[i] & (kCoded | kInvalid)) == kInvalid ? -1 : (int)(pw[i] & kSlotMask);
+        // a row rewritten by the next token goes out in the same store instruction as that
+        // token's, where lane order is not defined: only the later token stores it
+        if (A.pack2 && (t & 1) && l == 0 && (pw[i] & kCoded) && ((pw[i] >> 24) & 127) == 1)
+          slot_w[(size_t)((sl - 1) & smask) * W + ((pw[i] >> 18) & 63)] = -1;
+      }
     }
     release_lds();
     if (lane == 0) lds_st(&f_tok[sl], t);
@@ -648,7 +682,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 
 // ------------------------------------------------------------------ configuration
 struct PipeCfg {
-  int rb, P, S, win, tpb, vw, np, ng;
+  int rb, P, S, SM, win, tpb, vw, np, ng;
   size_t lds;
 };
 
@@ -674,22 +708,35 @@ bool pipe_fits(const sdm_shape& S, int rb, PipeCfg* c) {
   const int vw = cpr * isz / 4 + 2;
   if (vw > 64) return false;
   const int tpb = std::min(pow2_floor(std::max(1, 256 / E)), pow2_floor(64 / vw));
-  const size_t slot = 12 + (size_t)E * 8 + (size_t)vw * 4 + (size_t)E * rb + (size_t)cpr * 4;
-  const size_t fixed = kCtrlWords * 4 + kDumpBytes;
-  int ring = 256;
-  while (ring >= 64 && fixed + ring * slot > kLdsBudget) ring /= 2;
-  if (ring < 64) return false;
-  // progress: a blocked gather step and a meta batch fit between the store wave and the window
-  if (kGatherGroup + kStoreBatch > ring / 2 || kGatherGroup + tpb + kStoreBatch > ring - ring / 2) return false;
+  const size_t tslot = 12 + (size_t)E * rb + (size_t)S.W * 4 + (size_t)cpr * 4;  // token ring slot
+  const size_t mslot = (size_t)E * 8 + (size_t)vw * 4;                          // metadata ring slot
+  const size_t fixed = kCtrlWords * 4;
+  // the longest token ring that fits, then the longest metadata ring
+  int ring = 0, mring = 0;
+  for (int r = 256; r >= 64 && !ring; r /= 2)
+    for (int m = 256; m >= 64; m /= 2) {
+      const int w = std::min(kMaxWin, r / 2);
+      // progress: a blocked gather step fits between the store wave and the window, and a
+      // metadata batch between the store wave and the end of the metadata ring
+      if (kGatherGroup + kStoreBatch > w || kGatherGroup + kStoreBatch > r - w) continue;
+      if (kGatherGroup + tpb + kStoreBatch > m) continue;
+      if (fixed + r * tslot + m * mslot <= kLdsBudget) {
+        ring = r;
+        mring = m;
+        break;
+      }
+    }
+  if (!ring) return false;
   c->rb = rb;
   c->P = rowbytes / rb;
   c->S = ring;
+  c->SM = mring;
   c->win = std::min(kMaxWin, ring / 2);
   c->tpb = tpb;
   c->vw = vw;
   c->np = np;
   c->ng = ng;
-  c->lds = fixed + ring * slot;
+  c->lds = fixed + ring * tslot + mring * mslot;
   return true;
 }
 
@@ -805,11 +852,13 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   A.d_v = S.d_v;
   A.P = c.P;
   A.S = c.S;
+  A.SM = c.SM;
   A.win = c.win;
   A.tpb = c.tpb;
   A.vw = c.vw;
   A.rowbytes = S.d_v * (int)dtype_size(S.mem_dtype);
   A.N = S.N;
+  A.pack2 = (c.np == 1 && 2 * S.W <= 64 / (c.rb / 8)) ? 1 : 0;
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
   if (mb && ib) return pipe_launch<uint16_t, uint16_t>(A, c, stream);
   if (mb && !ib) return pipe_launch<uint16_t, float>(A, c, stream);

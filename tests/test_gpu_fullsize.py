@@ -1,0 +1,174 @@
+"""The HIP path at full workload sizes, in the launch configuration the benchmark times,
+checked where the oracle can follow it:
+
+* slot indices of tokens sampled over the whole sequence (addressing is per token) are
+  compared position by position, ties counted;
+* outputs over a long prefix of sampled units are compared with the oracle run on that
+  prefix (o_t depends only on tokens up to t), up to the first tie that changes a slot set;
+* table rows that no token writes stay bit-identical to M0, in every checked unit;
+* the whole sequence in two calls on the carried table equals one call, bit for bit;
+* decode: one step over all B x H tables, sampled units checked against the oracle after
+  the oracle's own prefill (other tables hold M0 only; units are independent).
+"""
+import numpy as np
+import pytest
+
+import oracle.sdm_oracle as O
+import sdm_inputs as SI
+from parity import compare_indices, empty_mem, from_dev, lib_shape, log, rel_err, to_dev, tolerance
+
+pytestmark = pytest.mark.gpu
+
+W_ = SI.WORKLOADS
+# workload -> (units checked against the oracle, prefix length, sampled tokens per unit)
+PLAN = {
+    "small": ([(0, 0), (3, 7)], 2048, 256),
+    "layer_1p4b": ([(0, 0), (7, 15)], 4096, 256),
+    "layer_8b_long": ([(0, 0), (0, 7)], 4096, 512),
+}
+
+
+@pytest.fixture(scope="module")
+def sdm():
+    import torch
+    import sparse_memory_linear_amd as S
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    S.lib()
+    return S
+
+
+def upload(inp, sh):
+    d = {k: to_dev(inp[k], sh.in_dtype) for k in ("q", "k", "v", "subkeys")}
+    d["alpha"] = to_dev(inp["alpha"], "f32")
+    d["beta"] = to_dev(inp["beta"], "f32")
+    d["M0"] = to_dev(inp["M0"], sh.mem_dtype)
+    return d
+
+
+def unit_inputs(inp, sh, b, h, T=None):
+    T = sh.T if T is None else T
+    sk = SI.widen(inp["subkeys"][h], sh.in_dtype)
+    return dict(q=SI.widen(inp["q"][b, h, :T], sh.in_dtype), k=SI.widen(inp["k"][b, h, :T], sh.in_dtype),
+                v=SI.widen(inp["v"][b, h, :T], sh.in_dtype), alpha=inp["alpha"][b, h, :T].astype(np.float64),
+                beta=inp["beta"][b, h, :T].astype(np.float64), C1=sk[0], C2=sk[1],
+                M0=SI.widen(inp["M0"][h], sh.mem_dtype))
+
+
+def forward(sdm, sh, dev, S, M, T_lo=0, T_hi=None):
+    import torch
+    T_hi = sh.T if T_hi is None else T_hi
+    Sp = lib_shape(sh, T=T_hi - T_lo)
+    sl = lambda t: t[:, :, T_lo:T_hi].contiguous()
+    o = torch.empty((sh.B, sh.H, T_hi - T_lo, sh.d_v), dtype=torch.float32, device="cuda")
+    wo = torch.empty((sh.B, sh.H, T_hi - T_lo, sh.W), dtype=torch.int32, device="cuda")
+    ro = torch.empty((sh.B, sh.H, T_hi - T_lo, sh.R), dtype=torch.int32, device="cuda")
+    ws = torch.empty(sdm.workspace_bytes(Sp), dtype=torch.uint8, device="cuda")
+    sdm.forward(Sp, sl(dev["q"]), sl(dev["k"]), sl(dev["v"]), sl(dev["alpha"]), sl(dev["beta"]), dev["subkeys"], M,
+                o, ws, wo, ro)
+    torch.cuda.synchronize()
+    assert sdm.workspace_error(ws) == 0
+    return o, wo, ro
+
+
+@pytest.mark.parametrize("name", list(PLAN))
+def test_fullsize_forward(sdm, name):
+    import torch
+    sh = W_[name]
+    units, prefix, nsamp = PLAN[name]
+    log(f"[full] {name}: generating inputs")
+    inp = SI.make_inputs(sh)
+    dev = upload(inp, sh)
+    S = lib_shape(sh)
+    M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, dev["M0"], M)
+    log(f"[full] {name}: forward B={sh.B} H={sh.H} T={sh.T}")
+    o, wo, ro = forward(sdm, sh, dev, S, M)
+    tol = tolerance(sh)
+    rng = np.random.default_rng(7)
+    ties = 0
+    for (b, h) in units:
+        U = unit_inputs(inp, sh, b, h)
+        gw, gr = wo[b, h].cpu().numpy(), ro[b, h].cpu().numpy()
+        # indices of tokens sampled over the whole sequence (always including the last)
+        ts = np.unique(np.concatenate([rng.choice(sh.T, nsamp, replace=False), [sh.T - 1]]))
+        for which, g, n_sel in (("k", gw, sh.W), ("q", gr, sh.R)):
+            oi, _, _ = O.address(U[which][ts], U["C1"], U["C2"], sh.kappa, n_sel)
+            t_, _, fails = compare_indices(g[ts], oi, U[which][ts], U["C1"], U["C2"], sh.N)
+            assert not fails, f"{name} unit ({b},{h}) {which}: {fails[:3]}"
+            ties += t_
+        # outputs over the prefix, up to the first slot-set change caused by a tie
+        P = min(prefix, sh.T)
+        Up = unit_inputs(inp, sh, b, h, T=P)
+        r = O.forward_unit(Up["q"], Up["k"], Up["v"], Up["alpha"], Up["beta"], Up["C1"], Up["C2"], Up["M0"],
+                           sh.kappa, sh.W, sh.R, sh.mem_dtype)
+        tw, cw, fw = compare_indices(gw[:P], r["widx"], Up["k"], Up["C1"], Up["C2"], sh.N)
+        tr, cr, fr = compare_indices(gr[:P], r["ridx"], Up["q"], Up["C1"], Up["C2"], sh.N)
+        assert not fw and not fr
+        first = min(cw + cr) if (cw or cr) else P
+        assert first >= P // 2, f"{name} unit ({b},{h}): slot sets diverge at token {first}"
+        eo = rel_err(o[b, h, :first].cpu().numpy(), r["o"][:first])
+        log(f"[full] {name} unit ({b},{h}): o over {first} tokens rel err {eo:.2e} (tol {tol}); "
+            f"tie positions {tw + tr}")
+        assert eo < tol
+        # rows no token wrote are still M0
+        Mh = SI.widen(from_dev(M[b, h], sh.mem_dtype), sh.mem_dtype)
+        touched = np.zeros(sh.N, bool)
+        touched[gw.ravel()] = True
+        assert np.array_equal(Mh[~touched], U["M0"][~touched])
+    log(f"[full] {name}: sampled tie positions {ties}")
+    # the same sequence in two calls on the carried table: bit for bit
+    M2 = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, dev["M0"], M2)
+    T1 = sh.T // 2 + 3
+    o1, _, _ = forward(sdm, sh, dev, S, M2, 0, T1)
+    o2, _, _ = forward(sdm, sh, dev, S, M2, T1, sh.T)
+    assert torch.equal(torch.cat([o1, o2], 2), o), "split call differs from the single call"
+    assert torch.equal(M2, M), "carried table differs"
+
+
+def test_fullsize_decode(sdm):
+    """One decode step over the full 64 x 16 tables (launch of the benchmark); sequences 0 and
+    37 are prefilled with their 4096 prior tokens, the others hold M0."""
+    import torch
+    sh = W_["decode"]
+    P = sh.prefill
+    log(f"[full] decode: B={sh.B} H={sh.H} N={sh.N}, prefill {P} on sampled sequences")
+    params = SI.make_inputs(sh)
+    dev = upload(params, sh)
+    S1 = lib_shape(sh, T=1)
+    M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S1, dev["M0"], M)
+    Sp = lib_shape(sh, B=1, T=P)
+    ws = torch.empty(sdm.workspace_bytes(Sp), dtype=torch.uint8, device="cuda")
+    o_pre = torch.empty((1, sh.H, P, sh.d_v), dtype=torch.float32, device="cuda")
+    pre = {}
+    for b in (0, 37):
+        pre[b] = SI.make_prefill(sh, b)
+        t = {n: to_dev(pre[b][n], sh.in_dtype if n in ("q", "k", "v") else "f32")
+             for n in ("q", "k", "v", "alpha", "beta")}
+        sdm.forward(Sp, t["q"], t["k"], t["v"], t["alpha"], t["beta"], dev["subkeys"], M[b:b + 1], o_pre, ws)
+    o = torch.empty((sh.B, sh.H, 1, sh.d_v), dtype=torch.float32, device="cuda")
+    sdm.decode_step(S1, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], M, o)
+    torch.cuda.synchronize()
+    tol = tolerance(sh)
+    for b, h in ((0, 0), (37, 15), (5, 3)):
+        sk = SI.widen(params["subkeys"][h], sh.in_dtype)
+        M0h = SI.widen(params["M0"][h], sh.mem_dtype)
+        if b in pre:
+            pb = pre[b]
+            r = O.forward_unit(SI.widen(pb["q"][0, h], sh.in_dtype), SI.widen(pb["k"][0, h], sh.in_dtype),
+                               SI.widen(pb["v"][0, h], sh.in_dtype), pb["alpha"][0, h].astype(np.float64),
+                               pb["beta"][0, h].astype(np.float64), sk[0], sk[1], M0h, sh.kappa, sh.W, sh.R,
+                               sh.mem_dtype)
+            Mstart = r["M"]
+        else:
+            Mstart = M0h
+        o_ref, M_ref, _ = O.decode_step_unit(Mstart, SI.widen(params["q"][b, h, 0], sh.in_dtype),
+                               SI.widen(params["k"][b, h, 0], sh.in_dtype), SI.widen(params["v"][b, h, 0], sh.in_dtype),
+                               float(params["alpha"][b, h, 0]), float(params["beta"][b, h, 0]), sk[0], sk[1],
+                               sh.kappa, sh.W, sh.R, sh.mem_dtype)
+        eo = rel_err(o[b, h, 0].cpu().numpy(), o_ref)
+        Mh = SI.widen(from_dev(M[b, h], sh.mem_dtype), sh.mem_dtype)
+        em = rel_err(Mh, M_ref)
+        log(f"[full] decode unit ({b},{h}): o rel err {eo:.2e}, table rel err {em:.2e} (tol {tol})")
+        assert eo < tol and em < tol

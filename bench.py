@@ -49,10 +49,14 @@ def recurrence_bytes_per_token_head(sh: SI.Shape) -> int:
     return (2 * sh.W + sh.R) * sh.d_v * mem + sh.d_v * inb + sh.d_v * 4 + 8
 
 
+RECURRENCE_SOURCES = ("sdm_dataflow.hip", "sdm_device.hpp")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources of the recurrence kernels (dependency pass and pipeline)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in RECURRENCE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -46,7 +46,7 @@ namespace sdm {
 namespace {
 
 constexpr int kDepBlk = 64;        // tokens per deps workgroup
-constexpr int kHashBits = 15;      // deps hash table: 32768 entries, at most (kDepBlk + kMaxWin) * W = 12224 used
+constexpr int kMaxHashBits = 15;   // deps hash table: at most 32768 entries, at most half full
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 constexpr int kMaxWin = 127;
 // packed slot word: [31] coded | [30:24] distance | [23:18] writer position | [17:0] slot,
@@ -74,21 +74,23 @@ struct DepArgs {
   const int32_t* widx;  // [U][T][W]
   const int32_t* ridx;  // [U][T][R]
   uint32_t* pk;         // [U][T][W+R] packed slot words
-  int T, W, R, win;
+  int T, W, R, win, bits;  // hash table of 2^bits entries
   long long N;
 };
 
-__device__ __forceinline__ uint32_t dep_hash(uint32_t slot) { return (slot * 2654435761u) >> (32 - kHashBits); }
+__device__ __forceinline__ uint32_t dep_hash(uint32_t slot, int bits) { return (slot * 2654435761u) >> (32 - bits); }
 
 // hash entry = slot << 14 | window offset << 6 | writer position
 __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
-  __shared__ uint32_t table[1 << kHashBits];
+  extern __shared__ uint32_t table[];  // 2^bits entries
+  const int bits = A.bits;
+  const uint32_t hmask = (1u << bits) - 1;
   const int u = blockIdx.y;
   const int t0 = blockIdx.x * kDepBlk;
   const int wlo = t0 - A.win > 0 ? t0 - A.win : 0;
   const int whi = t0 + kDepBlk < A.T ? t0 + kDepBlk : A.T;
   const int W = A.W, R = A.R, per = W + R;
-  for (int i = threadIdx.x; i < (1 << kHashBits); i += 256) table[i] = kEmpty;
+  for (int i = threadIdx.x; i < (1 << bits); i += 256) table[i] = kEmpty;
   __syncthreads();
   const int32_t* wi = A.widx + (size_t)u * A.T * W;
   const int32_t* ri = A.ridx + (size_t)u * A.T * R;
@@ -97,8 +99,8 @@ __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
     const int32_t slot = wi[(size_t)(wlo + k) * W + j];
     if (slot < 0 || slot >= A.N) continue;
     const uint32_t ent = ((uint32_t)slot << 14) | ((uint32_t)k << 6) | (uint32_t)j;
-    uint32_t h = dep_hash((uint32_t)slot);
-    while (atomicCAS(&table[h], kEmpty, ent) != kEmpty) h = (h + 1) & ((1u << kHashBits) - 1);
+    uint32_t h = dep_hash((uint32_t)slot, bits);
+    while (atomicCAS(&table[h], kEmpty, ent) != kEmpty) h = (h + 1) & hmask;
   }
   __syncthreads();
   uint32_t* out = A.pk + ((size_t)u * A.T + t0) * per;
@@ -110,7 +112,7 @@ __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
     uint32_t word = kInvalid;
     if (slot >= 0 && slot < A.N) {
       int best = -1, bestj = 0;
-      uint32_t h = dep_hash((uint32_t)slot);
+      uint32_t h = dep_hash((uint32_t)slot, bits);
       while (true) {
         const uint32_t ent = table[h];
         if (ent == kEmpty) break;
@@ -123,7 +125,7 @@ __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
             bestj = ent & 63;
           }
         }
-        h = (h + 1) & ((1u << kHashBits) - 1);
+        h = (h + 1) & hmask;
       }
       word = (uint32_t)slot;
       if (best >= 0) word |= kCoded | ((uint32_t)(kt - best) << 24) | ((uint32_t)bestj << 18);
@@ -831,7 +833,10 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   D.R = S.R;
   D.win = c.win;
   D.N = S.N;
-  hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), 0, stream, D);
+  // at most half full: writers of one block and its window
+  D.bits = 10;
+  while (D.bits < kMaxHashBits && (1 << D.bits) < 2 * (kDepBlk + c.win) * S.W) ++D.bits;
+  hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), (size_t)4 << D.bits, stream, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PipeArgs A;

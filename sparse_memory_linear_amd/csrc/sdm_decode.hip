@@ -14,6 +14,7 @@ namespace sdm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxK8 = 8;  // MFMA scoring for half widths up to 64
 
 struct DecArgs {
   const void* q;
@@ -101,14 +102,51 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
   const int d_k = 2 * hh;
 
   // 1. scores of (k half 0, k half 1, q half 0, q half 1) against their sub-keys
-  for (int p = tid; p < 4 * s; p += kThreads) {
-    const int c = p / s, m = p % s, half = c & 1;
-    const void* x = c < 2 ? A.k : A.q;
-    const size_t xo = (size_t)u * d_k + (size_t)half * hh;
-    const size_t co = ((size_t)head * 2 + half) * (size_t)s * hh + (size_t)m * hh;
-    float acc = 0.f;
-    for (int i = 0; i < hh; ++i) acc = fmaf(ld_in<BF16>(x, xo + i), ld_in<BF16>(A.subkeys, co + i), acc);
-    sc[c * (s + 1) + m] = acc;
+  if (BF16 && (s % 32 == 0) && (hh % 8 == 0) && hh <= 8 * kMaxK8) {
+    // MFMA: a 32-sub-key tile of one half is the A operand; the B operand's columns 0 and 1
+    // are that half of k and of q (the other columns are zero), so one pass scores both.
+    typedef short short4_t __attribute__((ext_vector_type(4)));
+    typedef float float16_t __attribute__((ext_vector_type(16)));
+    const int col = lane & 31, kq = (lane >> 5) * 4, nk = hh / 8;
+    for (int half = 0; half < 2; ++half) {
+      const uint16_t* xv = (const uint16_t*)(col == 0 ? A.k : A.q) + (size_t)u * d_k + (size_t)half * hh;
+      uint2 xf[kMaxK8];
+#pragma unroll
+      for (int kk = 0; kk < kMaxK8; ++kk)
+        if (kk < nk) xf[kk] = col < 2 ? *(const uint2*)(xv + 8 * kk + kq) : make_uint2(0u, 0u);
+      const uint16_t* C = (const uint16_t*)A.subkeys + ((size_t)head * 2 + half) * (size_t)s * hh;
+      for (int st = wave; st < s / 32; st += kThreads / 64) {
+        const uint16_t* crow = C + (size_t)(st * 32 + col) * hh;
+        uint2 cf[kMaxK8];
+#pragma unroll
+        for (int kk = 0; kk < kMaxK8; ++kk)
+          if (kk < nk) cf[kk] = *(const uint2*)(crow + 8 * kk + kq);
+        float16_t acc = {};
+#pragma unroll
+        for (int kk = 0; kk < kMaxK8; ++kk)
+          if (kk < nk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4_t, cf[kk]),
+                                                           __builtin_bit_cast(short4_t, xf[kk]), acc, 0, 0, 0);
+        // D[row = sub-key][col]; lane holds col = lane % 32, rows 8*(i/4) + 4*(lane/32) + i%4
+        if (col < 2) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            sc[(col * 2 + half) * (s + 1) + st * 32 + row] = acc[i];
+          }
+        }
+      }
+    }
+  } else {
+    for (int p = tid; p < 4 * s; p += kThreads) {
+      const int c = p / s, m = p % s, half = c & 1;
+      const void* x = c < 2 ? A.k : A.q;
+      const size_t xo = (size_t)u * d_k + (size_t)half * hh;
+      const size_t co = ((size_t)head * 2 + half) * (size_t)s * hh + (size_t)m * hh;
+      float acc = 0.f;
+      for (int i = 0; i < hh; ++i) acc = fmaf(ld_in<BF16>(x, xo + i), ld_in<BF16>(A.subkeys, co + i), acc);
+      sc[c * (s + 1) + m] = acc;
+    }
   }
   __syncthreads();
   // 2. per-half top-kappa, one wave per (vector, half)

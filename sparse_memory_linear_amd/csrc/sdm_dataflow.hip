@@ -58,6 +58,7 @@ constexpr int kWaves = 16;         // meta, 2 gather, store, 12 compute waves
 constexpr int kGatherWaves = 2;    // waves 1 and 3
 constexpr int kGatherDepth = 3;    // own gather steps in flight per gather wave
 constexpr int kMetaDepth = 16;     // meta batches in flight (3 loads each)
+constexpr int kMetaRing = 64;      // metadata ring slots
 constexpr int kGatherGroup = 4;    // tokens per gather step
 constexpr int kStoreBatch = 8;     // tokens per store step (watermark granularity)
 constexpr size_t kLdsBudget = 156 * 1024;
@@ -713,10 +714,12 @@ bool pipe_fits(const sdm_shape& S, int rb, PipeCfg* c) {
   const size_t tslot = 12 + (size_t)E * rb + (size_t)S.W * 4 + (size_t)cpr * 4;  // token ring slot
   const size_t mslot = (size_t)E * 8 + (size_t)vw * 4;                          // metadata ring slot
   const size_t fixed = kCtrlWords * 4;
-  // the longest token ring that fits, then the longest metadata ring
+  // The longest token ring that fits, with a metadata ring of 64 slots (or 32 if only that
+  // fits). A longer metadata ring lets the metadata wave run far ahead and take vector-memory
+  // issue slots from the gathers: measured slower at 128 slots and at 32.
   int ring = 0, mring = 0;
   for (int r = 256; r >= 64 && !ring; r /= 2)
-    for (int m = 256; m >= 64; m /= 2) {
+    for (int m = kMetaRing; m >= kMetaRing / 2; m /= 2) {
       const int w = std::min(kMaxWin, r / 2);
       // progress: a blocked gather step fits between the store wave and the window, and a
       // metadata batch between the store wave and the end of the metadata ring

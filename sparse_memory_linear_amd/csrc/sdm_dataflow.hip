@@ -56,8 +56,8 @@ constexpr uint32_t kInvalid = 0x40000000u;
 constexpr uint32_t kSlotMask = 0x3FFFFu;
 constexpr int kWaves = 16;         // meta, 2 gather, store, 12 compute waves
 constexpr int kGatherWaves = 2;    // waves 1 and 3
-constexpr int kGatherDepth = 3;    // own gather steps in flight per gather wave
-constexpr int kMetaDepth = 16;     // meta batches in flight (3 loads each)
+constexpr int kGatherRegs = 80;    // registers a gather wave spends on rows in flight
+constexpr int kMetaDepth = 4;      // meta batches in flight (3 loads each)
 constexpr int kMetaRing = 64;      // metadata ring slots
 constexpr int kGatherGroup = 4;    // tokens per gather step
 constexpr int kStoreBatch = 8;     // tokens per store step (watermark granularity)
@@ -147,33 +147,63 @@ struct PipeArgs {
   float* o;            // [U][T][d_v]
   unsigned long long* err;
   int U, T, W, R, E, d_v, P;
-  int S, SM, win, tpb, vw, rowbytes;
+  int S, RS, SM, win, tpb, vw, rowbytes;
   int pack2;  // two tokens' write rows per store instruction
+  int nh;     // compute passes per half wave: ceil(max(W, R) / (32 / lanes per row))
   long long N;
 };
 
-template <typename MemT>
-struct Pair;  // 8 bytes of a row: 2 float32 or 4 bf16 columns
+// The LB bytes of a row that one lane moves (8 or 16): LB/4 words of float32 or bf16 pairs.
+template <int LB>
+struct LaneVec;
 template <>
-struct Pair<float> {
-  static constexpr int kCols = 2;
-  __device__ static void unpack(u2 w, float* x) {
-    x[0] = __uint_as_float(w[0]);
-    x[1] = __uint_as_float(w[1]);
-  }
-  __device__ static u2 pack(const float* x) { return u2{__float_as_uint(x[0]), __float_as_uint(x[1])}; }
+struct LaneVec<8> {
+  using V = u2;
 };
 template <>
-struct Pair<uint16_t> {
-  static constexpr int kCols = 4;
-  __device__ static void unpack(u2 w, float* x) {
-    x[0] = bf16lo(w[0]);
-    x[1] = bf16hi(w[0]);
-    x[2] = bf16lo(w[1]);
-    x[3] = bf16hi(w[1]);
-  }
-  __device__ static u2 pack(const float* x) { return u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}; }
+struct LaneVec<16> {
+  using V = u4;
 };
+
+template <typename MemT, int LB>
+struct Lane {
+  using V = typename LaneVec<LB>::V;
+  static constexpr int kWords = LB / 4;
+  static constexpr int kCols = LB / (int)sizeof(MemT);
+  __device__ static void unpack(V w, float* x) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) {
+      if constexpr (sizeof(MemT) == 2) {
+        x[2 * i] = bf16lo(w[i]);
+        x[2 * i + 1] = bf16hi(w[i]);
+      } else {
+        x[i] = __uint_as_float(w[i]);
+      }
+    }
+  }
+  __device__ static V pack(const float* x) {
+    V w;
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) {
+      if constexpr (sizeof(MemT) == 2) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      else w[i] = __float_as_uint(x[i]);
+    }
+    return w;
+  }
+};
+
+__device__ __forceinline__ void buf_load(u2& d, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  d = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+}
+__device__ __forceinline__ void buf_load(u4& d, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  d = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(u2 d, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(d, rs, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(u4 d, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(d, rs, off, 0, 0);
+}
 
 __device__ __forceinline__ int lds_ld(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -207,21 +237,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Control words at the start of LDS.
-enum { kClaim = 0, kMetaDone = 1, kWm = 2, kStoreIssued = 3, kAbort = 4, kCtrlWords = 16 };
+enum { kMetaDone = 1, kWm = 2, kStoreIssued = 3, kAbort = 4, kCtrlWords = 16 };
 
 // Workgroup of kWaves waves serving one (unit, column block) of RB bytes per row. Lane
-// layout of row work: LPC = RB/8 lanes (8 bytes each) per row, G = 64/LPC rows per pass;
+// layout of row work: LPC = RB/LB lanes (LB bytes each) per row, G = 64/LPC rows per pass;
 // NP passes cover max(W, R) rows, NG passes cover the E = W + R rows gathered per token.
-template <typename MemT, typename InT, int RB, int NP, int NG>
+template <typename MemT, typename InT, int RB, int LB, int NP, int NG>
 __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
-  using PT = Pair<MemT>;
+  using PT = Lane<MemT, LB>;
+  using LV = typename PT::V;
   constexpr int CPL = PT::kCols;              // columns per lane
-  constexpr int LPC = RB / 8;
+  constexpr int LPC = RB / LB;
   constexpr int G = 64 / LPC;
   constexpr int CPR = RB / (int)sizeof(MemT);  // columns per row block
+  // outputs leave in pieces of OPL float32 columns, PPT pieces per token
+  constexpr int OPL = CPR < 4 ? CPR : 4;
+  constexpr int PPT = CPR / OPL;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int T = A.T, W = A.W, R = A.R, E = A.E, S = A.S, smask = A.S - 1, win = A.win;
+  const int T = A.T, W = A.W, R = A.R, E = A.E, S = A.S, smask = A.S - 1, win = A.win, rmask = A.RS - 1;
   const int SM = A.SM, mmask = A.SM - 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane / LPC, l = lane % LPC;
@@ -236,9 +270,12 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
   int* g_tok = ctrl + kCtrlWords;  // [S] token whose rows are gathered in ring slot i
   int* f_tok = g_tok + S;          // [S] token whose new write rows are in slot i
   int* c_tok = f_tok + S;          // [S] token whose compute is complete in slot i
-  // token ring (S slots): gathered rows, new write rows, write slots, output block
-  unsigned char* rows = (unsigned char*)(c_tok + S);                 // [S][E][RB]
-  int32_t* slot_w = (int32_t*)(rows + (size_t)S * E * RB);           // [S][W] slot of each write row, -1 = skip
+  // token ring (S slots): gathered then new write rows, write slots, output block; the
+  // gathered read rows live in a shorter ring of RS slots (they are dead once the token's
+  // compute is done, and a gather runs at most RS tokens ahead of the stores)
+  unsigned char* wrows = (unsigned char*)(c_tok + S);                // [S][W][RB]
+  unsigned char* rrows = wrows + (size_t)S * W * RB;                 // [RS][R][RB]
+  int32_t* slot_w = (int32_t*)(rrows + (size_t)A.RS * R * RB);       // [S][W] slot of each write row, -1 = skip
   float* obuf = (float*)(slot_w + (size_t)S * W);                    // [S][CPR]
   // metadata ring (SM slots): packed slot words, weights, v columns and gates
   uint32_t* pk_r = (uint32_t*)(obuf + (size_t)S * CPR);             // [SM][E]
@@ -251,8 +288,9 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 
   const size_t ut0 = (size_t)u * T;
   const uint32_t oob = 0x7FFFFFF0u;  // buffer offset past the end: loads give 0, stores are dropped
-  const uint32_t colb = (uint32_t)(cb * RB + l * 8);
-  auto row_ptr = [&](int sl, int e) -> u2* { return (u2*)(rows + ((size_t)sl * E + e) * RB + l * 8); };
+  const uint32_t colb = (uint32_t)(cb * RB + l * LB);
+  auto wrow_ptr = [&](int sl, int j) -> LV* { return (LV*)(wrows + ((size_t)sl * W + j) * RB + l * LB); };
+  auto rrow_ptr = [&](int rl, int r) -> LV* { return (LV*)(rrows + ((size_t)rl * R + r) * RB + l * LB); };
   auto give_up = [&]() {
     if (lane == 0) {
       lds_st(&ctrl[kAbort], 1);
@@ -326,12 +364,16 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 
   if (wave == 1 || wave == 3) {
     // ================================================================ gather waves
-    // Table rows of each token's slots, GB tokens per step, loaded into registers (8 bytes a
-    // lane, one lane per row block) and written to the ring GD own steps later. The two
+    // Table rows of each token's slots, GB tokens per step, loaded into registers (LB bytes
+    // a lane) and written to the rings GD own steps later. The two
     // waves take alternate steps. Slots with a writer inside the window come from the ring
     // instead: their loads (and those of slots outside [0, N)) are out of range and give 0.
     constexpr int GB = kGatherGroup;
-    constexpr int GD = kGatherDepth;
+    // own steps in flight: as many as kGatherRegs row registers hold, 3 to 6 (2 for four
+    // passes per token)
+    constexpr int GD0 = kGatherRegs / (GB * NG * (LB / 4));
+    constexpr int GDmin = NG >= 4 ? 2 : 3;
+    constexpr int GD = GD0 < GDmin ? GDmin : (GD0 > 6 ? 6 : GD0);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (char*)A.M + (size_t)u * (size_t)A.N * A.rowbytes, (short)0, (int)((size_t)A.N * A.rowbytes), 0x00020000);
     const int nsteps = (T + GB - 1) / GB;
@@ -341,10 +383,11 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     int done = -1;  // own step index last written to the ring
     bool aborted = false;
     long long budget = kSpinBudget;
-    u2 data[GD][GB][NG];
-    auto ready = [&](int tl) { return m_seen >= tl && wm_seen >= tl - 1 - win && s_seen >= tl - S + win; };
+    LV data[GD][GB][NG];
+    // metadata in, every token older than the window stored, ring slots free (RS <= S - win)
+    auto ready = [&](int tl) { return m_seen >= tl && wm_seen >= tl - 1 - win && s_seen >= tl - A.RS; };
     // own step i (held in d) into the ring, unless already written
-    auto complete = [&](int i, const u2 (&d)[GB][NG]) {
+    auto complete = [&](int i, const LV (&d)[GB][NG]) {
       if (i <= done) return;
       const int t0 = (gw + i * kGatherWaves) * GB;
 #pragma unroll
@@ -354,7 +397,8 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 #pragma unroll
           for (int n = 0; n < NG; ++n) {
             const int e = n * G + g;
-            if (e < E) *row_ptr(t & smask, e) = d[tt][n];
+            if (e < W) *wrow_ptr(t & smask, e) = d[tt][n];
+            else if (e < E) *rrow_ptr(t & rmask, e - W) = d[tt][n];
           }
         }
       }
@@ -362,7 +406,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       if (lane < GB && t0 + lane < T) lds_st(&g_tok[(t0 + lane) & smask], t0 + lane);
       done = i;
     };
-    auto issue = [&](int i, u2 (&d)[GB][NG]) {
+    auto issue = [&](int i, LV (&d)[GB][NG]) {
       const int t0 = (gw + i * kGatherWaves) * GB;
 #pragma unroll
       for (int tt = 0; tt < GB; ++tt) {
@@ -374,7 +418,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
           const int e = n * G + g;
           const uint32_t p = (tv && e < E) ? pk_r[(size_t)ml * E + e] : kInvalid;
           const uint32_t off = (p & (kCoded | kInvalid)) ? oob : (p & kSlotMask) * (uint32_t)A.rowbytes + colb;
-          d[tt][n] = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+          buf_load(d[tt][n], rs, off);
         }
       }
     };
@@ -417,8 +461,6 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (wave == 1) {
-    }
     if (aborted) give_up();
     return;
   }
@@ -450,36 +492,37 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
         __builtin_amdgcn_s_sleep(1);
       }
       acquire_lds();
-      // outputs of the whole batch in one instruction: lane k * LPC + l carries token k
-      float ov[CPL];
+      // outputs of the whole batch in one instruction: lane k * PPT + p carries piece p of
+      // token k
+      float ov[OPL];
       uint32_t ooff;
       {
-        const int k = lane / LPC, lo = lane % LPC;
+        const int k = lane / PPT, p = lane % PPT;
         const int t = t0 + k;
         const bool live = k < SB && t < T;
         const int sl = t & smask;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) ov[c] = live ? obuf[(size_t)sl * CPR + lo * CPL + c] : 0.f;
-        ooff = live ? (uint32_t)(((size_t)t * A.d_v + cb * CPR + lo * CPL) * 4) : oob;
+        for (int c = 0; c < OPL; ++c) ov[c] = live ? obuf[(size_t)sl * CPR + p * OPL + c] : 0.f;
+        ooff = live ? (uint32_t)(((size_t)t * A.d_v + cb * CPR + p * OPL) * 4) : oob;
       }
       if (A.pack2) {
         // two tokens per row instruction (the write rows of a token fill at most half a wave)
         constexpr int HG = G / 2;
         const int h = g / HG, j = g % HG;
-        u2 val[SB / 2];
+        LV val[SB / 2];
         uint32_t off[SB / 2];
 #pragma unroll
         for (int m = 0; m < SB / 2; ++m) {
           const int t = t0 + 2 * m + h;
           const int sl = t & smask;
           const int n = (t < T && j < W) ? slot_w[(size_t)sl * W + j] : -1;
-          val[m] = *row_ptr(sl, j < W ? j : 0);
+          val[m] = *wrow_ptr(sl, j < W ? j : 0);
           off[m] = n >= 0 ? (uint32_t)n * (uint32_t)A.rowbytes + colb : oob;
         }
 #pragma unroll
-        for (int m = 0; m < SB / 2; ++m) __builtin_amdgcn_raw_buffer_store_b64(val[m], rs, off[m], 0, 0);
+        for (int m = 0; m < SB / 2; ++m) buf_store(val[m], rs, off[m]);
       } else {
-        u2 val[SB][NP];
+        LV val[SB][NP];
         uint32_t off[SB][NP];
 #pragma unroll
         for (int k = 0; k < SB; ++k) {
@@ -489,16 +532,16 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
           for (int i = 0; i < NP; ++i) {
             const int j = i * G + g;
             const int n = (t < T && j < W) ? slot_w[(size_t)sl * W + j] : -1;
-            val[k][i] = *row_ptr(sl, j < W ? j : W - 1);
+            val[k][i] = *wrow_ptr(sl, j < W ? j : W - 1);
             off[k][i] = n >= 0 ? (uint32_t)n * (uint32_t)A.rowbytes + colb : oob;
           }
         }
 #pragma unroll
         for (int k = 0; k < SB; ++k)
 #pragma unroll
-          for (int i = 0; i < NP; ++i) __builtin_amdgcn_raw_buffer_store_b64(val[k][i], rs, off[k][i], 0, 0);
+          for (int i = 0; i < NP; ++i) buf_store(val[k][i], rs, off[k][i]);
       }
-      if constexpr (CPL == 4) {
+      if constexpr (OPL == 4) {
         u4 o4 = {__float_as_uint(ov[0]), __float_as_uint(ov[1]), __float_as_uint(ov[2]), __float_as_uint(ov[3])};
         __builtin_amdgcn_raw_buffer_store_b128(o4, ro, ooff, 0, 0);
       } else {
@@ -519,13 +562,21 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
   }
 
   // ================================================================== compute waves
+  // The lower half of the wave holds the token's write rows, the upper half its read rows
+  // (GH rows per pass, NH passes). One butterfly inside each half gives at once the weighted
+  // read of the write rows (lower half, the residual's read before decay) and the weighted
+  // read of the read rows (upper half). A read row that the token itself writes is taken
+  // after the write, with a second butterfly, only when the token has one.
+  // Compute wave c takes tokens c, c + NC, c + 2 NC, ...
+  constexpr int GH = 32 / LPC;
+  constexpr int NH = 2 * NP;  // passes per half at most; A.nh of them are live
+  constexpr int NC = kWaves - 4;
+  const int hh = lane >> 5;
+  const int gh = (lane & 31) / LPC;
+  const int nrows = hh ? R : W, rbase = hh ? W : 0, nh = A.nh;
   bool aborted = false;
-  while (!aborted) {
-    int t = 0;
-    if (lane == 0) t = atomicAdd(&ctrl[kClaim], 1);
-    t = __builtin_amdgcn_readfirstlane(t);
-    if (t >= T) break;
-    const int sl = t & smask;
+  for (int t = wave - 4; t < T && !aborted; t += NC) {
+    const int sl = t & smask, rl = t & rmask;
     {
       long long budget = kSpinBudget;
       while (lds_ld(&g_tok[sl]) != t) {
@@ -542,22 +593,23 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     const uint32_t* pks = pk_r + (size_t)ml * E;
     const float* wts = wt_r + (size_t)ml * E;
     const uint32_t* vab = vab_r + (size_t)ml * A.vw;
-    uint32_t pw[NP], pr[NP];
-    float aw[NP], ur[NP];
-    u2 xw[NP], xr[NP];
+    uint32_t pw[NH];
+    float wv[NH];
+    LV xv[NH];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int j = i * G + g;
-      pw[i] = j < W ? pks[j] : kInvalid;
-      pr[i] = j < R ? pks[W + j] : kInvalid;
-      aw[i] = j < W ? wts[j] : 0.f;
-      ur[i] = j < R ? wts[W + j] : 0.f;
-      // slots outside [0, N) carry no weight
-      if ((pw[i] & (kCoded | kInvalid)) == kInvalid) aw[i] = 0.f;
-      if ((pr[i] & (kCoded | kInvalid)) == kInvalid) ur[i] = 0.f;
-      xw[i] = *row_ptr(sl, j < W ? j : 0);
-      xr[i] = *row_ptr(sl, W + (j < R ? j : 0));
+    for (int i = 0; i < NH; ++i) {
+      const int j = i * GH + gh;
+      const bool live = i < nh && j < nrows;
+      const int jl = live ? j : 0;
+      pw[i] = pks[rbase + jl];
+      wv[i] = wts[rbase + jl];
+      // rows of this token's ring slot, all written by the gather (0 where not loaded)
+      xv[i] = hh ? *rrow_ptr(rl, jl) : *wrow_ptr(sl, jl);
+      if (!live) pw[i] = kInvalid;
     }
+#pragma unroll
+    for (int i = 0; i < NH; ++i)
+      if ((pw[i] & (kCoded | kInvalid)) == kInvalid) wv[i] = 0.f;  // slots outside [0, N) carry no weight
     float vv[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -571,18 +623,20 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     const float al = __uint_as_float(vab[A.vw - 2]);
     const float be = __uint_as_float(vab[A.vw - 1]);
     // wait for the writers inside the window to publish their new rows
-    {
+    bool fwd = false;
+#pragma unroll
+    for (int i = 0; i < NH; ++i) fwd |= (pw[i] & kCoded) && ((pw[i] >> 24) & 127) > 0;
+    bool own = false;  // a read row written by this token
+#pragma unroll
+    for (int i = 0; i < NH; ++i) own |= (pw[i] & kCoded) && ((pw[i] >> 24) & 127) == 0;
+    if (ballot(fwd)) {
       long long budget = kSpinBudget;
       while (true) {
         bool wait = false;
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
+        for (int i = 0; i < NH; ++i) {
           if (pw[i] & kCoded) {
             const int d = (pw[i] >> 24) & 127;
-            wait |= lds_ld(&f_tok[(sl - d) & smask]) != t - d;
-          }
-          if (pr[i] & kCoded) {
-            const int d = (pr[i] >> 24) & 127;
             if (d > 0) wait |= lds_ld(&f_tok[(sl - d) & smask]) != t - d;
           }
         }
@@ -594,98 +648,102 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
         __builtin_amdgcn_s_sleep(1);
       }
       if (aborted) break;
-    }
-    acquire_lds();
+      acquire_lds();
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      if (pw[i] & kCoded) {
-        const int d = (pw[i] >> 24) & 127, jj = (pw[i] >> 18) & 63;
-        xw[i] = *row_ptr((sl - d) & smask, jj);
+      for (int i = 0; i < NH; ++i) {
+        if (pw[i] & kCoded) {
+          const int d = (pw[i] >> 24) & 127, jj = (pw[i] >> 18) & 63;
+          if (d > 0) xv[i] = *wrow_ptr((sl - d) & smask, jj);
+        }
       }
     }
-    // decayed weighted read of the write slots
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      float x[CPL];
-      PT::unpack(xw[i], x);
+    for (int i = 0; i < NH; ++i) {
+      if (i < nh) {
+        float x[CPL];
+        PT::unpack(xv[i], x);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(aw[i], x[c], acc[c]);
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wv[i], x[c], acc[c]);
+      }
     }
 #pragma unroll
-    for (int s = LPC; s < 64; s <<= 1)
+    for (int s = LPC; s < 32; s <<= 1)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[c] += shfl_xor_f32(acc[c], s);
-    float dl[CPL];
+    // lower half: delta = beta (v - alpha * read of the write rows); new write rows
+    if (hh == 0) {
+      float dl[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) dl[c] = be * (vv[c] - al * acc[c]);
-    // gated delta write: new rows replace the write rows of this token's slot
+      for (int c = 0; c < CPL; ++c) dl[c] = be * (vv[c] - al * acc[c]);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int j = i * G + g;
-      float x[CPL], y[CPL];
-      PT::unpack(xw[i], x);
+      for (int i = 0; i < NH; ++i) {
+        const int j = i * GH + gh;
+        if (i < nh && j < W) {
+          float x[CPL], y[CPL];
+          PT::unpack(xv[i], x);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], aw[i] * dl[c]);
-      if (j < W) {
-        *row_ptr(sl, j) = PT::pack(y);
-        if (l == 0) slot_w[(size_t)sl * W + j] = (pw[i] & (kCoded | kInvalid)) == kInvalid ? -1 : (int)(pw[i] & kSlotMask);
-        // a row rewritten by the next token goes out in the same store instruction as that
-        // token's, where lane order is not defined: only the later token stores it
-        if (A.pack2 && (t & 1) && l == 0 && (pw[i] & kCoded) && ((pw[i] >> 24) & 127) == 1)
-          slot_w[(size_t)((sl - 1) & smask) * W + ((pw[i] >> 18) & 63)] = -1;
+          for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], wv[i] * dl[c]);
+          *wrow_ptr(sl, j) = PT::pack(y);
+          if (l == 0) slot_w[(size_t)sl * W + j] = (pw[i] & (kCoded | kInvalid)) == kInvalid ? -1 : (int)(pw[i] & kSlotMask);
+          // a row rewritten by the next token goes out in the same store instruction as that
+          // token's, where lane order is not defined: only the later token stores it
+          if (A.pack2 && (t & 1) && l == 0 && (pw[i] & kCoded) && ((pw[i] >> 24) & 127) == 1)
+            slot_w[(size_t)((sl - 1) & smask) * W + ((pw[i] >> 18) & 63)] = -1;
+        }
       }
     }
-    release_lds();
-    if (lane == 0) lds_st(&f_tok[sl], t);
-    // weighted read of the R slots after the write
+    // upper half: read rows this token wrote, at their new values (own rows written just
+    // above by this wave: its LDS accesses take effect in order)
+    if (ballot(own)) {
+      float cr[CPL];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      if (pr[i] & kCoded) {
-        const int d = (pr[i] >> 24) & 127, jj = (pr[i] >> 18) & 63;
-        xr[i] = *row_ptr((sl - d) & smask, jj);
+      for (int c = 0; c < CPL; ++c) cr[c] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        if ((pw[i] & kCoded) && ((pw[i] >> 24) & 127) == 0) {
+          float y[CPL];
+          PT::unpack(*wrow_ptr(sl, (pw[i] >> 18) & 63), y);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) cr[c] = fmaf(wv[i], y[c], cr[c]);
+        }
       }
+#pragma unroll
+      for (int s = LPC; s < 32; s <<= 1)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) cr[c] += shfl_xor_f32(cr[c], s);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += cr[c];
     }
-    float ov[CPL];
+    if (hh == 1 && gh == 0) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) ov[c] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      float y[CPL];
-      PT::unpack(xr[i], y);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) ov[c] = fmaf(ur[i], y[c], ov[c]);
-    }
-#pragma unroll
-    for (int s = LPC; s < 64; s <<= 1)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) ov[c] += shfl_xor_f32(ov[c], s);
-    if (g == 0) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) obuf[(size_t)sl * CPR + l * CPL + c] = ov[c];
+      for (int c = 0; c < CPL; ++c) obuf[(size_t)sl * CPR + l * CPL + c] = acc[c];
     }
     // slot indices outside [0, N) were skipped; the first column block counts them
     if (cb == 0) {
       int bad = 0;
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        const int j = i * G + g;
-        bad += popc64(ballot(l == 0 && j < W && (pw[i] & (kCoded | kInvalid)) == kInvalid));
-        bad += popc64(ballot(l == 0 && j < R && (pr[i] & (kCoded | kInvalid)) == kInvalid));
+      for (int i = 0; i < NH; ++i) {
+        const int j = i * GH + gh;
+        bad += popc64(ballot(l == 0 && i < nh && j < nrows && (pw[i] & (kCoded | kInvalid)) == kInvalid));
       }
       if (bad && lane == 0) atomicAdd(A.err, (unsigned long long)bad);
     }
+    // new rows and output published together
     release_lds();
-    if (lane == 0) lds_st(&c_tok[sl], t);
+    if (lane == 0) {
+      lds_st(&f_tok[sl], t);
+      lds_st(&c_tok[sl], t);
+    }
   }
   if (aborted) give_up();
 }
 
 // ------------------------------------------------------------------ configuration
 struct PipeCfg {
-  int rb, P, S, SM, win, tpb, vw, np, ng;
+  int rb, lb, P, S, RS, SM, win, tpb, vw, np, ng, nh;
   size_t lds;
 };
 
@@ -695,73 +753,95 @@ int pow2_floor(int x) {
   return p;
 }
 
-// Ring and batch sizes for a block width of rb bytes per row; false if it does not fit.
-bool pipe_fits(const sdm_shape& S, int rb, PipeCfg* c) {
+// Ring and batch sizes for a block width of rb bytes per row moved in lanes of lb bytes;
+// false if it does not fit.
+bool pipe_fits(const sdm_shape& S, int rb, int lb, PipeCfg* c) {
   const int msz = (int)dtype_size(S.mem_dtype), isz = (int)dtype_size(S.in_dtype);
   const int rowbytes = S.d_v * msz;
-  if (rowbytes % rb) return false;
+  if (rowbytes % rb || rb % lb) return false;
   const int E = S.W + S.R;
-  const int lpc = rb / 8, G = 64 / lpc;
+  const int lpc = rb / lb, G = 64 / lpc;
   const int np = (std::max(S.W, S.R) + G - 1) / G;
   int ng = (E + G - 1) / G;
   if (ng == 3) ng = 4;
   if (np > 2 || ng > 4 || np > ng) return false;
+  if (lb == 16 && ng > 2) return false;  // the gather registers would not fit
+  const int nh = (std::max(S.W, S.R) + G / 2 - 1) / (G / 2);  // compute passes per half wave
+  if (nh > 2 * np) return false;
   const int cpr = rb / msz;
   if ((cpr * isz) % 4) return false;
   const int vw = cpr * isz / 4 + 2;
   if (vw > 64) return false;
   const int tpb = std::min(pow2_floor(std::max(1, 256 / E)), pow2_floor(64 / vw));
-  const size_t tslot = 12 + (size_t)E * rb + (size_t)S.W * 4 + (size_t)cpr * 4;  // token ring slot
-  const size_t mslot = (size_t)E * 8 + (size_t)vw * 4;                          // metadata ring slot
+  const size_t tslot = 12 + (size_t)S.W * rb + (size_t)S.W * 4 + (size_t)cpr * 4;  // token ring slot
+  const size_t rslot = (size_t)S.R * rb;                                          // read-row ring slot
+  const size_t mslot = (size_t)E * 8 + (size_t)vw * 4;                             // metadata ring slot
   const size_t fixed = kCtrlWords * 4;
-  // The longest token ring that fits, with a metadata ring of 64 slots (or 32 if only that
-  // fits). A longer metadata ring lets the metadata wave run far ahead and take vector-memory
-  // issue slots from the gathers: measured slower at 128 slots and at 32.
-  int ring = 0, mring = 0;
-  for (int r = 256; r >= 64 && !ring; r /= 2)
-    for (int m = kMetaRing; m >= kMetaRing / 2; m /= 2) {
+  // A metadata ring of 64 slots (32 only if nothing fits beside 64) and the longest token
+  // ring that fits beside it. A longer metadata ring lets the metadata wave run far ahead and
+  // take vector-memory issue slots from the gathers: measured slower at 128 slots, and slower
+  // at 32 even with a token ring twice as long.
+  int ring = 0, mring = 0, rring = 0;
+  size_t bytes = 0;
+  for (int m = kMetaRing; m >= kMetaRing / 2 && !ring; m /= 2)
+    for (int r = 256; r >= 64; r /= 2) {
       const int w = std::min(kMaxWin, r / 2);
-      // progress: a blocked gather step fits between the store wave and the window, and a
-      // metadata batch between the store wave and the end of the metadata ring
-      if (kGatherGroup + kStoreBatch > w || kGatherGroup + kStoreBatch > r - w) continue;
+      const int rr = pow2_floor(r - w);
+      // progress: a blocked gather step fits between the store wave and the window and
+      // between the store wave and the end of the read-row ring, and a metadata batch
+      // between the store wave and the end of the metadata ring
+      if (kGatherGroup + kStoreBatch > w || kGatherGroup + kStoreBatch > rr) continue;
       if (kGatherGroup + tpb + kStoreBatch > m) continue;
-      if (fixed + r * tslot + m * mslot <= kLdsBudget) {
+      const size_t b = fixed + r * tslot + rr * rslot + m * mslot;
+      if (b <= kLdsBudget) {
         ring = r;
         mring = m;
+        rring = rr;
+        bytes = b;
         break;
       }
     }
   if (!ring) return false;
   c->rb = rb;
+  c->lb = lb;
   c->P = rowbytes / rb;
   c->S = ring;
+  c->RS = rring;
   c->SM = mring;
   c->win = std::min(kMaxWin, ring / 2);
   c->tpb = tpb;
   c->vw = vw;
   c->np = np;
   c->ng = ng;
-  c->lds = fixed + ring * tslot + mring * mslot;
+  c->nh = nh;
+  c->lds = bytes;
   return true;
 }
 
-// Every workgroup issues about the same number of row requests per token whatever its block
-// width, and one CU serves a bounded rate of them; so pick the width that needs the fewest
-// rounds of workgroups over the CUs, and the narrowest among those (more CUs, longer ring).
+// Each workgroup processes every token of its unit, so its time per token bounds the whole
+// unit: pick the block width that needs the fewest rounds of workgroups over the CUs. With
+// one round and CUs to spare, narrower blocks (more workgroups, each with less arithmetic per
+// token) are faster; once the chip is full, 16-byte lanes (half the row requests of 8-byte
+// lanes for the same bytes) are.
 bool pipe_config(const sdm_shape& S, int cus, PipeCfg* out) {
   bool any = false;
-  long long best = 0;
+  long long best_rounds = 0, best_wgs = 0;
   const long long U = (long long)S.B * S.H;
-  for (int rb = 8; rb <= 32; rb *= 2) {
-    PipeCfg c;
-    if (!pipe_fits(S, rb, &c) || c.S < 64) continue;
-    const long long rounds = (U * c.P + cus - 1) / cus;  // one 16-wave workgroup per CU
-    if (!any || rounds < best) {
-      *out = c;
-      best = rounds;
-      any = true;
+  for (int lb = 16; lb >= 8; lb /= 2)
+    for (int rb = lb; rb <= 32; rb *= 2) {
+      PipeCfg c;
+      if (!pipe_fits(S, rb, lb, &c) || c.S < 64) continue;
+      const long long wgs = U * c.P;
+      const long long rounds = (wgs + cus - 1) / cus;  // one 16-wave workgroup per CU
+      const bool better = !any || rounds < best_rounds ||
+                          (rounds == best_rounds && wgs <= cus && best_wgs <= cus && wgs > best_wgs);
+      if (better) {
+        *out = c;
+        best_rounds = rounds;
+        best_wgs = wgs;
+        any = true;
+      }
     }
-  }
   return any;
 }
 
@@ -775,26 +855,37 @@ int device_cus() {
   return cus;
 }
 
-template <typename MemT, typename InT, int RB>
+template <typename MemT, typename InT, int RB, int LB>
 hipError_t pipe_launch_rb(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
   const int groups = (A.U + 7) / 8;
   dim3 grid(8 * groups * A.P);
   dim3 block(kWaves * 64);
-  if (c.np == 1 && c.ng == 1) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 1, 1>), grid, block, c.lds, st, A);
-  else if (c.np == 1 && c.ng == 2) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 1, 2>), grid, block, c.lds, st, A);
-  else if (c.np == 2 && c.ng == 2) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 2, 2>), grid, block, c.lds, st, A);
-  else if (c.np == 2 && c.ng == 4) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 2, 4>), grid, block, c.lds, st, A);
-  else if (c.np == 1 && c.ng == 4) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, 1, 4>), grid, block, c.lds, st, A);
-  else return hipErrorInvalidValue;
+  if (c.np == 1 && c.ng == 1) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, LB, 1, 1>), grid, block, c.lds, st, A);
+  else if (c.np == 1 && c.ng == 2) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, LB, 1, 2>), grid, block, c.lds, st, A);
+  else if (c.np == 2 && c.ng == 2) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, LB, 2, 2>), grid, block, c.lds, st, A);
+  else if constexpr (LB == 8) {
+    if (c.np == 2 && c.ng == 4) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, LB, 2, 4>), grid, block, c.lds, st, A);
+    else if (c.np == 1 && c.ng == 4) hipLaunchKernelGGL((pipe_kernel<MemT, InT, RB, LB, 1, 4>), grid, block, c.lds, st, A);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <typename MemT, typename InT>
 hipError_t pipe_launch(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
+  if (c.lb == 16) {
+    switch (c.rb) {
+      case 16: return pipe_launch_rb<MemT, InT, 16, 16>(A, c, st);
+      case 32: return pipe_launch_rb<MemT, InT, 32, 16>(A, c, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (c.rb) {
-    case 8: return pipe_launch_rb<MemT, InT, 8>(A, c, st);
-    case 16: return pipe_launch_rb<MemT, InT, 16>(A, c, st);
-    case 32: return pipe_launch_rb<MemT, InT, 32>(A, c, st);
+    case 8: return pipe_launch_rb<MemT, InT, 8, 8>(A, c, st);
+    case 16: return pipe_launch_rb<MemT, InT, 16, 8>(A, c, st);
+    case 32: return pipe_launch_rb<MemT, InT, 32, 8>(A, c, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -860,13 +951,15 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   A.d_v = S.d_v;
   A.P = c.P;
   A.S = c.S;
+  A.RS = c.RS;
   A.SM = c.SM;
   A.win = c.win;
   A.tpb = c.tpb;
   A.vw = c.vw;
   A.rowbytes = S.d_v * (int)dtype_size(S.mem_dtype);
   A.N = S.N;
-  A.pack2 = (c.np == 1 && 2 * S.W <= 64 / (c.rb / 8)) ? 1 : 0;
+  A.pack2 = (c.np == 1 && 2 * S.W <= 64 / (c.rb / c.lb)) ? 1 : 0;
+  A.nh = c.nh;
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
   if (mb && ib) return pipe_launch<uint16_t, uint16_t>(A, c, stream);
   if (mb && !ib) return pipe_launch<uint16_t, float>(A, c, stream);

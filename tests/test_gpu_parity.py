@@ -25,6 +25,14 @@ CASES = {
     # 8B-scale layer shape with repeated keys
     "layer_8b_T300": W_["layer_8b_long"].replace(B=1, H=2, T=300),
 }
+# Shapes with enough (batch, head) units that the recurrence takes 16-byte lanes (the small
+# cases above take 8-byte lanes): one pass per half wave with a float32 table, two passes
+# with 32-byte blocks, and 16-byte blocks. name -> (shape, units compared with the oracle)
+LANE_CASES = {
+    "small_lanes16": (W_["small"].replace(B=4, H=8, T=96), None),
+    "layer_1p4b_lanes16": (W_["layer_1p4b"].replace(B=32, H=4, T=24), [(0, 0), (5, 1), (17, 2), (31, 3)]),
+    "layer_8b_lanes16": (W_["layer_8b_long"].replace(B=2, H=8, T=80), None),
+}
 
 
 @pytest.fixture(scope="module")
@@ -152,7 +160,7 @@ def test_recurrent_parity(sdm, name):
 
 
 # ----------------------------------------------------------------------------- forward
-def run_forward_and_compare(sdm, sh, inp, name):
+def run_forward_and_compare(sdm, sh, inp, name, units=None):
     import torch
     dev = upload(inp, sh)
     S = lib_shape(sh)
@@ -169,25 +177,26 @@ def run_forward_and_compare(sdm, sh, inp, name):
     tol = tolerance(sh)
     worst_o = worst_m = 0.0
     ties = cascades = 0
-    for b in range(sh.B):
-        for h in range(sh.H):
-            U = unit_inputs(inp, sh, b, h)
-            r = O.forward_unit(U["q"], U["k"], U["v"], U["alpha"], U["beta"], U["C1"], U["C2"], U["M0"], sh.kappa,
-                               sh.W, sh.R, sh.mem_dtype)
-            tw, cw, fw = compare_indices(gw[b, h], r["widx"], U["k"], U["C1"], U["C2"], sh.N)
-            tr, cr, fr = compare_indices(gr[b, h], r["ridx"], U["q"], U["C1"], U["C2"], sh.N)
-            assert not fw and not fr, f"{name} unit ({b},{h}): {(fw + fr)[:3]}"
-            ties += tw + tr
-            first = min(cw + cr) if (cw or cr) else sh.T
-            if first < sh.T:
-                cascades += 1
-            if first > 0:
-                worst_o = max(worst_o, rel_err(go[b, h][:first], r["o"][:first]))
-            if first == sh.T:
-                worst_m = max(worst_m, rel_err(gM[b, h], r["M"]))
-                touched = np.zeros(sh.N, bool)
-                touched[gw[b, h].ravel()] = True
-                assert np.array_equal(gM[b, h][~touched], U["M0"][~touched])
+    if units is None:
+        units = [(b, h) for b in range(sh.B) for h in range(sh.H)]
+    for (b, h) in units:
+        U = unit_inputs(inp, sh, b, h)
+        r = O.forward_unit(U["q"], U["k"], U["v"], U["alpha"], U["beta"], U["C1"], U["C2"], U["M0"], sh.kappa,
+                           sh.W, sh.R, sh.mem_dtype)
+        tw, cw, fw = compare_indices(gw[b, h], r["widx"], U["k"], U["C1"], U["C2"], sh.N)
+        tr, cr, fr = compare_indices(gr[b, h], r["ridx"], U["q"], U["C1"], U["C2"], sh.N)
+        assert not fw and not fr, f"{name} unit ({b},{h}): {(fw + fr)[:3]}"
+        ties += tw + tr
+        first = min(cw + cr) if (cw or cr) else sh.T
+        if first < sh.T:
+            cascades += 1
+        if first > 0:
+            worst_o = max(worst_o, rel_err(go[b, h][:first], r["o"][:first]))
+        if first == sh.T:
+            worst_m = max(worst_m, rel_err(gM[b, h], r["M"]))
+            touched = np.zeros(sh.N, bool)
+            touched[gw[b, h].ravel()] = True
+            assert np.array_equal(gM[b, h][~touched], U["M0"][~touched])
     log(f"[forward] {name}: rel err o {worst_o:.2e} table {worst_m:.2e} (tol {tol}); tie positions {ties}, "
         f"units compared up to a set-changing tie: {cascades}")
     assert worst_o < tol and worst_m < tol
@@ -198,6 +207,13 @@ def test_forward_parity(sdm, name):
     sh = CASES[name]
     log(f"[forward] {name}")
     run_forward_and_compare(sdm, sh, SI.make_inputs(sh), name)
+
+
+@pytest.mark.parametrize("name", list(LANE_CASES))
+def test_forward_parity_lanes(sdm, name):
+    sh, units = LANE_CASES[name]
+    log(f"[forward] {name}")
+    run_forward_and_compare(sdm, sh, SI.make_inputs(sh), name, units)
 
 
 @pytest.mark.parametrize("kind", ["same_key", "q_is_k", "period"])

@@ -76,20 +76,19 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-// Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
+// Bitonic sort of one key per lane across the wave, descending (lane 0 = largest). At each
+// step a lane keeps the larger of its key and its partner's when it is the lower lane of a
+// descending block or the upper lane of an ascending one, else the smaller: one compare,
+// folded with that lane pattern, and one select per word. Equal keys are interchangeable.
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t key) {
   const int lane = lane_id();
 #pragma unroll
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t other = shfl_xor_u64(key, j);
-      bool desc_block = (lane & k) == 0;
-      bool lower = (lane & j) == 0;
-      bool take_max = (lower == desc_block);
-      uint64_t mx = key > other ? key : other;
-      uint64_t mn = key > other ? other : key;
-      key = take_max ? mx : mn;
+      const uint64_t other = shfl_xor_u64(key, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      key = ((key > other) == take_max) ? key : other;
     }
   }
   return key;
@@ -100,13 +99,9 @@ __device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t key) {
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      uint32_t other = shfl_xor_u32(key, j);
-      bool desc_block = (lane & k) == 0;
-      bool lower = (lane & j) == 0;
-      bool take_max = (lower == desc_block);
-      uint32_t mx = key > other ? key : other;
-      uint32_t mn = key > other ? other : key;
-      key = take_max ? mx : mn;
+      const uint32_t other = shfl_xor_u32(key, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      key = ((key > other) == take_max) ? key : other;
     }
   }
   return key;
@@ -138,10 +133,10 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
 template <int E>
 __device__ uint64_t wave_topk(const uint64_t (&keys)[E], int count, uint64_t* buf) {
   const int lane = lane_id();
-  uint64_t lmax = keys[0];
+  uint32_t lmax = (uint32_t)(keys[0] >> 32);  // score words only
 #pragma unroll
-  for (int e = 1; e < E; ++e) lmax = keys[e] > lmax ? keys[e] : lmax;
-  uint32_t sorted_hi = wave_sort_desc_u32((uint32_t)(lmax >> 32));
+  for (int e = 1; e < E; ++e) lmax = max(lmax, (uint32_t)(keys[e] >> 32));
+  uint32_t sorted_hi = wave_sort_desc_u32(lmax);
   uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)sorted_hi, count - 1);
   uint64_t masks[E];
   int total = 0;

@@ -166,7 +166,7 @@ def address(x, C1, C2, kappa: int, n_sel: int, block: int = 4096):
 
 
 # ----------------------------------------------------------------------------- recurrence
-def recurrence(M0: np.ndarray, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype: str):
+def recurrence(M0: np.ndarray, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype: str, decay: str = "written"):
     """Sparse gated delta write and weighted read, token by token, for one (batch, head).
 
     For token t with write slots n (weights a) and read slots m (weights u):
@@ -181,7 +181,16 @@ def recurrence(M0: np.ndarray, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype: 
                                                "Sparse retrieval", before the output norm)
 
     M0: [N, d_v] values of the initial table (PL §3 "Learned initial state").
+
+    decay="table" is the other reading of R1: alpha_t decays every row of the table (then
+    the rule is Gated DeltaNet's S_t = alpha_t (I - beta_t k k^T) S + beta_t k v^T with the
+    sparse key k = sum_j a_j e_{n_j}). Rows are rounded to the table dtype only when they
+    are written (READING R19): an untouched row holds its last written value times the
+    exact product of the gates since.
+
     Returns o [T, d_v] float64 and the final table [N, d_v] float64."""
+    if decay not in ("written", "table"):
+        raise ValueError(decay)
     M = np.array(M0, dtype=np.float64, copy=True)
     T = len(widx)
     d_v = M.shape[1]
@@ -192,23 +201,26 @@ def recurrence(M0: np.ndarray, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype: 
         old = M[n]
         rho = alpha[t] * (a @ old)
         delta = beta[t] * (v[t] - rho)
+        if decay == "table":
+            M *= alpha[t]
         M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)
         m = np.asarray(ridx[t])
         o[t] = np.asarray(rgt[t], dtype=np.float64) @ M[m]
     return o, M
 
 
-def forward_unit(q, k, v, alpha, beta, C1, C2, M0, kappa: int, W: int, R: int, mem_dtype: str) -> Dict:
+def forward_unit(q, k, v, alpha, beta, C1, C2, M0, kappa: int, W: int, R: int, mem_dtype: str,
+                 decay: str = "written") -> Dict:
     """One (batch, head) of the SDM layer forward: addresses from keys (writes) and
     queries (reads) (PL §3 "Sparse addressing"; READING R4: one sub-key pair per head
     serves both), then the recurrence from M0. All arguments are float64 values."""
     widx, wgt, wsc = address(k, C1, C2, kappa, W)
     ridx, rgt, rsc = address(q, C1, C2, kappa, R)
-    o, M = recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype)
+    o, M = recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, mem_dtype, decay)
     return {"o": o, "M": M, "widx": widx, "wgt": wgt, "wscore": wsc, "ridx": ridx, "rgt": rgt, "rscore": rsc}
 
 
-def forward(inputs: Dict[str, np.ndarray], shape, units=None, columns=None) -> Dict:
+def forward(inputs: Dict[str, np.ndarray], shape, units=None, columns=None, decay: str = "written") -> Dict:
     """Run ``forward_unit`` over the (b, h) units of a generated workload (``sdm_inputs``).
 
     ``units``: optional list of (b, h); ``columns``: optional slice of d_v columns (the
@@ -226,13 +238,14 @@ def forward(inputs: Dict[str, np.ndarray], shape, units=None, columns=None) -> D
         out[(b, h)] = forward_unit(
             widen(inputs["q"][b, h], ind), widen(inputs["k"][b, h], ind), widen(inputs["v"][b, h][:, cols], ind),
             inputs["alpha"][b, h].astype(np.float64), inputs["beta"][b, h].astype(np.float64),
-            sk[0], sk[1], M0, shape.kappa, shape.W, shape.R, md)
+            sk[0], sk[1], M0, shape.kappa, shape.W, shape.R, md, decay)
     return out
 
 
-def decode_step_unit(M, q, k, v, alpha, beta, C1, C2, kappa: int, W: int, R: int, mem_dtype: str):
+def decode_step_unit(M, q, k, v, alpha, beta, C1, C2, kappa: int, W: int, R: int, mem_dtype: str,
+                     decay: str = "written"):
     """One token of one unit on a table M that already holds earlier tokens' writes: the
     same rule as ``forward_unit`` with T = 1. Returns (o [d_v], new M)."""
     r = forward_unit(q[None], k[None], v[None], np.array([alpha]), np.array([beta]), C1, C2, M,
-                     kappa, W, R, mem_dtype)
+                     kappa, W, R, mem_dtype, decay)
     return r["o"][0], r["M"], r

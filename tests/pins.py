@@ -336,6 +336,71 @@ def pin_read_uses_queries_write_uses_keys(O):
         assert list(r["ridx"][t]) == brute_force_top(q[t], C1, C2, 2)
 
 
+# ----------------------------------------------------------------------------- whole-table decay
+def _sparse_slots(rng, T, N, n_sel):
+    """T rows of n_sel distinct slots in [0, N) with positive weights summing to 1."""
+    idx = np.array([rng.choice(N, n_sel, replace=False) for _ in range(T)])
+    w = rng.random((T, n_sel)) + 0.1
+    return idx, w / w.sum(1, keepdims=True)
+
+
+def pin_table_decay_is_sparse_gdn(O):
+    """The other reading of whether alpha decays the whole table (decay="table"): the
+    recurrence is then Gated DeltaNet in its textbook matrix form over all N slots, with key
+    and query vectors k_t = sum_j a_j e_{n_j}, q_t = sum_r u_r e_{m_r} (PL §2 "Gated
+    DeltaNet"; PL §3 "Connection to GDN")."""
+    rng = np.random.default_rng(21)
+    N, d_v, T, W, R = 20, 3, 40, 4, 3
+    widx, wgt = _sparse_slots(rng, T, N, W)
+    ridx, rgt = _sparse_slots(rng, T, N, R)
+    V = rng.standard_normal((T, d_v))
+    alpha = rng.uniform(0.3, 1.0, T)
+    beta = rng.random(T)
+    S0 = rng.standard_normal((N, d_v))
+    K, Q = np.zeros((T, N)), np.zeros((T, N))
+    for t in range(T):
+        K[t, widx[t]] = wgt[t]
+        Q[t, ridx[t]] = rgt[t]
+    o, M = O.recurrence(S0, widx, wgt, ridx, rgt, V, alpha, beta, "f64", decay="table")
+    o_ref, S_ref = dense_gdn(S0, K, V, Q, alpha, beta)
+    assert np.allclose(o, o_ref, rtol=0, atol=1e-12)
+    assert np.allclose(M, S_ref, rtol=0, atol=1e-12)
+
+
+def pin_table_decay_rows(O):
+    """decay="table" with a bf16 table: a row no token writes ends as M0 times the product
+    of all gates (not rounded: READING R19); rows the last token writes are bf16 values."""
+    rng = np.random.default_rng(22)
+    N, d_v, T, W, R = 64, 4, 30, 3, 2
+    widx, wgt = _sparse_slots(rng, T, N, W)
+    ridx, rgt = _sparse_slots(rng, T, N, R)
+    V = O.round_mem(rng.standard_normal((T, d_v)), "bf16")
+    alpha = 1 / (1 + np.exp(-(rng.standard_normal(T) + 3)))
+    beta = rng.random(T)
+    M0 = O.round_mem(rng.standard_normal((N, d_v)) * 0.02, "bf16")
+    _, M = O.recurrence(M0, widx, wgt, ridx, rgt, V, alpha, beta, "bf16", decay="table")
+    touched = set(int(n) for row in widx for n in row)
+    untouched = [n for n in range(N) if n not in touched]
+    assert untouched
+    assert np.allclose(M[untouched], M0[untouched] * np.prod(alpha), rtol=1e-13, atol=0)
+    last = widx[-1]
+    assert np.array_equal(O.round_bf16(M[last]), M[last])
+
+
+def pin_table_decay_alpha_one(O):
+    """With alpha = 1 nothing decays, so both readings of the decay scope give the same
+    result bit for bit (float32 and bf16 tables)."""
+    rng = np.random.default_rng(23)
+    s, d_k, d_v, T = 6, 6, 4, 25
+    x, C1, C2, v, _, beta = _rand_unit(rng, T, d_k, d_v, s)
+    q = rng.standard_normal((T, d_k))
+    for md in ("f32", "bf16"):
+        M0 = O.round_mem(rng.standard_normal((s * s, d_v)) * 0.02, md)
+        a = O.forward_unit(q, x, v, np.ones(T), beta, C1, C2, M0, 4, 3, 3, md)
+        b = O.forward_unit(q, x, v, np.ones(T), beta, C1, C2, M0, 4, 3, 3, md, decay="table")
+        assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["M"], b["M"])
+
+
 ALL_PINS = [
     pin_round_bf16,
     pin_pk_equals_brute_force,
@@ -351,4 +416,7 @@ ALL_PINS = [
     pin_state_carry,
     pin_columns_independent,
     pin_read_uses_queries_write_uses_keys,
+    pin_table_decay_is_sparse_gdn,
+    pin_table_decay_rows,
+    pin_table_decay_alpha_one,
 ]

@@ -49,6 +49,12 @@ MUTANTS = {
     "read_uses_write_weights": ("o[t] = np.asarray(rgt[t], dtype=np.float64) @ M[m]", "o[t] = np.asarray(wgt[t], dtype=np.float64)[:len(m)] @ M[m]"),
     # reads addressed by keys
     "reads_from_keys": ("ridx, rgt, rsc = address(q, C1, C2, kappa, R)", "ridx, rgt, rsc = address(k, C1, C2, kappa, R)"),
+    # whole-table decay applied after the write (written rows decay twice)
+    "table_decay_after_write": (
+        "        if decay == \"table\":\n            M *= alpha[t]\n        M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)\n",
+        "        M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)\n        if decay == \"table\":\n            M *= alpha[t]\n"),
+    # whole-table decay never applied
+    "table_decay_missing": ("            M *= alpha[t]\n", "            pass\n"),
     # per-half top-k keeps too few sub-keys
     "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
 }

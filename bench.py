@@ -12,7 +12,11 @@ resident in HBM before timing starts. ``roofline`` describes the recurrence kern
 (HBM-bound): algorithmic bytes per launch / its average event-timed duration, against
 MI355X's 8 TB/s. ``cpu_baseline`` times the float64 CPU oracle on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --decay the step runs the whole-table decay variant instead (decay state reset with
+the table every step; the recurrence call then includes the log-decay scan and the decay
+pass).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay]
 """
 from __future__ import annotations
 
@@ -129,6 +133,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(SI.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decay", action="store_true", help="whole-table decay variant")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -141,6 +146,8 @@ def main():
     sh = SI.WORKLOADS[args.workload]
     if sh.T == 1:
         return bench_decode(args, sh)
+    if args.decay:
+        args.no_cpu_baseline = True  # the oracle baseline times the default rule
     log(f"[bench] generating {sh.name} inputs")
     t0 = time.time()
     inp = SI.make_inputs(sh)
@@ -165,7 +172,11 @@ def main():
     M = torch.empty((sh.B, sh.H, sh.N, sh.d_v), dtype=mdt, device="cuda")
     o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
     shape = S.make_shape(sh.B, sh.H, sh.T, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
-    ws = torch.empty(S.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((S.workspace_bytes_decay if args.decay else S.workspace_bytes)(shape), dtype=torch.uint8,
+                     device="cuda")
+    if args.decay:
+        lam = torch.empty((sh.B, sh.H, sh.N), dtype=torch.float64, device="cuda")
+        lrun = torch.empty((sh.B, sh.H), dtype=torch.float64, device="cuda")
     widx = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.int32, device="cuda")
     wgt = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.float32, device="cuda")
     ridx = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.int32, device="cuda")
@@ -174,11 +185,16 @@ def main():
 
     def step(ev=None):
         S.init_from_M0(shape, M0, M)
+        if args.decay:
+            S.decay_state_init(shape, lam, lrun)
         S.address(shape, k, subkeys, sh.W, widx, wgt)
         S.address(shape, q, subkeys, sh.R, ridx, rgt)
         if ev is not None:
             ev[0].record(stream)
-        S.recurrent(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws)
+        if args.decay:
+            S.recurrent_decay(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, lam, lrun, o, ws)
+        else:
+            S.recurrent(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -203,7 +219,7 @@ def main():
     achieved = launch_bytes / (rec_ms / 1e3) / 1e9
     log(f"[bench] {ms_step:.3f} ms/step, recurrence {rec_ms:.3f} ms, {achieved:.1f} GB/s")
 
-    traffic = traffic_from_profile(sh.name)
+    traffic = None if args.decay else traffic_from_profile(sh.name)
     out = {
         "metric": METRIC,
         "value": value,
@@ -219,7 +235,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": sh.T, "N": sh.N, "d_k": sh.d_k, "d_v": sh.d_v,
                    "kappa": sh.kappa, "W": sh.W, "R": sh.R, "in_dtype": sh.in_dtype, "mem_dtype": sh.mem_dtype,
-                   "arith": "fp32"},
+                   "arith": "fp32", **({"decay": "whole table"} if args.decay else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "recurrence",
                      "ms_per_launch": rec_ms, "bytes_per_launch": launch_bytes},

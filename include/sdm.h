@@ -141,6 +141,55 @@ sdm_status sdm_decode_step(const sdm_shape* shape, const void* q, const void* k,
  * sdm_recurrent on this workspace) to *host_count after synchronising `stream`. */
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Whole-table decay variant. The calls above decay only the W written rows by alpha_t. If
+ * alpha_t instead decays every row of the table, as the dense state of Gated DeltaNet
+ * decays (PL §2 "Gated DeltaNet"; PL §3 "Connection to GDN": the rule is then Gated
+ * DeltaNet's with the sparse key sum_j wgt_j e_{widx_j}), the calls below apply that decay
+ * lazily and never touch a row no token addresses. Beside the table the state holds
+ *   lam  [B,H,N] float64: the cumulative log-decay (sum of log alpha) at each slot's last
+ *        write; a row's current value is its stored value times exp(lrun - lam)
+ *   lrun [B,H]   float64: the cumulative log-decay of all tokens so far
+ * Stored rows are rounded to mem_dtype when written; an untouched row's value is its
+ * stored value times the exact decay since (it is never stored again). A gate of 0 decays
+ * fully (log alpha is floored at -1000). These calls take the pipelined recurrence only:
+ * shapes it cannot take return SDM_ERR_UNSUPPORTED.
+ * --------------------------------------------------------------------------------------- */
+
+/* lam = 0 and lrun = 0: the state of a table fresh from sdm_init_from_M0. */
+sdm_status sdm_decay_state_init(const sdm_shape* shape, double* lam, double* lrun, void* stream);
+
+/* Workspace bytes of sdm_forward_decay / sdm_recurrent_decay: sdm_workspace_bytes plus the
+ * per-token cumulative log-decay [B,H,T+1] float64 and one factor per token-slot
+ * [B,H,T,W+R] float32. 0 if the shape is invalid. */
+size_t sdm_workspace_bytes_decay(const sdm_shape* shape);
+
+/* sdm_recurrent with whole-table decay: for each unit, tokens in order,
+ *   x_j   = M[widx_j] * exp(L_{t-1} - lam[widx_j])        (the row's value before token t)
+ *   rho   = alpha_t * sum_j wgt_j x_j ;  delta = beta_t * (v_t - rho)
+ *   M[widx_j] = round_mem(alpha_t x_j + wgt_j delta) ;  lam[widx_j] = L_t
+ *   o_t   = sum_r rgt_r * M[ridx_r] * exp(L_t - lam[ridx_r])
+ * with L_t = lrun + sum_{s<=t} log alpha_s; lrun becomes L_{T-1}. lam, lrun in/out; other
+ * arguments as for sdm_recurrent. ws: at least sdm_workspace_bytes_decay(shape) bytes. */
+sdm_status sdm_recurrent_decay(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                               const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                               double* lam, double* lrun, float* o, void* ws, size_t ws_bytes, void* stream);
+
+/* sdm_forward with whole-table decay (addressing, then sdm_recurrent_decay's rule). */
+sdm_status sdm_forward_decay(const sdm_shape* shape, const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const void* subkeys, void* M, double* lam, double* lrun, float* o,
+                             int32_t* widx_out, int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* sdm_decode_step with whole-table decay (T must be 1; needs no workspace). */
+sdm_status sdm_decode_step_decay(const sdm_shape* shape, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const void* subkeys, void* M, double* lam,
+                                 double* lrun, float* o, void* stream);
+
+/* The current table of the whole-table decay variant: out[b,h,n,:] = M[b,h,n,:] *
+ * exp(lrun[b,h] - lam[b,h,n]), float32 [B,H,N,d_v] (out must not overlap the state). */
+sdm_status sdm_materialize(const sdm_shape* shape, const void* M, const double* lam, const double* lrun, float* out,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

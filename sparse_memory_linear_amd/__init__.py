@@ -18,6 +18,8 @@ __all__ = [
     "SDM_F32", "SDM_BF16", "SdmError", "SdmLibraryMissing", "Shape", "lib", "lib_path",
     "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
     "forward", "decode_step", "workspace_error", "status_string", "abi_version",
+    "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
+    "materialize",
 ]
 
 SDM_F32 = 0
@@ -64,6 +66,12 @@ _SIGS = {
     "sdm_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sdm_decode_step": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sdm_workspace_error": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P]),
+    "sdm_decay_state_init": (ctypes.c_int, [_SP, _P, _P, _P]),
+    "sdm_workspace_bytes_decay": (ctypes.c_size_t, [_SP]),
+    "sdm_recurrent_decay": (ctypes.c_int, [_SP] + [_P] * 12 + [ctypes.c_size_t, _P]),
+    "sdm_forward_decay": (ctypes.c_int, [_SP] + [_P] * 13 + [ctypes.c_size_t, _P]),
+    "sdm_decode_step_decay": (ctypes.c_int, [_SP] + [_P] * 11),
+    "sdm_materialize": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P]),
 }
 
 
@@ -165,3 +173,38 @@ def workspace_error(ws, stream=None) -> int:
     _check(lib().sdm_workspace_error(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(out), _stream(stream)),
            "sdm_workspace_error")
     return out.value
+
+
+# ----------------------------------------------------------------------------- whole-table decay
+def decay_state_init(shape: Shape, lam, lrun, stream=None):
+    _check(lib().sdm_decay_state_init(ctypes.byref(shape), _ptr(lam), _ptr(lrun), _stream(stream)),
+           "sdm_decay_state_init")
+
+
+def workspace_bytes_decay(shape: Shape) -> int:
+    return lib().sdm_workspace_bytes_decay(ctypes.byref(shape))
+
+
+def recurrent_decay(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, lam, lrun, o, ws, stream=None):
+    _check(lib().sdm_recurrent_decay(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
+                                     _ptr(alpha), _ptr(beta), _ptr(M), _ptr(lam), _ptr(lrun), _ptr(o), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "sdm_recurrent_decay")
+
+
+def forward_decay(shape: Shape, q, k, v, alpha, beta, subkeys, M, lam, lrun, o, ws, widx_out=None, ridx_out=None,
+                  stream=None):
+    _check(lib().sdm_forward_decay(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(subkeys), _ptr(M), _ptr(lam), _ptr(lrun), _ptr(o), _ptr(widx_out),
+                                   _ptr(ridx_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "sdm_forward_decay")
+
+
+def decode_step_decay(shape: Shape, q, k, v, alpha, beta, subkeys, M, lam, lrun, o, stream=None):
+    _check(lib().sdm_decode_step_decay(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(subkeys), _ptr(M), _ptr(lam), _ptr(lrun), _ptr(o), _stream(stream)),
+           "sdm_decode_step_decay")
+
+
+def materialize(shape: Shape, M, lam, lrun, out, stream=None):
+    _check(lib().sdm_materialize(ctypes.byref(shape), _ptr(M), _ptr(lam), _ptr(lrun), _ptr(out), _stream(stream)),
+           "sdm_materialize")

@@ -71,9 +71,116 @@ size_t tensor_bytes(const sdm_shape& S, int64_t last, size_t esize) {
 
 sdm_status hip_status(hipError_t e) { return e == hipSuccess ? SDM_OK : SDM_ERR_HIP; }
 
+// Validation of the whole-table decay state against the table, outputs and workspace.
+sdm_status check_decay(const sdm_shape* S, const double* lam, const double* lrun, const void* M, size_t mb,
+                       const void* o, size_t ob, const void* ws, size_t ws_bytes) {
+  if (!lam && !lrun) return SDM_OK;
+  if (!lam || !lrun || !aligned16(lam) || !aligned16(lrun)) return SDM_ERR_INVALID_ARG;
+  const size_t U = (size_t)S->B * S->H;
+  const size_t lb = U * (size_t)S->N * 8, rb = U * 8;
+  if (overlaps(lam, lb, lrun, rb) || overlaps(lam, lb, M, mb) || overlaps(lrun, rb, M, mb) || overlaps(lam, lb, o, ob) ||
+      overlaps(lrun, rb, o, ob) || overlaps(lam, lb, ws, ws_bytes) || overlaps(lrun, rb, ws, ws_bytes))
+    return SDM_ERR_INVALID_ARG;
+  return SDM_OK;
+}
+
+sdm_status recurrent_impl(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                          const float* rgt, const void* v, const float* alpha, const float* beta, void* M, double* lam,
+                          double* lrun, float* o, void* ws, size_t ws_bytes, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!widx || !wgt || !ridx || !rgt || !v || !alpha || !beta || !M || !o) return SDM_ERR_INVALID_ARG;
+  const void* ptrs[] = {widx, wgt, ridx, rgt, v, alpha, beta, M, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SDM_ERR_INVALID_ARG;
+  const bool decay = lam != nullptr;
+  if (decay && !dataflow_supported(*S, true)) return SDM_ERR_UNSUPPORTED;
+  const WsLayout L = workspace_layout(*S, decay);
+  if (!ws || ws_bytes < L.total) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
+  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
+  const size_t ob = tensor_bytes(*S, S->d_v, 4);
+  if (overlaps(M, mb, o, ob) || overlaps(M, mb, ws, ws_bytes) || overlaps(o, ob, ws, ws_bytes)) return SDM_ERR_INVALID_ARG;
+  st = check_decay(S, lam, lrun, M, mb, o, ob, ws, ws_bytes);
+  if (st != SDM_OK) return st;
+  if (S->T == 0) return SDM_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = launch_zero((char*)ws + L.err, 1, hs);
+  if (e != hipSuccess) return SDM_ERR_HIP;
+  DecayState dk{lam, lrun};
+  return hip_status(launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, decay ? &dk : nullptr, hs));
+}
+
+sdm_status forward_impl(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const void* subkeys, void* M, double* lam, double* lrun, float* o,
+                        int32_t* widx_out, int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!q || !k || !v || !alpha || !beta || !subkeys || !M || !o) return SDM_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, alpha, beta, subkeys, M, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SDM_ERR_INVALID_ARG;
+  if ((widx_out && !aligned16(widx_out)) || (ridx_out && !aligned16(ridx_out))) return SDM_ERR_INVALID_ARG;
+  const bool decay = lam != nullptr;
+  if (decay && !dataflow_supported(*S, true)) return SDM_ERR_UNSUPPORTED;
+  const WsLayout L = workspace_layout(*S, decay);
+  if (!ws || ws_bytes < L.total) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
+  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
+  const size_t ob = tensor_bytes(*S, S->d_v, 4);
+  const size_t xb = tensor_bytes(*S, S->d_k, dtype_size(S->in_dtype));
+  const size_t vb = tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype));
+  const size_t wb = tensor_bytes(*S, S->W, 4), rb = tensor_bytes(*S, S->R, 4);
+  if (overlaps(M, mb, o, ob) || overlaps(M, mb, ws, ws_bytes) || overlaps(o, ob, ws, ws_bytes) ||
+      overlaps(M, mb, q, xb) || overlaps(M, mb, k, xb) || overlaps(M, mb, v, vb) || overlaps(o, ob, q, xb) ||
+      overlaps(o, ob, k, xb) || overlaps(o, ob, v, vb) || overlaps(widx_out, wb, ws, ws_bytes) ||
+      overlaps(ridx_out, rb, ws, ws_bytes) || overlaps(widx_out, wb, M, mb) || overlaps(ridx_out, rb, M, mb) ||
+      overlaps(widx_out, wb, ridx_out, rb))
+    return SDM_ERR_INVALID_ARG;
+  st = check_decay(S, lam, lrun, M, mb, o, ob, ws, ws_bytes);
+  if (st != SDM_OK) return st;
+  if (S->T == 0) return SDM_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  char* w = (char*)ws;
+  int32_t* widx = widx_out ? widx_out : (int32_t*)(w + L.widx);
+  int32_t* ridx = ridx_out ? ridx_out : (int32_t*)(w + L.ridx);
+  float* wgt = (float*)(w + L.wgt);
+  float* rgt = (float*)(w + L.rgt);
+  hipError_t e = launch_address(*S, k, subkeys, S->W, widx, wgt, nullptr, hs);
+  if (e != hipSuccess) return SDM_ERR_HIP;
+  e = launch_address(*S, q, subkeys, S->R, ridx, rgt, nullptr, hs);
+  if (e != hipSuccess) return SDM_ERR_HIP;
+  e = launch_zero(w + L.err, 1, hs);
+  if (e != hipSuccess) return SDM_ERR_HIP;
+  DecayState dk{lam, lrun};
+  return hip_status(launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, decay ? &dk : nullptr, hs));
+}
+
+sdm_status decode_impl(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, const void* subkeys, void* M, double* lam, double* lrun, float* o,
+                       void* stream) {
+  sdm_status st = check_shape(S, false);
+  if (st != SDM_OK) return st;
+  if (S->T != 1) return SDM_ERR_INVALID_ARG;
+  if (!q || !k || !v || !alpha || !beta || !subkeys || !M || !o) return SDM_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, alpha, beta, subkeys, M, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SDM_ERR_INVALID_ARG;
+  const int cpl = S->mem_dtype == SDM_BF16 ? 2 : 1;
+  if (S->d_v / cpl > 256) return SDM_ERR_UNSUPPORTED;
+  if (decode_lds_bytes(*S) > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
+  const size_t ob = tensor_bytes(*S, S->d_v, 4);
+  if (overlaps(M, mb, o, ob)) return SDM_ERR_INVALID_ARG;
+  st = check_decay(S, lam, lrun, M, mb, o, ob, nullptr, 0);
+  if (st != SDM_OK) return st;
+  DecayState dk{lam, lrun};
+  return hip_status(launch_decode(*S, q, k, v, alpha, beta, subkeys, M, o, lam ? &dk : nullptr, (hipStream_t)stream));
+}
+
 }  // namespace
 
-WsLayout workspace_layout(const sdm_shape& S) {
+WsLayout workspace_layout(const sdm_shape& S, bool decay) {
   WsLayout L;
   const size_t tok = (size_t)S.B * S.H * (size_t)S.T;
   size_t o = 0;
@@ -84,10 +191,18 @@ WsLayout workspace_layout(const sdm_shape& S) {
   L.rgt = o; o = align_up(o + tok * S.R * 4);
   L.deps = o;
   L.sched = o;
-  if (dataflow_supported(S)) {
+  L.ltok = o;
+  L.fac = o;
+  if (dataflow_supported(S, decay)) {
     o = align_up(o + dataflow_deps_bytes(S));
     L.sched = o;
     o = align_up(o + dataflow_sched_words(S) * 4);
+    if (decay) {
+      L.ltok = o;
+      o = align_up(o + (size_t)S.B * S.H * ((size_t)S.T + 1) * 8);
+      L.fac = o;
+      o = align_up(o + tensor_bytes(S, (int64_t)S.W + S.R, 4));
+    }
   }
   L.total = o;
   return L;
@@ -150,81 +265,70 @@ sdm_status sdm_address(const sdm_shape* S, const void* x, const void* subkeys, i
 sdm_status sdm_recurrent(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                          const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                          void* ws, size_t ws_bytes, void* stream) {
-  sdm_status st = check_shape(S, true);
-  if (st != SDM_OK) return st;
-  if (!widx || !wgt || !ridx || !rgt || !v || !alpha || !beta || !M || !o) return SDM_ERR_INVALID_ARG;
-  const void* ptrs[] = {widx, wgt, ridx, rgt, v, alpha, beta, M, o};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SDM_ERR_INVALID_ARG;
-  const WsLayout L = workspace_layout(*S);
-  if (!ws || ws_bytes < L.total) return SDM_ERR_WORKSPACE;
-  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
-  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
-  const size_t ob = tensor_bytes(*S, S->d_v, 4);
-  if (overlaps(M, mb, o, ob) || overlaps(M, mb, ws, ws_bytes) || overlaps(o, ob, ws, ws_bytes)) return SDM_ERR_INVALID_ARG;
-  if (S->T == 0) return SDM_OK;
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = launch_zero((char*)ws + L.err, 1, hs);
-  if (e != hipSuccess) return SDM_ERR_HIP;
-  return hip_status(launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, hs));
+  return recurrent_impl(S, widx, wgt, ridx, rgt, v, alpha, beta, M, nullptr, nullptr, o, ws, ws_bytes, stream);
 }
 
 sdm_status sdm_forward(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
                        const float* beta, const void* subkeys, void* M, float* o, int32_t* widx_out,
                        int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream) {
-  sdm_status st = check_shape(S, true);
-  if (st != SDM_OK) return st;
-  if (!q || !k || !v || !alpha || !beta || !subkeys || !M || !o) return SDM_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, alpha, beta, subkeys, M, o};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SDM_ERR_INVALID_ARG;
-  if ((widx_out && !aligned16(widx_out)) || (ridx_out && !aligned16(ridx_out))) return SDM_ERR_INVALID_ARG;
-  const WsLayout L = workspace_layout(*S);
-  if (!ws || ws_bytes < L.total) return SDM_ERR_WORKSPACE;
-  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
-  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
-  const size_t ob = tensor_bytes(*S, S->d_v, 4);
-  const size_t xb = tensor_bytes(*S, S->d_k, dtype_size(S->in_dtype));
-  const size_t vb = tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype));
-  const size_t wb = tensor_bytes(*S, S->W, 4), rb = tensor_bytes(*S, S->R, 4);
-  if (overlaps(M, mb, o, ob) || overlaps(M, mb, ws, ws_bytes) || overlaps(o, ob, ws, ws_bytes) ||
-      overlaps(M, mb, q, xb) || overlaps(M, mb, k, xb) || overlaps(M, mb, v, vb) || overlaps(o, ob, q, xb) ||
-      overlaps(o, ob, k, xb) || overlaps(o, ob, v, vb) || overlaps(widx_out, wb, ws, ws_bytes) ||
-      overlaps(ridx_out, rb, ws, ws_bytes) || overlaps(widx_out, wb, M, mb) || overlaps(ridx_out, rb, M, mb) ||
-      overlaps(widx_out, wb, ridx_out, rb))
-    return SDM_ERR_INVALID_ARG;
-  if (S->T == 0) return SDM_OK;
-  hipStream_t hs = (hipStream_t)stream;
-  char* w = (char*)ws;
-  int32_t* widx = widx_out ? widx_out : (int32_t*)(w + L.widx);
-  int32_t* ridx = ridx_out ? ridx_out : (int32_t*)(w + L.ridx);
-  float* wgt = (float*)(w + L.wgt);
-  float* rgt = (float*)(w + L.rgt);
-  hipError_t e = launch_address(*S, k, subkeys, S->W, widx, wgt, nullptr, hs);
-  if (e != hipSuccess) return SDM_ERR_HIP;
-  e = launch_address(*S, q, subkeys, S->R, ridx, rgt, nullptr, hs);
-  if (e != hipSuccess) return SDM_ERR_HIP;
-  e = launch_zero(w + L.err, 1, hs);
-  if (e != hipSuccess) return SDM_ERR_HIP;
-  return hip_status(launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, hs));
+  return forward_impl(S, q, k, v, alpha, beta, subkeys, M, nullptr, nullptr, o, widx_out, ridx_out, ws, ws_bytes,
+                      stream);
 }
 
 sdm_status sdm_decode_step(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const void* subkeys, void* M, float* o, void* stream) {
-  sdm_status st = check_shape(S, false);
+  return decode_impl(S, q, k, v, alpha, beta, subkeys, M, nullptr, nullptr, o, stream);
+}
+
+size_t sdm_workspace_bytes_decay(const sdm_shape* shape) {
+  if (check_shape(shape, true) != SDM_OK) return 0;
+  return workspace_layout(*shape, true).total;
+}
+
+sdm_status sdm_decay_state_init(const sdm_shape* S, double* lam, double* lrun, void* stream) {
+  sdm_status st = check_shape(S, true);
   if (st != SDM_OK) return st;
-  if (S->T != 1) return SDM_ERR_INVALID_ARG;
-  if (!q || !k || !v || !alpha || !beta || !subkeys || !M || !o) return SDM_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, alpha, beta, subkeys, M, o};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SDM_ERR_INVALID_ARG;
-  const int cpl = S->mem_dtype == SDM_BF16 ? 2 : 1;
-  if (S->d_v / cpl > 256) return SDM_ERR_UNSUPPORTED;
-  if (decode_lds_bytes(*S) > kMaxLds) return SDM_ERR_UNSUPPORTED;
-  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
-  const size_t ob = tensor_bytes(*S, S->d_v, 4);
-  if (overlaps(M, mb, o, ob)) return SDM_ERR_INVALID_ARG;
-  return hip_status(launch_decode(*S, q, k, v, alpha, beta, subkeys, M, o, (hipStream_t)stream));
+  if (!lam || !lrun || !aligned16(lam) || !aligned16(lrun)) return SDM_ERR_INVALID_ARG;
+  const size_t U = (size_t)S->B * S->H;
+  if (overlaps(lam, U * (size_t)S->N * 8, lrun, U * 8)) return SDM_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  if (launch_zero(lam, U * (size_t)S->N, hs) != hipSuccess) return SDM_ERR_HIP;
+  return hip_status(launch_zero(lrun, U, hs));
+}
+
+sdm_status sdm_recurrent_decay(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                               const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                               double* lam, double* lrun, float* o, void* ws, size_t ws_bytes, void* stream) {
+  if (!lam || !lrun) return SDM_ERR_INVALID_ARG;
+  return recurrent_impl(S, widx, wgt, ridx, rgt, v, alpha, beta, M, lam, lrun, o, ws, ws_bytes, stream);
+}
+
+sdm_status sdm_forward_decay(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const void* subkeys, void* M, double* lam, double* lrun, float* o,
+                             int32_t* widx_out, int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!lam || !lrun) return SDM_ERR_INVALID_ARG;
+  return forward_impl(S, q, k, v, alpha, beta, subkeys, M, lam, lrun, o, widx_out, ridx_out, ws, ws_bytes, stream);
+}
+
+sdm_status sdm_decode_step_decay(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, const void* subkeys, void* M, double* lam, double* lrun, float* o,
+                                 void* stream) {
+  if (!lam || !lrun) return SDM_ERR_INVALID_ARG;
+  return decode_impl(S, q, k, v, alpha, beta, subkeys, M, lam, lrun, o, stream);
+}
+
+sdm_status sdm_materialize(const sdm_shape* S, const void* M, const double* lam, const double* lrun, float* out,
+                           void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!M || !lam || !lrun || !out) return SDM_ERR_INVALID_ARG;
+  if (!aligned16(M) || !aligned16(lam) || !aligned16(lrun) || !aligned16(out)) return SDM_ERR_INVALID_ARG;
+  const size_t U = (size_t)S->B * S->H;
+  const size_t mb = U * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
+  const size_t outb = U * (size_t)S->N * S->d_v * 4;
+  if (overlaps(out, outb, M, mb) || overlaps(out, outb, lam, U * (size_t)S->N * 8) || overlaps(out, outb, lrun, U * 8))
+    return SDM_ERR_INVALID_ARG;
+  return hip_status(launch_materialize(*S, M, lam, lrun, out, (hipStream_t)stream));
 }
 
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream) {

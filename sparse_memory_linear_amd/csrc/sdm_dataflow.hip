@@ -148,6 +148,7 @@ struct PipeArgs {
   unsigned long long* err;
   int U, T, W, R, E, d_v, P;
   int S, RS, SM, win, tpb, vw, rowbytes;
+  const float* fac;  // [U][T][E] decay factors of the accesses (whole-table decay), or null
   int pack2;  // two tokens' write rows per store instruction
   int nh;     // compute passes per half wave: ceil(max(W, R) / (32 / lanes per row))
   long long N;
@@ -281,6 +282,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
   uint32_t* pk_r = (uint32_t*)(obuf + (size_t)S * CPR);             // [SM][E]
   float* wt_r = (float*)(pk_r + (size_t)SM * E);                    // [SM][E]
   uint32_t* vab_r = (uint32_t*)(wt_r + (size_t)SM * E);             // [SM][vw]
+  float* fac_r = (float*)(vab_r + (size_t)SM * A.vw);                // [SM][E] decay factors (if any)
 
   for (int i = threadIdx.x; i < kCtrlWords; i += blockDim.x) ctrl[i] = 0;
   for (int i = threadIdx.x; i < 3 * S; i += blockDim.x) g_tok[i] = -1;
@@ -347,9 +349,15 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
         if (lane < tpb * vw && tb + tt < T)
           __builtin_amdgcn_global_load_lds(src, (void*)(vab_r + (size_t)sl0 * vw), 4, 0, 0);
       }
+      if (A.fac) {
+        const int q = lane * 4, tt = q / E;
+        if (q < tpb * E && tb + tt < T)
+          __builtin_amdgcn_global_load_lds(A.fac + (ut0 + tb) * E + q, (void*)(fac_r + (size_t)sl0 * E), 16, 0, 0);
+      }
       if (b >= kMetaDepth) {
-        // exactly 3 loads per batch: the batch kMetaDepth back is complete
-        wait_vmcnt<3 * kMetaDepth>();
+        // exactly 3 (4 with decay factors) loads per batch: the batch kMetaDepth back is complete
+        if (A.fac) wait_vmcnt<4 * kMetaDepth>();
+        else wait_vmcnt<3 * kMetaDepth>();
         const int done = (b - kMetaDepth + 1) * tpb;
         if (done > published) {
           published = done;
@@ -594,7 +602,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     const float* wts = wt_r + (size_t)ml * E;
     const uint32_t* vab = vab_r + (size_t)ml * A.vw;
     uint32_t pw[NH];
-    float wv[NH];
+    float wv[NH], xs[NH];  // weight; scale of the gathered row (decay factor of a write row)
     LV xv[NH];
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
@@ -603,6 +611,14 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       const int jl = live ? j : 0;
       pw[i] = pks[rbase + jl];
       wv[i] = wts[rbase + jl];
+      xs[i] = 1.f;
+      if (A.fac) {
+        // whole-table decay: a write row is scaled to its value before this token's decay,
+        // a read row's weight to its value after it
+        const float f = fac_r[(size_t)ml * E + rbase + jl];
+        if (hh == 0) xs[i] = f;
+        else wv[i] *= f;
+      }
       // rows of this token's ring slot, all written by the gather (0 where not loaded)
       xv[i] = hh ? *rrow_ptr(rl, jl) : *wrow_ptr(sl, jl);
       if (!live) pw[i] = kInvalid;
@@ -665,8 +681,9 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       if (i < nh) {
         float x[CPL];
         PT::unpack(xv[i], x);
+        const float wx = wv[i] * xs[i];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wv[i], x[c], acc[c]);
+        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wx, x[c], acc[c]);
       }
     }
 #pragma unroll
@@ -684,8 +701,9 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
         if (i < nh && j < W) {
           float x[CPL], y[CPL];
           PT::unpack(xv[i], x);
+          const float ax = al * xs[i];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], wv[i] * dl[c]);
+          for (int c = 0; c < CPL; ++c) y[c] = fmaf(ax, x[c], wv[i] * dl[c]);
           *wrow_ptr(sl, j) = PT::pack(y);
           if (l == 0) slot_w[(size_t)sl * W + j] = (pw[i] & (kCoded | kInvalid)) == kInvalid ? -1 : (int)(pw[i] & kSlotMask);
           // a row rewritten by the next token goes out in the same store instruction as that
@@ -755,7 +773,7 @@ int pow2_floor(int x) {
 
 // Ring and batch sizes for a block width of rb bytes per row moved in lanes of lb bytes;
 // false if it does not fit.
-bool pipe_fits(const sdm_shape& S, int rb, int lb, PipeCfg* c) {
+bool pipe_fits(const sdm_shape& S, int rb, int lb, bool decay, PipeCfg* c) {
   const int msz = (int)dtype_size(S.mem_dtype), isz = (int)dtype_size(S.in_dtype);
   const int rowbytes = S.d_v * msz;
   if (rowbytes % rb || rb % lb) return false;
@@ -775,7 +793,7 @@ bool pipe_fits(const sdm_shape& S, int rb, int lb, PipeCfg* c) {
   const int tpb = std::min(pow2_floor(std::max(1, 256 / E)), pow2_floor(64 / vw));
   const size_t tslot = 12 + (size_t)S.W * rb + (size_t)S.W * 4 + (size_t)cpr * 4;  // token ring slot
   const size_t rslot = (size_t)S.R * rb;                                          // read-row ring slot
-  const size_t mslot = (size_t)E * 8 + (size_t)vw * 4;                             // metadata ring slot
+  const size_t mslot = (size_t)E * (decay ? 12 : 8) + (size_t)vw * 4;              // metadata ring slot
   const size_t fixed = kCtrlWords * 4;
   // A metadata ring of 64 slots (32 only if nothing fits beside 64) and the longest token
   // ring that fits beside it. A longer metadata ring lets the metadata wave run far ahead and
@@ -823,14 +841,14 @@ bool pipe_fits(const sdm_shape& S, int rb, int lb, PipeCfg* c) {
 // one round and CUs to spare, narrower blocks (more workgroups, each with less arithmetic per
 // token) are faster; once the chip is full, 16-byte lanes (half the row requests of 8-byte
 // lanes for the same bytes) are.
-bool pipe_config(const sdm_shape& S, int cus, PipeCfg* out) {
+bool pipe_config(const sdm_shape& S, int cus, bool decay, PipeCfg* out) {
   bool any = false;
   long long best_rounds = 0, best_wgs = 0;
   const long long U = (long long)S.B * S.H;
   for (int lb = 16; lb >= 8; lb /= 2)
     for (int rb = lb; rb <= 32; rb *= 2) {
       PipeCfg c;
-      if (!pipe_fits(S, rb, lb, &c) || c.S < 64) continue;
+      if (!pipe_fits(S, rb, lb, decay, &c) || c.S < 64) continue;
       const long long wgs = U * c.P;
       const long long rounds = (wgs + cus - 1) / cus;  // one 16-wave workgroup per CU
       const bool better = !any || rounds < best_rounds ||
@@ -892,13 +910,13 @@ hipError_t pipe_launch(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
 
 }  // namespace
 
-bool dataflow_supported(const sdm_shape& S) {
+bool dataflow_supported(const sdm_shape& S, bool decay) {
   if (S.W % 4 || S.R % 4) return false;  // weight lists move in 16-byte pieces
   if (S.N > (1 << 18)) return false;     // packed slot words hold 18-bit slots
   if ((size_t)S.N * S.d_v * dtype_size(S.mem_dtype) > 0x7FFFFFFFull) return false;  // buffer offsets
   if ((size_t)S.T * S.d_v * 4 > 0x7FFFFFFFull) return false;
   PipeCfg c;
-  return pipe_config(S, 256, &c);
+  return pipe_config(S, 256, decay, &c);
 }
 
 size_t dataflow_deps_bytes(const sdm_shape& S) {
@@ -912,9 +930,9 @@ size_t dataflow_sched_words(const sdm_shape& S) {
 
 hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                           void* ws, const WsLayout& L, hipStream_t stream) {
+                           void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream) {
   PipeCfg c;
-  if (!pipe_config(S, device_cus(), &c)) return hipErrorInvalidValue;
+  if (!pipe_config(S, device_cus(), dk != nullptr, &c)) return hipErrorInvalidValue;
   const int U = S.B * S.H;
   char* w = (char*)ws;
   uint32_t* pk = (uint32_t*)(w + L.deps);
@@ -933,8 +951,19 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), (size_t)4 << D.bits, stream, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  float* fac = nullptr;
+  if (dk) {
+    // whole-table decay: cumulative log-decay per token, then every access's factor
+    double* Ltok = (double*)(w + L.ltok);
+    fac = (float*)(w + L.fac);
+    e = launch_log_decay_scan(S, alpha, Ltok, dk->lrun, stream);
+    if (e != hipSuccess) return e;
+    e = launch_decay_pass(S, pk, Ltok, dk->lam, fac, c.win, stream);
+    if (e != hipSuccess) return e;
+  }
   PipeArgs A;
   A.pk = pk;
+  A.fac = fac;
   A.wgt = wgt;
   A.rgt = rgt;
   A.v = v;

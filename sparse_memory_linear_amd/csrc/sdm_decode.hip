@@ -25,6 +25,8 @@ struct DecArgs {
   const void* subkeys;
   void* M;
   float* o;
+  double* lam;   // whole-table decay state [units][N] and [units], or null
+  double* lrun;
   int H, s, h, kappa, W, R, d_v, stairW, stairR;
   long long N;
 };
@@ -51,7 +53,7 @@ struct DMem<uint16_t> {
 };
 
 struct DecLds {
-  size_t sc, sel_i, sel_s, wbuf, widx, wgt, ridx, rgt, rmatch, wrow, part, delta, total;
+  size_t sc, sel_i, sel_s, wbuf, widx, wgt, ridx, rgt, rmatch, fw, fr, wrow, part, delta, total;
 };
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -68,6 +70,8 @@ __host__ __device__ inline DecLds dec_lds(int s, int kappa, int W, int R, int ro
   L.ridx = o; o = al16(o + (size_t)R * 4);
   L.rgt = o; o = al16(o + (size_t)R * 4);
   L.rmatch = o; o = al16(o + (size_t)R * 4);
+  L.fw = o; o = al16(o + (size_t)W * 4);
+  L.fr = o; o = al16(o + (size_t)R * 4);
   L.wrow = o; o = al16(o + (size_t)W * rowdw * 4);
   L.part = o; o = al16(o + (size_t)kThreads * cpl * 4);
   L.delta = o; o = al16(o + (size_t)rowdw * cpl * 4);
@@ -92,6 +96,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
   int32_t* sridx = (int32_t*)(smem + L.ridx);
   float* srgt = (float*)(smem + L.rgt);
   int32_t* rmatch = (int32_t*)(smem + L.rmatch);
+  float* sfw = (float*)(smem + L.fw);
+  float* sfr = (float*)(smem + L.fr);
   uint32_t* wrow = (uint32_t*)(smem + L.wrow);
   float* part = (float*)(smem + L.part);
   float* sdelta = (float*)(smem + L.delta);
@@ -184,6 +190,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
       if (swidx[j] == sridx[tid]) pos = j;
     rmatch[tid] = pos;
   }
+  // whole-table decay: a write row's value before this token's decay is its stored value
+  // times exp(lrun - lam); a read row's after it, times exp(lrun + log alpha - lam), or 1 for
+  // a row this token writes
+  double lnew = 0.0;
+  if (A.lam) {
+    const double lold = A.lrun[u];
+    lnew = lold + fmax(log((double)A.alpha[u]), -1000.0);
+    const double* lam = A.lam + (size_t)u * A.N;
+    if (tid < W) sfw[tid] = expf((float)(lold - lam[swidx[tid]]));
+    if (tid < R) sfr[tid] = rmatch[tid] >= 0 ? 1.f : expf((float)(lnew - lam[sridx[tid]]));
+    __syncthreads();
+  }
   // 4. rows: thread = (row group g, row word dw)
   const int G = kThreads / rowdw;
   const int g = tid / rowdw, dw = tid % rowdw;
@@ -199,8 +217,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
       wrow[j * rowdw + dw] = w;
       float x[CPL];
       MT::unpack(w, x);
+      const float wx = A.lam ? swgt[j] * sfw[j] : swgt[j];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(swgt[j], x[c], acc[c]);
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wx, x[c], acc[c]);
     }
   }
 #pragma unroll
@@ -220,8 +239,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
     for (int j = g; j < W; j += G) {
       float x[CPL], y[CPL];
       MT::unpack(wrow[j * rowdw + dw], x);
+      const float ax = A.lam ? al * sfw[j] : al;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], swgt[j] * sdelta[dw * CPL + c]);
+      for (int c = 0; c < CPL; ++c) y[c] = fmaf(ax, x[c], swgt[j] * sdelta[dw * CPL + c]);
       const uint32_t nw = MT::pack(y);
       Mu[(size_t)swidx[j] * rowdw + dw] = nw;
       wrow[j * rowdw + dw] = nw;
@@ -236,8 +256,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
       const uint32_t w = pos >= 0 ? wrow[pos * rowdw + dw] : Mu[(size_t)sridx[r] * rowdw + dw];
       float x[CPL];
       MT::unpack(w, x);
+      const float wr = A.lam ? srgt[r] * sfr[r] : srgt[r];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(srgt[r], x[c], acc[c]);
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wr, x[c], acc[c]);
     }
   }
 #pragma unroll
@@ -250,6 +271,11 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
       for (int gg = 0; gg < G; ++gg) ov += part[(gg * rowdw + tid) * CPL + c];
       A.o[(size_t)u * A.d_v + (size_t)tid * CPL + c] = ov;
     }
+  }
+  if (A.lam) {
+    // the written slots now hold values as of this token
+    if (tid < W) A.lam[(size_t)u * A.N + swidx[tid]] = lnew;
+    if (tid == 0) A.lrun[u] = lnew;
   }
 }
 
@@ -297,8 +323,11 @@ size_t decode_lds_bytes(const sdm_shape& S) {
 }
 
 hipError_t launch_decode(const sdm_shape& S, const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const void* subkeys, void* M, float* o, hipStream_t stream) {
+                         const float* beta, const void* subkeys, void* M, float* o, const DecayState* dk,
+                         hipStream_t stream) {
   DecArgs A;
+  A.lam = dk ? dk->lam : nullptr;
+  A.lrun = dk ? dk->lrun : nullptr;
   A.q = q;
   A.k = k;
   A.v = v;

@@ -23,9 +23,17 @@ struct WsLayout {
   size_t err;                   // int64 error counter
   size_t deps;                  // dependency lists (dataflow scheduler)
   size_t sched;                 // scheduler counters and done flags
+  size_t ltok, fac;             // whole-table decay: log-decay per token [U][T+1], factors [U][T][E]
   size_t total;
 };
-WsLayout workspace_layout(const sdm_shape& S);
+WsLayout workspace_layout(const sdm_shape& S, bool decay = false);
+
+// Whole-table decay state of the caller: lam [U][N] (cumulative log-decay at each slot's
+// last write), lrun [U] (cumulative log-decay of every token so far).
+struct DecayState {
+  double* lam;
+  double* lrun;
+};
 
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t stream);
 size_t address_lds_bytes(int s, int kappa);
@@ -34,16 +42,23 @@ hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys
 hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t stream);
 hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                             const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                            void* ws, const WsLayout& L, hipStream_t stream);
+                            void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream);
 hipError_t launch_decode(const sdm_shape& S, const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const void* subkeys, void* M, float* o, hipStream_t stream);
+                         const float* beta, const void* subkeys, void* M, float* o, const DecayState* dk,
+                         hipStream_t stream);
 size_t decode_lds_bytes(const sdm_shape& S);
 
-bool dataflow_supported(const sdm_shape& S);
+bool dataflow_supported(const sdm_shape& S, bool decay = false);
 size_t dataflow_deps_bytes(const sdm_shape& S);
 size_t dataflow_sched_words(const sdm_shape& S);
 hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                           void* ws, const WsLayout& L, hipStream_t stream);
+                           void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream);
+
+hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun, hipStream_t stream);
+hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,
+                             int win, hipStream_t stream);
+hipError_t launch_materialize(const sdm_shape& S, const void* M, const double* lam, const double* lrun, float* out,
+                              hipStream_t stream);
 
 }  // namespace sdm

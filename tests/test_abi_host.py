@@ -143,3 +143,49 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(S, "_lib", None)
     with pytest.raises(S.SdmLibraryMissing):
         S.lib()
+
+
+# ----------------------------------------------------------------------------- whole-table decay
+def test_workspace_bytes_decay(sdm):
+    S = base()
+    n, nd = sdm.workspace_bytes(S), sdm.workspace_bytes_decay(S)
+    tok = 2 * 2 * 64
+    # per token: the cumulative log-decay (8 B) and one factor per slot (4 B each)
+    assert nd >= n + tok * 8 + tok * (16 + 16) * 4
+    assert sdm.workspace_bytes_decay(base(N=65535)) == 0
+
+
+def test_decay_calls_validate(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    p = [FAKE + i * (1 << 36) for i in range(16)]
+    need = sdm.workspace_bytes_decay(S)
+    # recurrent: widx wgt ridx rgt v alpha beta M lam lrun o ws
+    args = p[:12]
+    assert L.sdm_recurrent_decay(sp, *args[:8], None, args[9], args[10], args[11], need, None) == -1
+    assert L.sdm_recurrent_decay(sp, *args[:9], None, args[10], args[11], need, None) == -1
+    assert L.sdm_recurrent_decay(sp, *args[:8], args[7] + 4096, *args[9:12], need, None) == -1  # lam inside M
+    assert L.sdm_recurrent_decay(sp, *args[:12], sdm.workspace_bytes(S), None) == -3  # plain workspace too small
+    assert L.sdm_recurrent_decay(sp, *args[:8], args[8] + 8, *args[9:12], need, None) == -1  # misaligned lam
+    # forward: q k v alpha beta subkeys M lam lrun o widx_out ridx_out ws
+    assert L.sdm_forward_decay(sp, *p[:7], None, p[8], p[9], None, None, p[12], need, None) == -1
+    assert L.sdm_forward_decay(sp, *p[:7], p[8], p[8] + 8, p[9], None, None, p[12], need, None) == -1  # lam/lrun overlap
+    # decode: T must be 1, state required
+    S1 = base(T=1)
+    assert L.sdm_decode_step_decay(ctypes.byref(S1), *p[:7], None, p[8], p[9], None) == -1
+    assert L.sdm_decode_step_decay(ctypes.byref(base(T=2)), *p[:10], None) == -1
+    # state init and materialize
+    assert L.sdm_decay_state_init(sp, None, p[1], None) == -1
+    assert L.sdm_decay_state_init(sp, p[0], p[0] + 16, None) == -1  # lrun inside lam
+    assert L.sdm_materialize(sp, p[0], p[1], p[2], None, None) == -1
+    assert L.sdm_materialize(sp, p[0], p[1], p[2], p[0] + 4096, None) == -1  # out overlaps M
+
+
+def test_decay_needs_the_pipelined_recurrence(sdm, no_gpu):
+    """Whole-table decay runs only on the pipelined recurrence: a shape it does not take
+    (slot lists that are not a multiple of 4 long) is refused before any launch."""
+    L = sdm.lib()
+    S = base(W=6, R=6)
+    p = [FAKE + i * (1 << 36) for i in range(16)]
+    assert L.sdm_recurrent_decay(ctypes.byref(S), *p[:12], 1 << 34, None) == -2

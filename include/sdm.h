@@ -160,8 +160,8 @@ sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_co
 sdm_status sdm_decay_state_init(const sdm_shape* shape, double* lam, double* lrun, void* stream);
 
 /* Workspace bytes of sdm_forward_decay / sdm_recurrent_decay: sdm_workspace_bytes plus the
- * per-token cumulative log-decay [B,H,T+1] float64 and one factor per token-slot
- * [B,H,T,W+R] float32. 0 if the shape is invalid. */
+ * per-token cumulative log-decay [B,H,T+1] float64, one factor per token-slot [B,H,T,W+R]
+ * float32 and the latest writer of each slot [B,H,N] int32. 0 if the shape is invalid. */
 size_t sdm_workspace_bytes_decay(const sdm_shape* shape);
 
 /* sdm_recurrent with whole-table decay: for each unit, tokens in order,

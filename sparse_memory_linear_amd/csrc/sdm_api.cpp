@@ -193,6 +193,7 @@ WsLayout workspace_layout(const sdm_shape& S, bool decay) {
   L.sched = o;
   L.ltok = o;
   L.fac = o;
+  L.lastw = o;
   if (dataflow_supported(S, decay)) {
     o = align_up(o + dataflow_deps_bytes(S));
     L.sched = o;
@@ -202,6 +203,8 @@ WsLayout workspace_layout(const sdm_shape& S, bool decay) {
       o = align_up(o + (size_t)S.B * S.H * ((size_t)S.T + 1) * 8);
       L.fac = o;
       o = align_up(o + tensor_bytes(S, (int64_t)S.W + S.R, 4));
+      L.lastw = o;
+      o = align_up(o + (size_t)S.B * S.H * (size_t)S.N * 4);
     }
   }
   L.total = o;

@@ -13,11 +13,14 @@
 // that the pipeline applies to the gathered row (write slots) or to the read weight.
 //
 // The factors depend only on which tokens write which slots, known before the recurrence
-// runs: decay_pass_kernel walks the tokens of a unit in chunks of at most `win` tokens.
-// Within the window the dependency pass already names each access's latest writer; an
-// access with none there sees no write since the chunk began, so the per-slot record of
-// the latest writer as of the chunk start decides it. Each workgroup keeps that record for
-// one range of slots in LDS.
+// runs. Within the window the dependency pass already names each access's latest writer;
+// for the other accesses decay_order_kernel walks the tokens of a unit in chunks of at
+// most `win` tokens, keeping per slot range (in LDS) the latest writer so far: an access
+// with no writer inside the window sees no write since its chunk began, so the record as
+// of the chunk start is its latest writer. decay_factor_kernel then forms every factor in
+// parallel, and decay_lam_kernel moves lam forward for the slots the call wrote.
+
+#include <algorithm>
 
 #include "sdm_device.hpp"
 #include "sdm_internal.hpp"
@@ -28,7 +31,7 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kPassThreads = 1024;
-constexpr int kPassChunk = 32;                 // tokens per chunk; at most the smallest window
+constexpr int kPerThread = 8;                  // accesses per thread and chunk (chunk * (W + R) <= 8192)
 constexpr int kPassSlotsMax = 32768;           // slots of one workgroup's LDS record (128 KB)
 constexpr uint32_t kCoded = 0x80000000u;       // packed slot word of the dependency pass
 constexpr uint32_t kInvalid = 0x40000000u;
@@ -73,62 +76,98 @@ struct PassArgs {
   const uint32_t* pk;  // [U][T][E] packed slot words (write slots, then read slots)
   const double* L;     // [U][T + 1]
   double* lam;         // [U][N] in/out
-  float* fac;          // [U][T][E] out
-  int T, W, E, P, span;
+  float* fac;          // [U][T][E] out (first holds each outside-window access's latest writer)
+  int* lastw;          // [U][N] latest writer of each slot in this call, -1 = none
+  int U, T, W, E, P, span, chunk;
   long long N;
 };
 
-// One workgroup per (unit, slot range of `span` slots): factors of the accesses to its
-// slots, then the cumulative log-decay at each of its slots' last write.
-__global__ void __launch_bounds__(kPassThreads) decay_pass_kernel(PassArgs A) {
-  extern __shared__ int last_tok[];  // [span]: latest writer so far in this call, -1 = none
-  const int u = blockIdx.x / A.P, p = blockIdx.x % A.P, tid = threadIdx.x;
-  const int T = A.T, W = A.W, E = A.E, span = A.span;
+// Order pass: one workgroup per (unit, range of `span` slots), tokens in chunks of at most
+// `win`. An access with no writer inside the window sees no write since its chunk began,
+// so the record of the latest writer as of the chunk start (LDS) is its latest writer; it
+// is left, as an int, in the access's factor word. Then the chunk's writes update the
+// record. The next chunk's slot words are loaded while a chunk is processed; the loop
+// touches nothing but LDS and registers otherwise. All ranges of a unit run on one XCD.
+__global__ void __launch_bounds__(kPassThreads) decay_order_kernel(PassArgs A) {
+  extern __shared__ int last_tok[];  // [span]
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int u = xcd + 8 * (k / A.P), p = k % A.P, tid = threadIdx.x;
+  if (u >= A.U) return;
+  const int T = A.T, W = A.W, E = A.E, span = A.span, C = A.chunk;
   const long long n0 = (long long)p * span;
   for (int i = tid; i < span; i += kPassThreads) last_tok[i] = -1;
-  __syncthreads();
   const uint32_t* pk = A.pk + (size_t)u * T * E;
-  const double* L = A.L + (size_t)u * (T + 1);
-  double* lam = A.lam + (size_t)u * A.N;
-  float* fac = A.fac + (size_t)u * T * E;
-  for (int c0 = 0; c0 < T; c0 += kPassChunk) {
-    const int c1 = min(T, c0 + kPassChunk);
-    // factors of the chunk's accesses to this range, from the record as of the chunk start
-    for (int i = c0 * E + tid; i < c1 * E; i += kPassThreads) {
-      const int t = i / E, e = i - t * E;
-      const uint32_t w = pk[i];
-      if ((w & (kCoded | kInvalid)) == kInvalid) {
-        if (p == 0) fac[i] = 1.f;  // slot outside [0, N): no weight, any finite factor
-        continue;
-      }
+  int* lt_out = (int*)(A.fac + (size_t)u * T * E);
+  const int per = C * E;  // accesses per chunk, at most kPerThread * kPassThreads
+  uint32_t cur[kPerThread], nxt[kPerThread];
+  auto load = [&](int c0, uint32_t (&w)[kPerThread]) {
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+      const int q = tid + r * kPassThreads;
+      const long long i = (long long)c0 * E + q;
+      w[r] = (q < per && i < (long long)T * E) ? pk[i] : kInvalid;
+    }
+  };
+  load(0, cur);
+  __syncthreads();
+  for (int c0 = 0; c0 < T; c0 += C) {
+    load(c0 + C, nxt);
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+      const uint32_t w = cur[r];
+      if (w & (kCoded | kInvalid)) continue;  // inside the window, or outside [0, N)
       const long long n = w & kSlotMask;
       if (n < n0 || n >= n0 + span) continue;
-      const double to = e >= W ? L[t + 1] : L[t];
-      float f;
-      if (w & kCoded) {
-        const int d = (w >> 24) & 127;
-        f = d == 0 ? 1.f : decay_factor(to, L[t - d + 1]);
-      } else {
-        const int lt = last_tok[n - n0];
-        f = decay_factor(to, lt >= 0 ? L[lt + 1] : lam[n]);
-      }
-      fac[i] = f;
+      lt_out[(size_t)c0 * E + tid + r * kPassThreads] = last_tok[n - n0];
     }
     __syncthreads();
-    // the chunk's writes to this range
-    for (int i = c0 * W + tid; i < c1 * W; i += kPassThreads) {
-      const int t = i / W, j = i - t * W;
-      const uint32_t w = pk[(size_t)t * E + j];
-      if ((w & (kCoded | kInvalid)) == kInvalid) continue;
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+      const int q = tid + r * kPassThreads;
+      const uint32_t w = cur[r];
+      if ((w & (kCoded | kInvalid)) == kInvalid || q % E >= W) continue;
       const long long n = w & kSlotMask;
-      if (n >= n0 && n < n0 + span) atomicMax(&last_tok[n - n0], t);
+      if (n >= n0 && n < n0 + span) atomicMax(&last_tok[n - n0], c0 + q / E);
     }
     __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) cur[r] = nxt[r];
   }
-  for (int i = tid; i < span; i += kPassThreads) {
-    const long long n = n0 + i;
-    if (n < A.N && last_tok[i] >= 0) lam[n] = L[last_tok[i] + 1];
+  int* lastw = A.lastw + (size_t)u * A.N;
+  for (int i = tid; i < span; i += kPassThreads)
+    if (n0 + i < A.N) lastw[n0 + i] = last_tok[i];
+}
+
+// Factor of every access (one thread each), from the window's writer or the order pass's.
+__global__ void __launch_bounds__(256) decay_factor_kernel(PassArgs A) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long per_unit = (long long)A.T * A.E;
+  if (i >= per_unit * A.U) return;
+  const int u = (int)(i / per_unit);
+  const long long iu = i - (long long)u * per_unit;
+  const int t = (int)(iu / A.E), e = (int)(iu - (long long)t * A.E);
+  const uint32_t w = A.pk[i];
+  const double* L = A.L + (size_t)u * (A.T + 1);
+  float f = 1.f;  // also for a slot outside [0, N): it carries no weight
+  if ((w & (kCoded | kInvalid)) != kInvalid) {
+    const double to = e >= A.W ? L[t + 1] : L[t];
+    if (w & kCoded) {
+      const int d = (w >> 24) & 127;
+      if (d > 0) f = decay_factor(to, L[t - d + 1]);
+    } else {
+      const int lt = __float_as_int(A.fac[i]);
+      f = decay_factor(to, lt >= 0 ? L[lt + 1] : A.lam[(size_t)u * A.N + (w & kSlotMask)]);
+    }
   }
+  A.fac[i] = f;
+}
+
+// lam of every slot written in this call: the cumulative log-decay after its latest writer.
+__global__ void __launch_bounds__(256) decay_lam_kernel(PassArgs A) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)A.U * A.N) return;
+  const int lt = A.lastw[i];
+  if (lt >= 0) A.lam[i] = A.L[(size_t)(i / A.N) * (A.T + 1) + lt + 1];
 }
 
 // out[u][n][c] = M[u][n][c] * exp(lrun[u] - lam[u][n]), float32
@@ -158,20 +197,33 @@ hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double*
 int decay_pass_ranges(const sdm_shape& S) { return (int)((S.N + kPassSlotsMax - 1) / kPassSlotsMax); }
 
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,
-                             int win, hipStream_t stream) {
-  if (win < kPassChunk) return hipErrorInvalidValue;
+                             int* lastw, int win, hipStream_t stream) {
   PassArgs A;
   A.pk = pk;
   A.L = L;
   A.lam = lam;
   A.fac = fac;
+  A.lastw = lastw;
+  A.U = S.B * S.H;
   A.T = S.T;
   A.W = S.W;
   A.E = S.W + S.R;
   A.P = decay_pass_ranges(S);
   A.span = (int)((S.N + A.P - 1) / A.P);
   A.N = S.N;
-  hipLaunchKernelGGL(decay_pass_kernel, dim3(S.B * S.H * A.P), dim3(kPassThreads), (size_t)A.span * 4, stream, A);
+  // the longest chunk inside the window whose accesses fit the threads' registers
+  A.chunk = std::min(win, kPerThread * kPassThreads / A.E);
+  if (A.chunk < 1) return hipErrorInvalidValue;
+  const int groups = (A.U + 7) / 8;
+  hipLaunchKernelGGL(decay_order_kernel, dim3(8 * groups * A.P), dim3(kPassThreads), (size_t)A.span * 4, stream, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long acc = (long long)A.U * A.T * A.E;
+  hipLaunchKernelGGL(decay_factor_kernel, dim3((unsigned)((acc + 255) / 256)), dim3(256), 0, stream, A);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long slots = (long long)A.U * S.N;
+  hipLaunchKernelGGL(decay_lam_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, stream, A);
   return hipGetLastError();
 }
 

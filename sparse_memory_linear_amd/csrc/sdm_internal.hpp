@@ -23,7 +23,8 @@ struct WsLayout {
   size_t err;                   // int64 error counter
   size_t deps;                  // dependency lists (dataflow scheduler)
   size_t sched;                 // scheduler counters and done flags
-  size_t ltok, fac;             // whole-table decay: log-decay per token [U][T+1], factors [U][T][E]
+  size_t ltok, fac, lastw;      // whole-table decay: log-decay per token [U][T+1], factors [U][T][E],
+                                // latest writer per slot [U][N]
   size_t total;
 };
 WsLayout workspace_layout(const sdm_shape& S, bool decay = false);
@@ -57,7 +58,7 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
 
 hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun, hipStream_t stream);
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,
-                             int win, hipStream_t stream);
+                             int* lastw, int win, hipStream_t stream);
 hipError_t launch_materialize(const sdm_shape& S, const void* M, const double* lam, const double* lrun, float* out,
                               hipStream_t stream);
 

@@ -150,8 +150,9 @@ def test_workspace_bytes_decay(sdm):
     S = base()
     n, nd = sdm.workspace_bytes(S), sdm.workspace_bytes_decay(S)
     tok = 2 * 2 * 64
-    # per token: the cumulative log-decay (8 B) and one factor per slot (4 B each)
-    assert nd >= n + tok * 8 + tok * (16 + 16) * 4
+    # per token: the cumulative log-decay (8 B) and one factor per slot (4 B each); per slot
+    # its latest writer (4 B)
+    assert nd >= n + tok * 8 + tok * (16 + 16) * 4 + 2 * 2 * 65536 * 4
     assert sdm.workspace_bytes_decay(base(N=65535)) == 0
 
 

@@ -53,6 +53,9 @@ __all__ = [
     "forward_unit",
     "forward",
     "decode_step_unit",
+    "gates",
+    "output_gate",
+    "head_mix",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -249,3 +252,41 @@ def decode_step_unit(M, q, k, v, alpha, beta, C1, C2, kappa: int, W: int, R: int
     r = forward_unit(q[None], k[None], v[None], np.array([alpha]), np.array([beta]), C1, C2, M,
                      kappa, W, R, mem_dtype, decay)
     return r["o"][0], r["M"], r
+
+
+# ----------------------------------------------------------------------------- gates and output
+def _softplus(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def gates(a, b, A_log, dt_bias):
+    """Decay and input gates from their pre-activations (PL App. B "Gate dynamics": the
+    forget gate is exp(g), the input gate sigma(b); PL §4 "SDM Configuration": the forget
+    gate and time-step bias follow Gated DeltaNet's conventions). READING R20:
+    g = -exp(A_log[h]) * softplus(a + dt_bias[h]) <= 0, alpha = exp(g), beta = sigmoid(b).
+    a, b: [..., H, T] per token-head pre-activations; A_log, dt_bias: [H]."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    A = np.exp(np.asarray(A_log, dtype=np.float64))[:, None]
+    g = -A * _softplus(a + np.asarray(dt_bias, dtype=np.float64)[:, None])
+    return np.exp(g), 1.0 / (1.0 + np.exp(-b))
+
+
+def output_gate(o, z, w, eps: float):
+    """Output of one token-head after the read (PL §3 "Sparse retrieval": RMS-normalised,
+    then elementwise gated). READING R21: RMS over d_v with one weight vector w [d_v]
+    shared by the heads; READING R22: the gate is SiLU(z), z from its own projection.
+    o, z: [..., d_v]."""
+    o = np.asarray(o, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o * r * np.asarray(w, dtype=np.float64) * (z / (1.0 + np.exp(-z)))
+
+
+def head_mix(x, Wo):
+    """Mixing of the heads into the layer output (PL §3 "Sparse retrieval": projected into
+    the layer output). READING R23: y = x Wo^T, no bias; x [M, H*d_v] (heads concatenated
+    per token), Wo [d_model, H*d_v]."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(Wo, dtype=np.float64).T
+

@@ -401,6 +401,58 @@ def pin_table_decay_alpha_one(O):
         assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["M"], b["M"])
 
 
+# ----------------------------------------------------------------------------- gates and output
+def pin_gates_closed_forms(O):
+    """PL App. B: alpha = exp(g), beta = sigmoid(b). With A_log = log c and a + dt_bias = 0,
+    softplus(0) = ln 2 gives alpha = 2^-c; a -> -inf gives alpha -> 1; b = 0 gives 1/2 and
+    beta(b) + beta(-b) = 1."""
+    A_log = np.log(np.array([1.0, 2.0, 0.5]))
+    dt = np.array([0.3, -1.0, 2.0])
+    a = -dt[:, None] * np.ones((3, 4))
+    b = np.array([[0.0, 1.0, -1.0, 3.0]] * 3)
+    al, be = O.gates(a, b, A_log, dt)
+    assert np.allclose(al, (2.0 ** -np.array([1.0, 2.0, 0.5]))[:, None] * np.ones((3, 4)), rtol=1e-15, atol=0)
+    assert np.array_equal(be[:, 0], np.full(3, 0.5))
+    assert np.allclose(be[:, 1] + be[:, 2], 1.0, rtol=0, atol=1e-15)
+    al2, _ = O.gates(np.full((3, 1), -800.0), np.zeros((3, 1)), A_log, dt)
+    assert np.all(al2 == 1.0)
+    al3, _ = O.gates(np.full((3, 1), 50.0), np.zeros((3, 1)), A_log, dt)  # softplus(x) = x for large x
+    assert np.allclose(al3[:, 0], np.exp(-np.exp(A_log) * (50.0 + dt)), rtol=1e-13, atol=0)
+
+
+def pin_output_gate(O):
+    """RMS normalisation then SiLU gate: a hand-worked token (o = (3, 4): RMS = sqrt(12.5);
+    z = (1, -2): SiLU = 1/(1+e^-1), -2/(1+e^2)), invariance under a positive scale of o
+    (eps = 0), and a zero gate where z = 0."""
+    o = np.array([3.0, 4.0])
+    w = np.array([1.0, 2.0])
+    z = np.array([1.0, -2.0])
+    y = O.output_gate(o, z, w, 0.0)
+    r = math.sqrt(12.5)
+    ref = np.array([3.0 / r * 1.0 / (1 + math.exp(-1.0)), 4.0 / r * 2.0 * (-2.0) / (1 + math.exp(2.0))])
+    assert np.allclose(y, ref, rtol=1e-15, atol=0)
+    rng = np.random.default_rng(31)
+    o = rng.standard_normal((5, 8))
+    z = rng.standard_normal((5, 8))
+    w = rng.standard_normal(8)
+    assert np.allclose(O.output_gate(o * 7.5, z, w, 0.0), O.output_gate(o, z, w, 0.0), rtol=1e-14, atol=0)
+    z[:, 3] = 0.0
+    assert np.all(O.output_gate(o, z, w, 1e-6)[:, 3] == 0.0)
+
+
+def pin_head_mix(O):
+    """The head mixing equals the explicit sum over heads and value columns."""
+    rng = np.random.default_rng(32)
+    M, H, dv, dm = 3, 2, 4, 5
+    x = rng.standard_normal((M, H * dv))
+    Wo = rng.standard_normal((dm, H * dv))
+    y = O.head_mix(x, Wo)
+    for m in range(M):
+        for j in range(dm):
+            ref = sum(x[m, h * dv + c] * Wo[j, h * dv + c] for h in range(H) for c in range(dv))
+            assert abs(y[m, j] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
 ALL_PINS = [
     pin_round_bf16,
     pin_pk_equals_brute_force,
@@ -419,4 +471,7 @@ ALL_PINS = [
     pin_table_decay_is_sparse_gdn,
     pin_table_decay_rows,
     pin_table_decay_alpha_one,
+    pin_gates_closed_forms,
+    pin_output_gate,
+    pin_head_mix,
 ]

@@ -55,6 +55,16 @@ MUTANTS = {
         "        M[n] = round_mem(alpha[t] * old + a[:, None] * delta[None, :], mem_dtype)\n        if decay == \"table\":\n            M *= alpha[t]\n"),
     # whole-table decay never applied
     "table_decay_missing": ("            M *= alpha[t]\n", "            pass\n"),
+    # decay gate without the time-step bias
+    "gate_no_dt_bias": ("g = -A * _softplus(a + np.asarray(dt_bias, dtype=np.float64)[:, None])", "g = -A * _softplus(a)"),
+    # input gate not squashed
+    "gate_beta_raw": ("return np.exp(g), 1.0 / (1.0 + np.exp(-b))", "return np.exp(g), b"),
+    # RMS without the mean (L2 norm)
+    "norm_l2": ("r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)", "r = 1.0 / np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps)"),
+    # sigmoid gate instead of SiLU
+    "gate_sigmoid": ("(z / (1.0 + np.exp(-z)))", "(1.0 / (1.0 + np.exp(-z)))"),
+    # head mixing with the untransposed weight
+    "mix_transposed": ("@ np.asarray(Wo, dtype=np.float64).T", "@ np.asarray(Wo, dtype=np.float64).T[::-1]"),
     # per-half top-k keeps too few sub-keys
     "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
 }

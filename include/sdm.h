@@ -142,6 +142,33 @@ sdm_status sdm_decode_step(const sdm_shape* shape, const void* q, const void* k,
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * The steps on either side of the recurrence (PL App. B "Gate dynamics": forget gate
+ * exp(g), input gate sigma(b); PL §4 "SDM Configuration": gate and time-step bias as in
+ * Gated DeltaNet; PL §3 "Sparse retrieval": the read is RMS-normalised, elementwise gated
+ * and projected into the layer output).
+ * --------------------------------------------------------------------------------------- */
+
+/* Gates from their per token-head pre-activations a, b [B,H,T] f32 and per-head parameters
+ * A_log, dt_bias [H] f32:  alpha = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])) in (0, 1],
+ * beta = sigmoid(b); alpha, beta [B,H,T] f32 out (float32 arithmetic). */
+sdm_status sdm_gates(const sdm_shape* shape, const float* a, const float* b, const float* A_log, const float* dt_bias,
+                     float* alpha, float* beta, void* stream);
+
+/* Normalised, gated output of every token-head:
+ *   x[b,t,h,:] = o[b,h,t,:] / sqrt(mean(o[b,h,t,:]^2) + eps) * w * silu(z[b,t,h,:])
+ * o [B,H,T,d_v] f32 (the recurrence's output); z [B,T,H,d_v] in_dtype (the gate's
+ * pre-activation, token-major); w [d_v] f32 shared by the heads; x [B,T,H,d_v] bf16 out
+ * (token-major: row b*T + t of x is the concatenation of the heads, the input of
+ * sdm_head_mix). 0 <= eps <= 1. */
+sdm_status sdm_output_gate(const sdm_shape* shape, const float* o, const void* z, const float* w, float eps, void* x,
+                           void* stream);
+
+/* Mixing of the heads into the layer output: y = x . Wo^T, i.e. y[m, n] = sum_k x[m,k] Wo[n,k]
+ *   x [M, K] bf16 (K = H*d_v, rows from sdm_output_gate), Wo [N, K] bf16 (d_model = N
+ *   rows), y [M, N] f32 out. K a multiple of 32; bf16 products, float32 sums (MFMA). */
+sdm_status sdm_head_mix(const void* x, const void* Wo, float* y, int64_t M, int32_t K, int32_t N, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Whole-table decay variant. The calls above decay only the W written rows by alpha_t. If
  * alpha_t instead decays every row of the table, as the dense state of Gated DeltaNet
  * decays (PL §2 "Gated DeltaNet"; PL §3 "Connection to GDN": the rule is then Gated

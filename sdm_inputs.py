@@ -213,3 +213,24 @@ def adversarial(shape: Shape, kind: str, seed: int = 99) -> Dict[str, np.ndarray
     out["k"] = cast(k, shape.in_dtype)
     out["q"] = cast(q, shape.in_dtype)
     return out
+
+
+def make_epilogue_inputs(shape: Shape, d_model: int, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Synthetic inputs of the steps around the recurrence, from their own generator
+    (seeded with (workload seed, 7)): gate pre-activations a, b [B,H,T] ~ N(0, 1); per-head
+    A_log ~ U(log 1, log 16) and dt_bias ~ N(-2, 0.5) (the ranges of Gated DeltaNet's
+    initialisation); output gate pre-activation z [B,T,H,d_v] ~ N(0, 1) in the input dtype;
+    norm weight w [d_v] ~ 1 + N(0, 0.1^2); head mixing weight Wo [d_model, H*d_v] ~
+    N(0, 1/(H*d_v)) in bf16 (uint16 bits)."""
+    rng = np.random.default_rng([shape.seed if seed is None else seed, 7])
+    B, H, T, dv = shape.B, shape.H, shape.T, shape.d_v
+    out = {
+        "a": rng.standard_normal((B, H, T), dtype=np.float32),
+        "b": rng.standard_normal((B, H, T), dtype=np.float32),
+        "A_log": np.log(rng.uniform(1.0, 16.0, H)).astype(np.float32),
+        "dt_bias": (rng.standard_normal(H) * 0.5 - 2.0).astype(np.float32),
+        "w": (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32),
+    }
+    out["z"] = cast(rng.standard_normal((B, T, H, dv), dtype=np.float32), shape.in_dtype)
+    out["Wo"] = cast((rng.standard_normal((d_model, H * dv)) / np.sqrt(H * dv)).astype(np.float32), "bf16")
+    return out

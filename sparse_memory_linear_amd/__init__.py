@@ -19,7 +19,7 @@ __all__ = [
     "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
     "forward", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
-    "materialize",
+    "materialize", "gates", "output_gate", "head_mix",
 ]
 
 SDM_F32 = 0
@@ -72,6 +72,9 @@ _SIGS = {
     "sdm_forward_decay": (ctypes.c_int, [_SP] + [_P] * 13 + [ctypes.c_size_t, _P]),
     "sdm_decode_step_decay": (ctypes.c_int, [_SP] + [_P] * 11),
     "sdm_materialize": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P]),
+    "sdm_gates": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
+    "sdm_output_gate": (ctypes.c_int, [_SP, _P, _P, _P, ctypes.c_float, _P, _P]),
+    "sdm_head_mix": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
 }
 
 
@@ -208,3 +211,18 @@ def decode_step_decay(shape: Shape, q, k, v, alpha, beta, subkeys, M, lam, lrun,
 def materialize(shape: Shape, M, lam, lrun, out, stream=None):
     _check(lib().sdm_materialize(ctypes.byref(shape), _ptr(M), _ptr(lam), _ptr(lrun), _ptr(out), _stream(stream)),
            "sdm_materialize")
+
+
+# ----------------------------------------------------------------------------- gates and output
+def gates(shape: Shape, a, b, A_log, dt_bias, alpha, beta, stream=None):
+    _check(lib().sdm_gates(ctypes.byref(shape), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(alpha), _ptr(beta),
+                           _stream(stream)), "sdm_gates")
+
+
+def output_gate(shape: Shape, o, z, w, eps: float, x, stream=None):
+    _check(lib().sdm_output_gate(ctypes.byref(shape), _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(x),
+                                 _stream(stream)), "sdm_output_gate")
+
+
+def head_mix(x, Wo, y, M: int, K: int, N: int, stream=None):
+    _check(lib().sdm_head_mix(_ptr(x), _ptr(Wo), _ptr(y), int(M), int(K), int(N), _stream(stream)), "sdm_head_mix")

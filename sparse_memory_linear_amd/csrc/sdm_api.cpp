@@ -334,6 +334,49 @@ sdm_status sdm_materialize(const sdm_shape* S, const void* M, const double* lam,
   return hip_status(launch_materialize(*S, M, lam, lrun, out, (hipStream_t)stream));
 }
 
+sdm_status sdm_gates(const sdm_shape* S, const float* a, const float* b, const float* A_log, const float* dt_bias,
+                     float* alpha, float* beta, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  const void* ptrs[] = {a, b, A_log, dt_bias, alpha, beta};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SDM_ERR_INVALID_ARG;
+  const size_t gb = tensor_bytes(*S, 1, 4), hb = (size_t)S->H * 4;
+  const void* ins[] = {a, b};
+  for (const void* p : ins)
+    if (overlaps(p, gb, alpha, gb) || overlaps(p, gb, beta, gb)) return SDM_ERR_INVALID_ARG;
+  if (overlaps(alpha, gb, beta, gb) || overlaps(A_log, hb, alpha, gb) || overlaps(A_log, hb, beta, gb) ||
+      overlaps(dt_bias, hb, alpha, gb) || overlaps(dt_bias, hb, beta, gb))
+    return SDM_ERR_INVALID_ARG;
+  if (S->T == 0) return SDM_OK;
+  return hip_status(launch_gates(*S, a, b, A_log, dt_bias, alpha, beta, (hipStream_t)stream));
+}
+
+sdm_status sdm_output_gate(const sdm_shape* S, const float* o, const void* z, const float* w, float eps, void* x,
+                           void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!o || !z || !w || !x || !aligned16(o) || !aligned16(z) || !aligned16(w) || !aligned16(x))
+    return SDM_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || eps > 1.f) return SDM_ERR_INVALID_ARG;
+  const size_t ob = tensor_bytes(*S, S->d_v, 4), zb = tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype));
+  const size_t xb = tensor_bytes(*S, S->d_v, 2);
+  if (overlaps(x, xb, o, ob) || overlaps(x, xb, z, zb) || overlaps(x, xb, w, (size_t)S->d_v * 4))
+    return SDM_ERR_INVALID_ARG;
+  if (S->T == 0) return SDM_OK;
+  return hip_status(launch_output_gate(*S, o, z, w, eps, (uint16_t*)x, (hipStream_t)stream));
+}
+
+sdm_status sdm_head_mix(const void* x, const void* Wo, float* y, int64_t M, int32_t K, int32_t N, void* stream) {
+  if (M < 0 || K < 32 || K % 32 != 0 || N < 1) return SDM_ERR_INVALID_ARG;
+  if (M > ((int64_t)1 << 40) || K > (1 << 20) || N > (1 << 22)) return SDM_ERR_UNSUPPORTED;
+  if (!x || !Wo || !y || !aligned16(x) || !aligned16(Wo) || !aligned16(y)) return SDM_ERR_INVALID_ARG;
+  const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K * 2, yb = (size_t)M * N * 4;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, Wo, wb)) return SDM_ERR_INVALID_ARG;
+  if (M == 0) return SDM_OK;
+  return hip_status(launch_head_mix((const uint16_t*)x, (const uint16_t*)Wo, y, (long long)M, K, N, (hipStream_t)stream));
+}
+
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream) {
   if (!ws || !host_count || ws_bytes < 8 || !aligned16(ws)) return SDM_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;

@@ -59,6 +59,12 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
 hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun, hipStream_t stream);
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,
                              int* lastw, int win, hipStream_t stream);
+hipError_t launch_gates(const sdm_shape& S, const float* a, const float* b, const float* A_log, const float* dt_bias,
+                        float* alpha, float* beta, hipStream_t stream);
+hipError_t launch_output_gate(const sdm_shape& S, const float* o, const void* z, const float* w, float eps,
+                              uint16_t* x, hipStream_t stream);
+hipError_t launch_head_mix(const uint16_t* x, const uint16_t* Wo, float* y, long long M, int K, int N,
+                           hipStream_t stream);
 hipError_t launch_materialize(const sdm_shape& S, const void* M, const double* lam, const double* lrun, float* out,
                               hipStream_t stream);
 

@@ -190,3 +190,19 @@ def test_decay_needs_the_pipelined_recurrence(sdm, no_gpu):
     S = base(W=6, R=6)
     p = [FAKE + i * (1 << 36) for i in range(16)]
     assert L.sdm_recurrent_decay(ctypes.byref(S), *p[:12], 1 << 34, None) == -2
+
+
+# ----------------------------------------------------------------------------- gates and output
+def test_epilogue_calls_validate(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    p = [FAKE + i * (1 << 36) for i in range(8)]
+    assert L.sdm_gates(sp, None, *p[1:6], None) == -1
+    assert L.sdm_gates(sp, p[0], p[1], p[2], p[3], p[0] + 256, p[5], None) == -1  # alpha overlaps a
+    assert L.sdm_output_gate(sp, p[0], p[1], p[2], ctypes.c_float(-1.0), p[3], None) == -1  # negative eps
+    assert L.sdm_output_gate(sp, p[0], p[1], p[2], ctypes.c_float(1e-5), p[0] + 512, None) == -1  # x overlaps o
+    assert L.sdm_head_mix(p[0], p[1], p[2], 100, 48, 64, None) == -1    # K not a multiple of 32
+    assert L.sdm_head_mix(p[0], p[1], p[2], 100, 64, 0, None) == -1     # no output columns
+    assert L.sdm_head_mix(p[0], p[1], p[0] + 64, 100, 64, 64, None) == -1  # y overlaps x
+    assert L.sdm_head_mix(p[0], p[1], p[2], 0, 64, 64, None) == 0       # nothing to do

@@ -56,14 +56,17 @@ __global__ void __launch_bounds__(256) output_gate_kernel(const float* o, const 
 
 // ------------------------------------------------------------------ head mixing
 // y[M, N] = x[M, K] . Wo[N, K]^T, bf16 operands, float32 accumulation on MFMA
-// (v_mfma_f32_32x32x8bf16_1k). Workgroup tile 128 x 128 (four waves, 64 x 64 each), K in
-// steps of 32 staged through LDS; rows of the LDS tiles padded to 36 bf16 so that the 32
-// rows one fragment read touches fall in distinct banks.
+// (v_mfma_f32_32x32x16_bf16). Workgroup tile 128 x 128 (four waves, 64 x 64 each); K in
+// steps of 64 staged through LDS, the next step's global loads in flight while the current
+// one is multiplied. Each lane takes 8 consecutive k of its row of x and of Wo for one MFMA:
+// the same split of k for both operands, so the products pair up whatever the instruction's
+// internal order of k. Rows of the LDS tiles are padded to 72 bf16 (144 bytes) so that the
+// 16-byte fragment reads stay aligned.
 constexpr int kMixTile = 128;
-constexpr int kMixK = 32;
-constexpr int kMixPad = 36;
+constexpr int kMixK = 64;
+constexpr int kMixPad = 72;
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 __global__ void __launch_bounds__(256) head_mix_kernel(const uint16_t* X, const uint16_t* Wo, float* Y, long long M,
@@ -75,36 +78,40 @@ __global__ void __launch_bounds__(256) head_mix_kernel(const uint16_t* X, const 
   const int n0 = blockIdx.y * kMixTile;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   float16_t acc[2][2] = {};
-  // staging: each thread copies 16 bytes (8 bf16) of A and of B per K step, twice
+  // staging: 128 rows x 64 k of each operand = 1024 pieces of 8 bf16, four per thread
+  uint4 ra[4], rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = tid + r * 256, row = q >> 3, kk = (q & 7) * 8;
+      const bool kin = k0 + kk < K;  // K is a multiple of 32: the last step may be half full
+      ra[r] = kin && m0 + row < M ? *(const uint4*)(X + (m0 + row) * (long long)K + k0 + kk) : make_uint4(0u, 0u, 0u, 0u);
+      rb[r] = kin && n0 + row < N ? *(const uint4*)(Wo + (long long)(n0 + row) * K + k0 + kk) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  load(0);
   for (int k0 = 0; k0 < K; k0 += kMixK) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int q = tid + r * 256;          // 512 pieces of 8 bf16: row q / 4, k offset (q % 4) * 8
-      const int row = q >> 2, kk = (q & 3) * 8;
-      uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = make_uint4(0u, 0u, 0u, 0u);
-      if (m0 + row < M) va = *(const uint4*)(X + (m0 + row) * (long long)K + k0 + kk);
-      if (n0 + row < N) vb = *(const uint4*)(Wo + (long long)(n0 + row) * K + k0 + kk);
-      uint2* da = (uint2*)(As + row * kMixPad + kk);
-      uint2* db = (uint2*)(Bs + row * kMixPad + kk);
-      da[0] = make_uint2(va.x, va.y);
-      da[1] = make_uint2(va.z, va.w);
-      db[0] = make_uint2(vb.x, vb.y);
-      db[1] = make_uint2(vb.z, vb.w);
+    for (int r = 0; r < 4; ++r) {
+      const int q = tid + r * 256, row = q >> 3, kk = (q & 7) * 8;
+      *(uint4*)(As + row * kMixPad + kk) = ra[r];
+      *(uint4*)(Bs + row * kMixPad + kk) = rb[r];
     }
     __syncthreads();
+    if (k0 + kMixK < K) load(k0 + kMixK);
 #pragma unroll
-    for (int ks = 0; ks < kMixK; ks += 8) {
-      short4_t af[2], bf[2];
-      const int kq = ks + (lane >> 5) * 4;
+    for (int ks = 0; ks < kMixK; ks += 16) {
+      bf16x8_t af[2], bf[2];
+      const int kq = ks + (lane >> 5) * 8;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = *(const short4_t*)(As + (wm + i * 32 + (lane & 31)) * kMixPad + kq);
-        bf[i] = *(const short4_t*)(Bs + (wn + i * 32 + (lane & 31)) * kMixPad + kq);
+        af[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(As + (wm + i * 32 + (lane & 31)) * kMixPad + kq));
+        bf[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(Bs + (wn + i * 32 + (lane & 31)) * kMixPad + kq));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }

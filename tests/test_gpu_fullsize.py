@@ -172,3 +172,66 @@ def test_fullsize_decode(sdm):
         em = rel_err(Mh, M_ref)
         log(f"[full] decode unit ({b},{h}): o rel err {eo:.2e}, table rel err {em:.2e} (tol {tol})")
         assert eo < tol and em < tol
+
+
+def test_fullsize_decay_variant(sdm):
+    """The whole-table decay variant at the full 8B-scale shape (131072 tokens, 8 units):
+    with every gate alpha = 1 it decays nothing, so it must equal the written-rows path bit
+    for bit; with the workload's gates the running log-decay equals sum(log alpha), two
+    calls on the carried state match one call, and untouched slots keep lam = 0."""
+    import torch
+    sh = W_["layer_8b_long"]
+    log("[full] decay variant: generating inputs")
+    inp = SI.make_inputs(sh)
+    dev = upload(inp, sh)
+    S = lib_shape(sh)
+    wsd = torch.empty(sdm.workspace_bytes_decay(S), dtype=torch.uint8, device="cuda")
+
+    def run_decay(alpha, lo=0, hi=None, M=None, lam=None, lrun=None, wo=None):
+        hi = sh.T if hi is None else hi
+        Sp = lib_shape(sh, T=hi - lo)
+        if M is None:
+            M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+            sdm.init_from_M0(S, dev["M0"], M)
+            lam = torch.empty((sh.B, sh.H, sh.N), dtype=torch.float64, device="cuda")
+            lrun = torch.empty((sh.B, sh.H), dtype=torch.float64, device="cuda")
+            sdm.decay_state_init(S, lam, lrun)
+        sl = lambda t: t[:, :, lo:hi].clone()
+        o = torch.empty((sh.B, sh.H, hi - lo, sh.d_v), dtype=torch.float32, device="cuda")
+        sdm.forward_decay(Sp, sl(dev["q"]), sl(dev["k"]), sl(dev["v"]), sl(alpha), sl(dev["beta"]), dev["subkeys"],
+                          M, lam, lrun, o, wsd, wo)
+        return o, M, lam, lrun
+
+    ones = torch.ones_like(dev["alpha"])
+    log("[full] decay variant, alpha = 1")
+    o1, M1, lam1, lrun1 = run_decay(ones)
+    M2 = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, dev["M0"], M2)
+    o2 = torch.empty_like(o1)
+    ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    sdm.forward(S, dev["q"], dev["k"], dev["v"], ones, dev["beta"], dev["subkeys"], M2, o2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(M1, M2), "alpha = 1: decay variant differs from the plain path"
+    assert float(lrun1.abs().max()) == 0.0
+    log("[full] decay variant, workload gates, one call and two calls")
+    wo = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.int32, device="cuda")
+    oa, Ma, lama, lruna = run_decay(dev["alpha"], wo=wo)
+    T1 = sh.T // 2 + 5
+    ob1, Mb, lamb, lrunb = run_decay(dev["alpha"], 0, T1)
+    ob2, Mb, lamb, lrunb = run_decay(dev["alpha"], T1, sh.T, Mb, lamb, lrunb)
+    torch.cuda.synchronize()
+    L = np.log(inp["alpha"].astype(np.float64)).sum(-1)
+    assert np.allclose(lruna.cpu().numpy(), L, rtol=1e-9, atol=0)
+    assert np.allclose(lrunb.cpu().numpy(), L, rtol=1e-9, atol=0)
+    ob = torch.cat([ob1, ob2], 2).cpu().numpy()
+    assert rel_err(ob, oa.cpu().numpy()) < 1e-5
+    assert rel_err(SI.widen(from_dev(Mb, sh.mem_dtype), sh.mem_dtype),
+                   SI.widen(from_dev(Ma, sh.mem_dtype), sh.mem_dtype)) < 1e-2
+    # slots no token wrote keep lam = 0 (their value is still M0 times the whole decay);
+    # written ones hold the (negative) log-decay after their last writer
+    gw = wo.cpu().numpy()
+    for b, h in ((0, 0), (0, 7)):
+        touched = np.zeros(sh.N, bool)
+        touched[gw[b, h].ravel()] = True
+        lam_h = lama[b, h].cpu().numpy()
+        assert np.all(lam_h[~touched] == 0.0) and np.all(lam_h[touched] < 0.0)

@@ -56,6 +56,8 @@ __all__ = [
     "gates",
     "output_gate",
     "head_mix",
+    "recurrence_log",
+    "recurrence_backward",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -289,4 +291,75 @@ def head_mix(x, Wo):
     the layer output). READING R23: y = x Wo^T, no bias; x [M, H*d_v] (heads concatenated
     per token), Wo [d_model, H*d_v]."""
     return np.asarray(x, dtype=np.float64) @ np.asarray(Wo, dtype=np.float64).T
+
+
+# ----------------------------------------------------------------------------- backward
+def recurrence_log(M0, widx, wgt, v, alpha, beta, mem_dtype: str):
+    """The forward's record for the memory-efficient backward (PL App. A.3: sparse updates
+    are applied in place and undone in the backward, keeping O(N d + T W d) memory): the
+    pre-update values of each token's W write rows, xlog [T, W, d_v], as the token read
+    them. The reads do not change the table, so only the write slots are needed."""
+    M = np.array(M0, dtype=np.float64, copy=True)
+    T, d_v = len(widx), M.shape[1]
+    W = len(widx[0]) if T else 0
+    xlog = np.zeros((T, W, d_v))
+    for t in range(T):
+        n = np.asarray(widx[t])
+        a = np.asarray(wgt[t], dtype=np.float64)
+        prev = M[n]
+        xlog[t] = prev
+        dl = beta[t] * (v[t] - alpha[t] * (a @ prev))
+        M[n] = round_mem(alpha[t] * prev + a[:, None] * dl[None, :], mem_dtype)
+    return xlog
+
+
+def recurrence_backward(MT, xlog, widx, wgt, ridx, rgt, v, alpha, beta, go, dMT=None):
+    """Gradients of L = sum_t <go_t, o_t> + <dMT, M_T> through ``recurrence`` (written-rows
+    rule, R1), walking the tokens in reverse and restoring the table in place from the
+    forward's log (PL App. A.3). The rounding of written rows is passed through unchanged.
+
+    For token t (x_j = xlog[t, j], rho = alpha sum_j a_j x_j, delta = beta (v - rho)),
+    with G the gradient of L with respect to the table after token t:
+      read:   du_r = <go_t, M_t[m_r]>;  G[m_r] += u_r go_t
+      write:  dy_j = G[n_j];  d delta = sum_j a_j dy_j;  da_j = <dy_j, delta>
+              dalpha = sum_j <dy_j, x_j>;  dx_j = alpha dy_j
+              dv_t = beta d delta;  dbeta = <d delta, v_t - rho>;  d rho = -beta d delta
+              dalpha += <d rho, sum_j a_j x_j>;  da_j += alpha <d rho, x_j>
+              dx_j += alpha a_j d rho;  G[n_j] = dx_j
+      undo:   M[n_j] = x_j
+    Returns a dict: dv [T, d_v], dalpha [T], dbeta [T], dwgt [T, W], drgt [T, R],
+    dM0 [N, d_v] (G after token 0) and M0 (the table after every undo)."""
+    M = np.array(MT, dtype=np.float64, copy=True)
+    G = np.zeros_like(M) if dMT is None else np.array(dMT, dtype=np.float64, copy=True)
+    T, d_v = len(widx), M.shape[1]
+    W, R = (len(widx[0]), len(ridx[0])) if T else (0, 0)
+    dv, dal, dbe = np.zeros((T, d_v)), np.zeros(T), np.zeros(T)
+    dw, du = np.zeros((T, W)), np.zeros((T, R))
+    for t in reversed(range(T)):
+        n, m = np.asarray(widx[t]), np.asarray(ridx[t])
+        a, u = np.asarray(wgt[t], dtype=np.float64), np.asarray(rgt[t], dtype=np.float64)
+        x = np.asarray(xlog[t], dtype=np.float64)
+        g = np.asarray(go[t], dtype=np.float64)
+        # read after the write: o_t = sum_r u_r M_t[m_r]
+        du[t] = M[m] @ g
+        np.add.at(G, m, u[:, None] * g[None, :])
+        # write
+        s = a @ x
+        rho = alpha[t] * s
+        resid = v[t] - rho
+        delta = beta[t] * resid
+        dy = G[n].copy()
+        ddelta = a @ dy
+        dw[t] = dy @ delta
+        dal[t] = np.sum(dy * x)
+        dx = alpha[t] * dy
+        dv[t] = beta[t] * ddelta
+        dbe[t] = ddelta @ resid
+        drho = -beta[t] * ddelta
+        dal[t] += drho @ s
+        dw[t] += alpha[t] * (x @ drho)
+        dx += alpha[t] * a[:, None] * drho[None, :]
+        G[n] = dx
+        M[n] = x
+    return {"dv": dv, "dalpha": dal, "dbeta": dbe, "dwgt": dw, "drgt": du, "dM0": G, "M0": M}
 

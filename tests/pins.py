@@ -453,6 +453,47 @@ def pin_head_mix(O):
             assert abs(y[m, j] - ref) <= 1e-12 * max(1.0, abs(ref))
 
 
+# ----------------------------------------------------------------------------- backward
+def pin_backward_finite_differences(O):
+    """The reverse recurrence's gradients equal central finite differences of the forward
+    oracle (float64, no rounding) for every input: v, alpha, beta, write and read weights,
+    M0; and the undo restores M0 exactly."""
+    rng = np.random.default_rng(41)
+    N, d_v, T, W, R = 12, 3, 9, 3, 2
+    widx, wgt = _sparse_slots(rng, T, N, W)
+    ridx = np.array([np.concatenate([[widx[t][0]], rng.choice(np.setdiff1d(np.arange(N), [widx[t][0]]), R - 1,
+                                                                 replace=False)]) for t in range(T)])
+    rgt = rng.random((T, R)) + 0.1
+    v = rng.standard_normal((T, d_v))
+    alpha = rng.uniform(0.4, 0.95, T)
+    beta = rng.uniform(0.1, 0.9, T)
+    M0 = rng.standard_normal((N, d_v))
+    go = rng.standard_normal((T, d_v))
+    dMT = rng.standard_normal((N, d_v))
+
+    def loss(M0_, v_, al_, be_, w_, u_):
+        o, M = O.recurrence(M0_, widx, w_, ridx, u_, v_, al_, be_, "f64")
+        return float(np.sum(go * o) + np.sum(dMT * M))
+
+    o, MT = O.recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, "f64")
+    xlog = O.recurrence_log(M0, widx, wgt, v, alpha, beta, "f64")
+    g = O.recurrence_backward(MT, xlog, widx, wgt, ridx, rgt, v, alpha, beta, go, dMT)
+    assert np.array_equal(g["M0"], M0)
+    args = [M0, v, alpha, beta, wgt, rgt]
+    names = ["dM0", "dv", "dalpha", "dbeta", "dwgt", "drgt"]
+    h = 1e-6
+    for k, name in enumerate(names):
+        base = args[k]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus = [np.array(a_, dtype=np.float64, copy=True) for a_ in args]
+            minus = [np.array(a_, dtype=np.float64, copy=True) for a_ in args]
+            plus[k][idx] += h
+            minus[k][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert np.allclose(g[name], num, rtol=1e-6, atol=1e-7), name
+
+
 ALL_PINS = [
     pin_round_bf16,
     pin_pk_equals_brute_force,
@@ -474,4 +515,5 @@ ALL_PINS = [
     pin_gates_closed_forms,
     pin_output_gate,
     pin_head_mix,
+    pin_backward_finite_differences,
 ]

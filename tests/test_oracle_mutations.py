@@ -65,6 +65,12 @@ MUTANTS = {
     "gate_sigmoid": ("(z / (1.0 + np.exp(-z)))", "(1.0 / (1.0 + np.exp(-z)))"),
     # head mixing with the untransposed weight
     "mix_transposed": ("@ np.asarray(Wo, dtype=np.float64).T", "@ np.asarray(Wo, dtype=np.float64).T[::-1]"),
+    # backward: the read's gradient added after the write part
+    "bwd_read_after_write": ("        np.add.at(G, m, u[:, None] * g[None, :])\n", "\n"),
+    # backward: the residual's decay dropped from the weight gradient
+    "bwd_dw_no_alpha": ("dw[t] += alpha[t] * (x @ drho)", "dw[t] += (x @ drho)"),
+    # backward: the table's gradient accumulated instead of replaced at the written rows
+    "bwd_g_accumulate": ("        G[n] = dx\n", "        G[n] += dx\n"),
     # per-half top-k keeps too few sub-keys
     "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
 }

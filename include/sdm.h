@@ -142,6 +142,36 @@ sdm_status sdm_decode_step(const sdm_shape* shape, const void* q, const void* k,
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Memory-efficient backward of the recurrence (PL App. A.3: the forward's sparse updates
+ * are undone in place during the backward, so memory stays O(N d + T W d)).
+ * --------------------------------------------------------------------------------------- */
+
+/* sdm_recurrent that also logs, for the backward, the pre-update value of every written row
+ * as its token read it: xlog [B,H,T,W,d_v] mem_dtype out (rows of slots outside [0, N) are
+ * 0). T*W*d_v*sizeof(mem) must stay below 2^31 bytes per unit. Written-rows rule only. */
+sdm_status sdm_recurrent_log(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                             const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
+                             void* xlog, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of L = sum <go, o> + <G_in, M_T> through the recurrence of sdm_recurrent_log,
+ * walking the tokens in reverse (for token t, x_j = xlog[t, j], s = sum_j wgt_j x_j,
+ * rho = alpha_t s, delta = beta_t (v_t - rho), G the gradient of the current table):
+ *   drgt_r = <go_t, M[ridx_r]>;  G[ridx_r] += rgt_r go_t
+ *   dy_j = G[widx_j];  dd = sum_j wgt_j dy_j;  dv_t = beta_t dd;  drho = -beta_t dd
+ *   dwgt_j = <dy_j, delta> + alpha_t <drho, x_j>
+ *   dalpha_t = sum_j <dy_j, x_j> + <drho, s>;  dbeta_t = <dd, v_t - rho>
+ *   G[widx_j] = alpha_t dy_j + alpha_t wgt_j drho;  M[widx_j] = x_j  (undo)
+ * The rounding of written rows to mem_dtype is passed through (straight-through).
+ *   M [B,H,N,d_v] mem_dtype: the table after the forward in, M0 out (restored in place)
+ *   G [B,H,N,d_v] f32: gradient of the final table in (zeros if none), of M0 out
+ *   go, dv [B,H,T,d_v] f32; dalpha, dbeta [B,H,T] f32; dwgt [B,H,T,W], drgt [B,H,T,R] f32
+ * Other arguments as for sdm_recurrent; W, R <= 64. Needs no workspace. */
+sdm_status sdm_recurrent_backward(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                                  const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                                  const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
+                                  float* dwgt, float* drgt, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * The steps on either side of the recurrence (PL App. B "Gate dynamics": forget gate
  * exp(g), input gate sigma(b); PL §4 "SDM Configuration": gate and time-step bias as in
  * Gated DeltaNet; PL §3 "Sparse retrieval": the read is RMS-normalised, elementwise gated

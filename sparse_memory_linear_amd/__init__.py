@@ -19,7 +19,7 @@ __all__ = [
     "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
     "forward", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
-    "materialize", "gates", "output_gate", "head_mix",
+    "materialize", "gates", "output_gate", "head_mix", "recurrent_log", "recurrent_backward",
 ]
 
 SDM_F32 = 0
@@ -75,6 +75,8 @@ _SIGS = {
     "sdm_gates": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
     "sdm_output_gate": (ctypes.c_int, [_SP, _P, _P, _P, ctypes.c_float, _P, _P]),
     "sdm_head_mix": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "sdm_recurrent_log": (ctypes.c_int, [_SP] + [_P] * 11 + [ctypes.c_size_t, _P]),
+    "sdm_recurrent_backward": (ctypes.c_int, [_SP] + [_P] * 17),
 }
 
 
@@ -226,3 +228,18 @@ def output_gate(shape: Shape, o, z, w, eps: float, x, stream=None):
 
 def head_mix(x, Wo, y, M: int, K: int, N: int, stream=None):
     _check(lib().sdm_head_mix(_ptr(x), _ptr(Wo), _ptr(y), int(M), int(K), int(N), _stream(stream)), "sdm_head_mix")
+
+
+# ----------------------------------------------------------------------------- backward
+def recurrent_log(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, xlog, ws, stream=None):
+    _check(lib().sdm_recurrent_log(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
+                                   _ptr(alpha), _ptr(beta), _ptr(M), _ptr(o), _ptr(xlog), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "sdm_recurrent_log")
+
+
+def recurrent_backward(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dalpha, dbeta, dwgt,
+                       drgt, stream=None):
+    _check(lib().sdm_recurrent_backward(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
+                                        _ptr(alpha), _ptr(beta), _ptr(M), _ptr(xlog), _ptr(go), _ptr(G), _ptr(dv),
+                                        _ptr(dalpha), _ptr(dbeta), _ptr(dwgt), _ptr(drgt), _stream(stream)),
+           "sdm_recurrent_backward")

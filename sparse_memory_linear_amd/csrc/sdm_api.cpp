@@ -86,7 +86,7 @@ sdm_status check_decay(const sdm_shape* S, const double* lam, const double* lrun
 
 sdm_status recurrent_impl(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                           const float* rgt, const void* v, const float* alpha, const float* beta, void* M, double* lam,
-                          double* lrun, float* o, void* ws, size_t ws_bytes, void* stream) {
+                          double* lrun, float* o, void* ws, size_t ws_bytes, void* stream, void* xlog = nullptr) {
   sdm_status st = check_shape(S, true);
   if (st != SDM_OK) return st;
   if (!widx || !wgt || !ridx || !rgt || !v || !alpha || !beta || !M || !o) return SDM_ERR_INVALID_ARG;
@@ -103,12 +103,21 @@ sdm_status recurrent_impl(const sdm_shape* S, const int32_t* widx, const float* 
   if (overlaps(M, mb, o, ob) || overlaps(M, mb, ws, ws_bytes) || overlaps(o, ob, ws, ws_bytes)) return SDM_ERR_INVALID_ARG;
   st = check_decay(S, lam, lrun, M, mb, o, ob, ws, ws_bytes);
   if (st != SDM_OK) return st;
+  if (xlog) {
+    if (!aligned16(xlog)) return SDM_ERR_INVALID_ARG;
+    const size_t lb = tensor_bytes(*S, (int64_t)S->W * S->d_v, dtype_size(S->mem_dtype));
+    if (overlaps(xlog, lb, M, mb) || overlaps(xlog, lb, o, ob) || overlaps(xlog, lb, ws, ws_bytes))
+      return SDM_ERR_INVALID_ARG;
+    // one unit's log is addressed with 32-bit buffer offsets
+    if ((size_t)S->T * S->W * S->d_v * dtype_size(S->mem_dtype) > 0x7FFFFFFFull) return SDM_ERR_UNSUPPORTED;
+  }
   if (S->T == 0) return SDM_OK;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = launch_zero((char*)ws + L.err, 1, hs);
   if (e != hipSuccess) return SDM_ERR_HIP;
   DecayState dk{lam, lrun};
-  return hip_status(launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, decay ? &dk : nullptr, hs));
+  return hip_status(
+      launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, decay ? &dk : nullptr, hs, xlog));
 }
 
 sdm_status forward_impl(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
@@ -281,6 +290,46 @@ sdm_status sdm_forward(const sdm_shape* S, const void* q, const void* k, const v
 sdm_status sdm_decode_step(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const void* subkeys, void* M, float* o, void* stream) {
   return decode_impl(S, q, k, v, alpha, beta, subkeys, M, nullptr, nullptr, o, stream);
+}
+
+sdm_status sdm_recurrent_log(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                             const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
+                             void* xlog, void* ws, size_t ws_bytes, void* stream) {
+  if (!xlog) return SDM_ERR_INVALID_ARG;
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!dataflow_supported(*S)) return SDM_ERR_UNSUPPORTED;
+  return recurrent_impl(S, widx, wgt, ridx, rgt, v, alpha, beta, M, nullptr, nullptr, o, ws, ws_bytes, stream, xlog);
+}
+
+sdm_status sdm_recurrent_backward(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                                  const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                                  const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
+                                  float* dwgt, float* drgt, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  const void* ptrs[] = {widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dalpha, dbeta, dwgt, drgt};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SDM_ERR_INVALID_ARG;
+  const size_t U = (size_t)S->B * S->H;
+  const size_t mb = U * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype), gb = U * (size_t)S->N * S->d_v * 4;
+  const size_t lb = tensor_bytes(*S, (int64_t)S->W * S->d_v, dtype_size(S->mem_dtype));
+  const size_t vb = tensor_bytes(*S, S->d_v, 4), sb = tensor_bytes(*S, 1, 4);
+  const size_t wb = tensor_bytes(*S, S->W, 4), rb = tensor_bytes(*S, S->R, 4);
+  // outputs apart from each other and from every input
+  const void* outs[] = {M, G, dv, dalpha, dbeta, dwgt, drgt};
+  const size_t osz[] = {mb, gb, vb, sb, sb, wb, rb};
+  const void* ins[] = {widx, wgt, ridx, rgt, v, alpha, beta, xlog, go};
+  const size_t isz[] = {wb, wb, rb, rb, tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype)), sb, sb, lb, vb};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SDM_ERR_INVALID_ARG;
+    for (int j = 0; j < 9; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return SDM_ERR_INVALID_ARG;
+  }
+  if (S->T == 0) return SDM_OK;
+  return hip_status(launch_backward(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dalpha, dbeta,
+                                    dwgt, drgt, (hipStream_t)stream));
 }
 
 size_t sdm_workspace_bytes_decay(const sdm_shape* shape) {

@@ -149,6 +149,7 @@ struct PipeArgs {
   int U, T, W, R, E, d_v, P;
   int S, RS, SM, win, tpb, vw, rowbytes;
   const float* fac;  // [U][T][E] decay factors of the accesses (whole-table decay), or null
+  void* xlog;        // [U][T][W][d_v] pre-update write rows for the backward, or null
   int pack2;  // two tokens' write rows per store instruction
   int nh;     // compute passes per half wave: ceil(max(W, R) / (32 / lanes per row))
   long long N;
@@ -673,6 +674,16 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
         }
       }
     }
+    if (A.xlog && hh == 0) {
+      // the pre-update write rows as this token read them, for the backward's undo
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+          (char*)A.xlog + (size_t)u * T * W * A.rowbytes, (short)0, (int)((size_t)T * W * A.rowbytes), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const int j = i * GH + gh;
+        if (i < nh && j < W) buf_store(xv[i], xr, (uint32_t)(((size_t)t * W + j) * A.rowbytes) + colb);
+      }
+    }
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
@@ -930,7 +941,7 @@ size_t dataflow_sched_words(const sdm_shape& S) {
 
 hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                           void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream) {
+                           void* ws, const WsLayout& L, const DecayState* dk, void* xlog, hipStream_t stream) {
   PipeCfg c;
   if (!pipe_config(S, device_cus(), dk != nullptr, &c)) return hipErrorInvalidValue;
   const int U = S.B * S.H;
@@ -964,6 +975,7 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   PipeArgs A;
   A.pk = pk;
   A.fac = fac;
+  A.xlog = xlog;
   A.wgt = wgt;
   A.rgt = rgt;
   A.v = v;

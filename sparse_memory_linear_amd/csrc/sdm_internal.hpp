@@ -43,7 +43,8 @@ hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys
 hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t stream);
 hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                             const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                            void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream);
+                            void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream,
+                            void* xlog = nullptr);
 hipError_t launch_decode(const sdm_shape& S, const void* q, const void* k, const void* v, const float* alpha,
                          const float* beta, const void* subkeys, void* M, float* o, const DecayState* dk,
                          hipStream_t stream);
@@ -54,7 +55,11 @@ size_t dataflow_deps_bytes(const sdm_shape& S);
 size_t dataflow_sched_words(const sdm_shape& S);
 hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                           void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream);
+                           void* ws, const WsLayout& L, const DecayState* dk, void* xlog, hipStream_t stream);
+hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                           const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                           const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
+                           float* dwgt, float* drgt, hipStream_t stream);
 
 hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun, hipStream_t stream);
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,

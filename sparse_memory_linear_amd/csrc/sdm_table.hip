@@ -183,7 +183,7 @@ hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t 
 
 hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                             const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
-                            void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream) {
+                            void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream, void* xlog) {
   RecArgs A;
   A.widx = widx;
   A.wgt = wgt;
@@ -203,8 +203,8 @@ hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float
   A.N = S.N;
   if (A.U == 0 || A.T == 0) return hipSuccess;
   if (dataflow_supported(S, dk != nullptr))
-    return launch_dataflow(S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, dk, stream);
-  if (dk) return hipErrorInvalidValue;  // whole-table decay runs on the pipeline only
+    return launch_dataflow(S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, dk, xlog, stream);
+  if (dk || xlog) return hipErrorInvalidValue;  // whole-table decay and the row log run on the pipeline only
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
   if (mb && ib) return launch_seq<uint16_t, uint16_t>(A, stream);
   if (mb && !ib) return launch_seq<uint16_t, float>(A, stream);

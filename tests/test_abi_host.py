@@ -206,3 +206,23 @@ def test_epilogue_calls_validate(sdm, no_gpu):
     assert L.sdm_head_mix(p[0], p[1], p[2], 100, 64, 0, None) == -1     # no output columns
     assert L.sdm_head_mix(p[0], p[1], p[0] + 64, 100, 64, 64, None) == -1  # y overlaps x
     assert L.sdm_head_mix(p[0], p[1], p[2], 0, 64, 64, None) == 0       # nothing to do
+
+
+# ----------------------------------------------------------------------------- backward
+def test_backward_calls_validate(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    p = [FAKE + i * (1 << 36) for i in range(20)]
+    need = sdm.workspace_bytes(S)
+    assert L.sdm_recurrent_log(sp, *p[:9], None, p[10], need, None) == -1            # no log buffer
+    assert L.sdm_recurrent_log(sp, *p[:9], p[7] + 4096, p[10], need, None) == -1     # log inside the table
+    args = list(p[:16])
+    args[10] = args[7] + 64                                                            # G overlaps M
+    assert L.sdm_recurrent_backward(sp, *args, None) == -1
+    args = list(p[:16])
+    args[11] = args[9]                                                                 # dv overlaps go
+    assert L.sdm_recurrent_backward(sp, *args, None) == -1
+    args = list(p[:16])
+    args[0] = None
+    assert L.sdm_recurrent_backward(sp, *args, None) == -1

@@ -1,0 +1,97 @@
+"""Memory-efficient backward on the GPU against the oracle: the forward's log of pre-update
+write rows, the reverse walk's gradients (v, alpha, beta, write and read weights, M0) and the
+in-place undo that restores M0. The oracle runs its own forward and backward on the same
+inputs (slots and weights from the oracle's addressing)."""
+import numpy as np
+import pytest
+
+import oracle.sdm_oracle as O
+import sdm_inputs as SI
+from parity import empty_mem, from_dev, lib_shape, log, rel_err, to_dev, tolerance
+
+pytestmark = pytest.mark.gpu
+
+W_ = SI.WORKLOADS
+CASES = {
+    "tiny_fp32": W_["tiny_fp32"],
+    "small_T128": W_["small"].replace(B=1, H=2, T=128),
+    "layer_8b_T100": W_["layer_8b_long"].replace(B=1, H=2, T=100),
+}
+
+
+@pytest.fixture(scope="module")
+def sdm():
+    import torch
+    import sparse_memory_linear_amd as S
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    S.lib()
+    return S
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_log_and_backward(sdm, name):
+    import torch
+    sh = CASES[name]
+    log(f"[backward] {name}")
+    inp = SI.make_inputs(sh)
+    S = lib_shape(sh)
+    rng = np.random.default_rng(17)
+    go = rng.standard_normal((sh.B, sh.H, sh.T, sh.d_v)).astype(np.float32)
+    dMT = np.zeros((sh.B, sh.H, sh.N, sh.d_v), np.float32)
+    shp_w, shp_r = (sh.B, sh.H, sh.T, sh.W), (sh.B, sh.H, sh.T, sh.R)
+    widx, wgt = np.zeros(shp_w, np.int32), np.zeros(shp_w, np.float32)
+    ridx, rgt = np.zeros(shp_r, np.int32), np.zeros(shp_r, np.float32)
+    ref = {}
+    for b in range(sh.B):
+        for h in range(sh.H):
+            sk = SI.widen(inp["subkeys"][h], sh.in_dtype)
+            k = SI.widen(inp["k"][b, h], sh.in_dtype)
+            q = SI.widen(inp["q"][b, h], sh.in_dtype)
+            v = SI.widen(inp["v"][b, h], sh.in_dtype)
+            al, be = inp["alpha"][b, h].astype(np.float64), inp["beta"][b, h].astype(np.float64)
+            M0 = SI.widen(inp["M0"][h], sh.mem_dtype)
+            wi, ww, _ = O.address(k, sk[0], sk[1], sh.kappa, sh.W)
+            ri, rw, _ = O.address(q, sk[0], sk[1], sh.kappa, sh.R)
+            ww, rw = ww.astype(np.float32), rw.astype(np.float32)
+            widx[b, h], wgt[b, h], ridx[b, h], rgt[b, h] = wi, ww, ri, rw
+            o, MT = O.recurrence(M0, wi, ww.astype(np.float64), ri, rw.astype(np.float64), v, al, be, sh.mem_dtype)
+            xl = O.recurrence_log(M0, wi, ww.astype(np.float64), v, al, be, sh.mem_dtype)
+            g = O.recurrence_backward(MT, xl, wi, ww.astype(np.float64), ri, rw.astype(np.float64), v, al, be,
+                                      go[b, h].astype(np.float64))
+            ref[(b, h)] = (o, MT, xl, g)
+    dev = {n: to_dev(inp[n], sh.in_dtype) for n in ("v",)}
+    alpha, beta = to_dev(inp["alpha"], "f32"), to_dev(inp["beta"], "f32")
+    M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, to_dev(inp["M0"], sh.mem_dtype), M)
+    M0_dev = M.clone()
+    o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+    xlog = empty_mem((sh.B, sh.H, sh.T, sh.W, sh.d_v), sh.mem_dtype)
+    ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    dW, dR = to_dev(widx, "i32"), to_dev(ridx, "i32")
+    aW, aR = to_dev(wgt, "f32"), to_dev(rgt, "f32")
+    sdm.recurrent_log(S, dW, aW, dR, aR, dev["v"], alpha, beta, M, o, xlog, ws)
+    torch.cuda.synchronize()
+    tol = tolerance(sh)
+    gx = SI.widen(from_dev(xlog, sh.mem_dtype), sh.mem_dtype)
+    go_o = o.cpu().numpy()
+    for (b, h), (ro, rMT, rxl, _) in ref.items():
+        eo, ex = rel_err(go_o[b, h], ro), rel_err(gx[b, h], rxl)
+        log(f"[backward] {name} forward ({b},{h}): o {eo:.2e} log {ex:.2e}")
+        assert eo < tol and ex < tol
+    # backward from the GPU's own final table and log
+    G = to_dev(dMT, "f32")
+    dv = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+    dal = torch.empty((sh.B, sh.H, sh.T), dtype=torch.float32, device="cuda")
+    dbe = torch.empty_like(dal)
+    dwg = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.float32, device="cuda")
+    drg = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
+    sdm.recurrent_backward(S, dW, aW, dR, aR, dev["v"], alpha, beta, M, xlog, to_dev(go, "f32"), G, dv, dal, dbe,
+                           dwg, drg)
+    torch.cuda.synchronize()
+    assert torch.equal(M, M0_dev), "the undo did not restore M0 bit for bit"
+    out = {"dv": dv, "dalpha": dal, "dbeta": dbe, "dwgt": dwg, "drgt": drg, "dM0": G}
+    for (b, h), (_, _, _, g) in ref.items():
+        errs = {k: rel_err(t[b, h].cpu().numpy(), g[k]) for k, t in out.items()}
+        log(f"[backward] {name} grads ({b},{h}): " + " ".join(f"{k} {e:.1e}" for k, e in errs.items()) + f" (tol {tol})")
+        for k, e in errs.items():
+            assert e < tol, k

@@ -153,6 +153,11 @@ sdm_status sdm_recurrent_log(const sdm_shape* shape, const int32_t* widx, const 
                              const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                              void* xlog, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device memory sdm_recurrent_backward needs as workspace (0 for an invalid shape):
+ * per token a dependency mask, a store mask and the read-write coupling tables (W + R floats),
+ * and the error word at offset 0 (sdm_workspace_error reads it). */
+size_t sdm_backward_workspace_bytes(const sdm_shape* shape);
+
 /* Gradients of L = sum <go, o> + <G_in, M_T> through the recurrence of sdm_recurrent_log,
  * walking the tokens in reverse (for token t, x_j = xlog[t, j], s = sum_j wgt_j x_j,
  * rho = alpha_t s, delta = beta_t (v_t - rho), G the gradient of the current table):
@@ -165,11 +170,17 @@ sdm_status sdm_recurrent_log(const sdm_shape* shape, const int32_t* widx, const 
  *   M [B,H,N,d_v] mem_dtype: the table after the forward in, M0 out (restored in place)
  *   G [B,H,N,d_v] f32: gradient of the final table in (zeros if none), of M0 out
  *   go, dv [B,H,T,d_v] f32; dalpha, dbeta [B,H,T] f32; dwgt [B,H,T,W], drgt [B,H,T,R] f32
- * Other arguments as for sdm_recurrent; W, R <= 64. Needs no workspace. */
+ * Other arguments as for sdm_recurrent; W, R <= 64; read slots may repeat and may equal the
+ * token's write slots; a slot outside [0, N) touches nothing and gets zero gradients.
+ * Per unit, N*d_v*4, T*d_v*4 and T*W*d_v*sizeof(mem) bytes must each stay below 2^32.
+ * ws: at least sdm_backward_workspace_bytes(shape) bytes, apart from every other buffer; its
+ * error word counts workgroups that gave up waiting (about 3.6 s; the result is then
+ * invalid). Floating-point sums over columns are added with atomics: the summation order of
+ * dwgt, drgt, dalpha and dbeta can differ from run to run. */
 sdm_status sdm_recurrent_backward(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
                                   const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
                                   const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
-                                  float* dwgt, float* drgt, void* stream);
+                                  float* dwgt, float* drgt, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * The steps on either side of the recurrence (PL App. B "Gate dynamics": forget gate

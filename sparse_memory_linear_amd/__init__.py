@@ -20,6 +20,7 @@ __all__ = [
     "forward", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
     "materialize", "gates", "output_gate", "head_mix", "recurrent_log", "recurrent_backward",
+    "backward_workspace_bytes",
 ]
 
 SDM_F32 = 0
@@ -76,7 +77,8 @@ _SIGS = {
     "sdm_output_gate": (ctypes.c_int, [_SP, _P, _P, _P, ctypes.c_float, _P, _P]),
     "sdm_head_mix": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
     "sdm_recurrent_log": (ctypes.c_int, [_SP] + [_P] * 11 + [ctypes.c_size_t, _P]),
-    "sdm_recurrent_backward": (ctypes.c_int, [_SP] + [_P] * 17),
+    "sdm_backward_workspace_bytes": (ctypes.c_size_t, [_SP]),
+    "sdm_recurrent_backward": (ctypes.c_int, [_SP] + [_P] * 17 + [ctypes.c_size_t, _P]),
 }
 
 
@@ -237,9 +239,13 @@ def recurrent_log(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, xlog
                                    ws.numel() * ws.element_size(), _stream(stream)), "sdm_recurrent_log")
 
 
+def backward_workspace_bytes(shape: Shape) -> int:
+    return lib().sdm_backward_workspace_bytes(ctypes.byref(shape))
+
+
 def recurrent_backward(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dalpha, dbeta, dwgt,
-                       drgt, stream=None):
+                       drgt, ws, stream=None):
     _check(lib().sdm_recurrent_backward(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
                                         _ptr(alpha), _ptr(beta), _ptr(M), _ptr(xlog), _ptr(go), _ptr(G), _ptr(dv),
-                                        _ptr(dalpha), _ptr(dbeta), _ptr(dwgt), _ptr(drgt), _stream(stream)),
-           "sdm_recurrent_backward")
+                                        _ptr(dalpha), _ptr(dbeta), _ptr(dwgt), _ptr(drgt), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)), "sdm_recurrent_backward")

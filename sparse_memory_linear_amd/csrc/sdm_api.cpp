@@ -302,34 +302,45 @@ sdm_status sdm_recurrent_log(const sdm_shape* S, const int32_t* widx, const floa
   return recurrent_impl(S, widx, wgt, ridx, rgt, v, alpha, beta, M, nullptr, nullptr, o, ws, ws_bytes, stream, xlog);
 }
 
+size_t sdm_backward_workspace_bytes(const sdm_shape* shape) {
+  if (check_shape(shape, true) != SDM_OK) return 0;
+  return backward_workspace_bytes(*shape);
+}
+
 sdm_status sdm_recurrent_backward(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                                   const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
                                   const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
-                                  float* dwgt, float* drgt, void* stream) {
+                                  float* dwgt, float* drgt, void* ws, size_t ws_bytes, void* stream) {
   sdm_status st = check_shape(S, true);
   if (st != SDM_OK) return st;
   const void* ptrs[] = {widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dalpha, dbeta, dwgt, drgt};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return SDM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < backward_workspace_bytes(*S)) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
   const size_t U = (size_t)S->B * S->H;
+  // per-unit row traffic uses 32-bit byte offsets
+  if ((size_t)S->N * S->d_v * 4 > 0xFFFFFFFFull || (size_t)S->T * S->d_v * 4 > 0xFFFFFFFFull ||
+      (size_t)S->T * S->W * S->d_v * dtype_size(S->mem_dtype) > 0xFFFFFFFFull)
+    return SDM_ERR_INVALID_ARG;
   const size_t mb = U * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype), gb = U * (size_t)S->N * S->d_v * 4;
   const size_t lb = tensor_bytes(*S, (int64_t)S->W * S->d_v, dtype_size(S->mem_dtype));
   const size_t vb = tensor_bytes(*S, S->d_v, 4), sb = tensor_bytes(*S, 1, 4);
   const size_t wb = tensor_bytes(*S, S->W, 4), rb = tensor_bytes(*S, S->R, 4);
-  // outputs apart from each other and from every input
-  const void* outs[] = {M, G, dv, dalpha, dbeta, dwgt, drgt};
-  const size_t osz[] = {mb, gb, vb, sb, sb, wb, rb};
+  // outputs (and the workspace) apart from each other and from every input
+  const void* outs[] = {M, G, dv, dalpha, dbeta, dwgt, drgt, ws};
+  const size_t osz[] = {mb, gb, vb, sb, sb, wb, rb, ws_bytes};
   const void* ins[] = {widx, wgt, ridx, rgt, v, alpha, beta, xlog, go};
   const size_t isz[] = {wb, wb, rb, rb, tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype)), sb, sb, lb, vb};
-  for (int i = 0; i < 7; ++i) {
-    for (int j = i + 1; j < 7; ++j)
+  for (int i = 0; i < 8; ++i) {
+    for (int j = i + 1; j < 8; ++j)
       if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SDM_ERR_INVALID_ARG;
     for (int j = 0; j < 9; ++j)
       if (overlaps(outs[i], osz[i], ins[j], isz[j])) return SDM_ERR_INVALID_ARG;
   }
   if (S->T == 0) return SDM_OK;
   return hip_status(launch_backward(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dalpha, dbeta,
-                                    dwgt, drgt, (hipStream_t)stream));
+                                    dwgt, drgt, ws, (hipStream_t)stream));
 }
 
 size_t sdm_workspace_bytes_decay(const sdm_shape* shape) {

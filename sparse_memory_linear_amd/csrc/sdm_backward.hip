@@ -12,11 +12,25 @@
 //          dalpha = sum_j <dy_j, x_j> + <d rho, s>;  dbeta = <d delta, v - rho>
 //          G[n_j] = alpha dy_j + alpha a_j d rho
 //   undo:  M[n_j] = x_j
-// Every column of the table and of G evolves on its own, so a wave owns 64 columns of one
-// unit and walks all its tokens: each lane touches only its own column of every row, and
-// needs no synchronisation with other lanes or waves for the table. The scalar gradients
-// (sums over columns) are reduced in the wave through LDS and added across the column
-// blocks with atomics into outputs zeroed first.
+//
+// Every column of the table and of G evolves on its own, and two tokens interact only
+// through a slot they share. A workgroup owns C columns of one unit; its K waves take the
+// tokens in reverse, wave w the tokens T-1-w, T-1-w-K, ... A token starts once every later
+// token that shares a slot with it has finished (at most K-1 of them can still be running;
+// the preparation pass lists them per token as a bit mask) and every token K or more later
+// has finished; a wave publishes a finished token in an LDS ring once its stores are
+// complete. Inside a wave, NG row groups of C = 64 / NG lanes hold the same C columns and
+// split the token's rows (up to 8 write and 8 read rows per group); only the sums over rows
+// (s and d delta) cross between groups.
+//
+// Each token issues all of its row loads at once. The read-write coupling inside a token (a
+// read slot that is also written: its G update must land before the write consumes G) is
+// resolved by tables from the preparation pass instead of through memory: wadd_j, the sum
+// of u_r over the reads of slot n_j, is folded into dy_j, and only reads of slots the token
+// does not write store G (the first of equal read slots, carrying their summed weight).
+// Slot lists and tables are fetched two own tokens ahead; the sums over columns (weight,
+// alpha and beta gradients) go through LDS and shuffles and are added across column blocks
+// with atomics into outputs zeroed first.
 
 #include "sdm_device.hpp"
 #include "sdm_internal.hpp"
@@ -25,25 +39,144 @@ namespace sdm {
 
 namespace {
 
-constexpr int kCols = 64;      // columns per wave
-constexpr int kMaxSel = 64;    // W, R <= 64
+constexpr int kMaxSel = 64;        // W, R <= 64
+constexpr int kXcd = 8;            // workgroups are dealt round-robin to this many L2 domains
+constexpr uint32_t kNone = ~0u;    // row slot of a row that touches nothing
+constexpr int MH = 8;              // rows of each kind per row group
+constexpr int kMaxWaves = 16;      // waves per workgroup (K)
+constexpr int kFinRing = 128;      // finished-token ring (> 4 K: a token waits on at most
+                                   // 2K - 1 later tokens, none older than 2K is running)
+constexpr int kPrepBlk = 16;       // tokens per preparation workgroup
+// Longest a wave waits for another (in units of s_sleep 1, ~27 ns): about 3.6 s. When it
+// runs out the workgroup gives up, every wave exits, and the error word counts it.
+constexpr long long kSpinBudget = 1ll << 27;
 
-template <typename T>
-__device__ __forceinline__ float ld_val(const T* p, size_t i) {
-  if constexpr (sizeof(T) == 2) return bf16_to_f32(p[i]);
-  else return p[i];
+// Row traffic goes through buffer instructions on per-unit resources: a 32-bit byte offset
+// per row (one register) instead of a 64-bit address. Loads return the raw bits (bf16 in
+// the low half), so that no use of a load has to wait before the token's other loads are
+// issued; cvt() turns them into a float.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rs(const void* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
 template <typename T>
-__device__ __forceinline__ void st_val(T* p, size_t i, float x) {
-  if constexpr (sizeof(T) == 2) p[i] = (uint16_t)pack_bf16x2(x, 0.f);
-  else p[i] = x;
+__device__ __forceinline__ uint32_t bld(rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(T) == 2) return __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+}
+template <typename T>
+__device__ __forceinline__ void bst(rsrc_t rs, uint32_t off, float x) {
+  if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pack_bf16x2(x, 0.f), rs, off, 0, 0);
+  else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
+}
+template <typename T>
+__device__ __forceinline__ float cvt(uint32_t r) {
+  if constexpr (sizeof(T) == 2) return __uint_as_float(r << 16);
+  else return __uint_as_float(r);
+}
+__device__ __forceinline__ int lds_ld(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// ------------------------------------------------------------------ preparation pass
+// Per token: dep, bit i set if token t+1+i (i < win) shares a slot with it; rst, bit r set
+// if read r stores G; wadd[j] and rc[r] (the coupling tables). An LDS hash of every slot of
+// the block's tokens and the win tokens after them (key: slot; info: token offset, kind,
+// position) answers each (token, position) by one probe sequence.
+struct PrepArgs {
+  const int32_t* widx;  // [U][T][W]
+  const int32_t* ridx;  // [U][T][R]
+  const float* rgt;     // [U][T][R]
+  uint32_t* dep;        // [U][T]
+  unsigned long long* rst;  // [U][T]
+  float* wadd;          // [U][T][W]
+  float* rc;            // [U][T][R]
+  int T, W, R, win, bits;
+  long long N;
+};
+
+__device__ __forceinline__ uint32_t prep_hash(uint32_t slot, int bits) { return (slot * 2654435761u) >> (32 - bits); }
+
+__global__ void __launch_bounds__(256) bwd_prep_kernel(PrepArgs A) {
+  extern __shared__ uint32_t psm[];
+  const int bits = A.bits;
+  const uint32_t hmask = (1u << bits) - 1;
+  uint32_t* keys = psm;                                    // 2^bits slots (kEmptyKey: free)
+  uint16_t* info = (uint16_t*)(psm + (1 << bits));         // offset << 7 | kind << 6 | position
+  uint32_t* depm = (uint32_t*)(info + (1 << bits));        // [kPrepBlk]
+  uint32_t* rstm = depm + kPrepBlk;                        // [2 kPrepBlk]
+  constexpr uint32_t kEmptyKey = 0xFFFFFFFFu;
+  const int u = blockIdx.y, t0 = blockIdx.x * kPrepBlk, T = A.T, W = A.W, R = A.R, per = W + R;
+  const int t_end = min(t0 + kPrepBlk, T), h_end = min(t_end + A.win, T);
+  for (int i = threadIdx.x; i < (1 << bits); i += 256) keys[i] = kEmptyKey;
+  for (int i = threadIdx.x; i < 3 * kPrepBlk; i += 256) depm[i] = 0u;
+  __syncthreads();
+  const int32_t* wi = A.widx + (size_t)u * T * W;
+  const int32_t* ri = A.ridx + (size_t)u * T * R;
+  const float* rg = A.rgt + (size_t)u * T * R;
+  for (int e = threadIdx.x; e < (h_end - t0) * per; e += 256) {
+    const int k = e / per, p = e - k * per;
+    const bool rd = p >= W;
+    const int q = rd ? p - W : p;
+    const int32_t slot = rd ? ri[(size_t)(t0 + k) * R + q] : wi[(size_t)(t0 + k) * W + q];
+    if (slot < 0 || slot >= A.N) continue;
+    uint32_t h = prep_hash((uint32_t)slot, bits);
+    while (atomicCAS(&keys[h], kEmptyKey, (uint32_t)slot) != kEmptyKey) h = (h + 1) & hmask;
+    info[h] = (uint16_t)((k << 7) | ((int)rd << 6) | q);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < (t_end - t0) * per; e += 256) {
+    const int k = e / per, p = e - k * per, t = t0 + k;
+    const bool rd = p >= W;
+    const int q = rd ? p - W : p;
+    const int32_t slot = rd ? ri[(size_t)t * R + q] : wi[(size_t)t * W + q];
+    float acc = 0.f;
+    bool dup = false, inw = false;
+    uint32_t dm = 0;
+    const bool valid = slot >= 0 && slot < A.N;
+    if (valid) {
+      uint32_t h = prep_hash((uint32_t)slot, bits);
+      while (true) {
+        const uint32_t key = keys[h];
+        if (key == kEmptyKey) break;
+        if (key == (uint32_t)slot) {
+          const int inf = info[h], d = (inf >> 7) - k, kind = (inf >> 6) & 1, qq = inf & 63;
+          if (d >= 1 && d <= A.win) dm |= 1u << (d - 1);
+          if (d == 0 && kind == 1) {  // a read of the same slot in this token
+            acc += rg[(size_t)t * R + qq];
+            dup = dup || (rd && qq < q);
+          }
+          if (d == 0 && kind == 0 && rd) inw = true;
+        }
+        h = (h + 1) & hmask;
+      }
+    }
+    if (dm) atomicOr(&depm[k], dm);
+    const size_t ut = (size_t)u * T + t;
+    if (!rd) {
+      A.wadd[ut * W + q] = acc;
+    } else {
+      const bool st = valid && !dup && !inw;
+      A.rc[ut * R + q] = st ? acc : 0.f;
+      if (st) atomicOr(&rstm[2 * k + (q >> 5)], 1u << (q & 31));
+    }
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < t_end - t0; k += 256) {
+    const size_t ut = (size_t)u * T + t0 + k;
+    A.dep[ut] = depm[k];
+    A.rst[ut] = (unsigned long long)rstm[2 * k] | ((unsigned long long)rstm[2 * k + 1] << 32);
+  }
+}
+
+// ------------------------------------------------------------------ reverse walk
 struct BwdArgs {
   const int32_t* widx;  // [U][T][W]
   const float* wgt;
   const int32_t* ridx;  // [U][T][R]
-  const float* rgt;
   const void* v;        // [U][T][d_v] in dtype
   const float* alpha;   // [U][T]
   const float* beta;
@@ -56,91 +189,262 @@ struct BwdArgs {
   float* dbeta;         // [U][T] (zeroed)
   float* dwgt;          // [U][T][W] (zeroed)
   float* drgt;          // [U][T][R] (zeroed)
-  int T, W, R, d_v, P;
+  const uint32_t* dep;  // preparation pass outputs
+  const unsigned long long* rst;
+  const float* wadd;
+  const float* rc;
+  unsigned long long* err;
+  int U, T, W, R, d_v, P, K;
   long long N;
 };
 
-template <typename MemT, typename InT>
-__global__ void __launch_bounds__(64) backward_kernel(BwdArgs A) {
-  __shared__ int sn[kMaxSel], sm[kMaxSel];
-  __shared__ float sa[kMaxSel], su[kMaxSel];
-  __shared__ float part[2 * kMaxSel + 2][kCols + 1];  // per-lane partial sums, padded rows
-  const int lane = threadIdx.x;
-  const int u = blockIdx.x / A.P, p = blockIdx.x % A.P;
-  const int c = p * kCols + lane;
+// Slot lists of one token and its coupling tables.
+template <int LIST>
+struct TokMeta {
+  int n[LIST], m[LIST];
+  float a[LIST], wadd[LIST], rc[LIST];
+  float al, be;
+  uint32_t dep, rlo, rhi, pad;
+};
+
+template <int NG>
+constexpr size_t wave_lds_bytes() {
+  constexpr int C = 64 / NG, LIST = MH * NG;
+  return 3 * sizeof(TokMeta<LIST>) + (size_t)2 * LIST * (C + 1) * 4;
+}
+constexpr size_t kCtrlBytes = (kFinRing + 16) * 4;
+
+template <typename MemT, typename InT, int NG>
+__global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
+  constexpr int C = 64 / NG;
+  constexpr int LIST = MH * NG;  // longest slot list handled; group h holds rows h*MH + i
+  using Meta = TokMeta<LIST>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* fin = (int*)smem;       // [kFinRing]: token that finished in each ring position
+  int* ctrl = fin + kFinRing;  // [0]: give-up flag
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, K = A.K;
+  Meta* meta = (Meta*)(smem + kCtrlBytes + wave * wave_lds_bytes<NG>());
+  // per-column partials of one token: write rows [0, LIST), read rows [LIST, 2 LIST)
+  float(*part)[C + 1] = (float(*)[C + 1])((unsigned char*)(meta + 3));
+  for (int i = threadIdx.x; i < kFinRing + 16; i += blockDim.x) fin[i] = -1;
+  if (threadIdx.x == 0) ctrl[0] = 0;
+  __syncthreads();
+  const int h = lane / C, cl = lane % C, hb = h * MH;
+  // blockIdx -> (unit, column block) with all column blocks of a unit in one L2 domain
+  const int xcd = blockIdx.x % kXcd, y = blockIdx.x / kXcd;
+  const int p = y % A.P, u = (y / A.P) * kXcd + xcd;
+  if (u >= A.U) return;
+  const int c = p * C + cl;
   const bool act = c < A.d_v;
+  const uint32_t cc = act ? c : 0;  // inactive lanes load column 0 and discard it
   const int T = A.T, W = A.W, R = A.R, d_v = A.d_v;
-  MemT* M = (MemT*)A.M + (size_t)u * A.N * d_v;
-  float* G = A.G + (size_t)u * A.N * d_v;
-  const MemT* xlog = (const MemT*)A.xlog + (size_t)u * T * W * d_v;
-  const InT* v = (const InT*)A.v + (size_t)u * T * d_v;
+  const long long N = A.N;
+  constexpr uint32_t ms = sizeof(MemT), is = sizeof(InT);
+  const rsrc_t rM = make_rs((const char*)A.M + (size_t)u * N * d_v * ms, (size_t)N * d_v * ms);
+  const rsrc_t rG = make_rs(A.G + (size_t)u * N * d_v, (size_t)N * d_v * 4);
+  const rsrc_t rX = make_rs((const char*)A.xlog + (size_t)u * T * W * d_v * ms, (size_t)T * W * d_v * ms);
+  const rsrc_t rV = make_rs((const char*)A.v + (size_t)u * T * d_v * is, (size_t)T * d_v * is);
+  const rsrc_t rO = make_rs(A.go + (size_t)u * T * d_v, (size_t)T * d_v * 4);
+  const rsrc_t rD = make_rs(A.dv + (size_t)u * T * d_v, (size_t)T * d_v * 4);
+  const uint32_t rowG = (uint32_t)d_v * 4, rowM = (uint32_t)d_v * ms;
   const size_t ut = (size_t)u * T;
-  float x[kMaxSel], dy[kMaxSel];
-  for (int t = T - 1; t >= 0; --t) {
-    if (lane < W) {
-      sn[lane] = A.widx[(ut + t) * W + lane];
-      sa[lane] = A.wgt[(ut + t) * W + lane];
-    }
-    if (lane < R) {
-      sm[lane] = A.ridx[(ut + t) * R + lane];
-      su[lane] = A.rgt[(ut + t) * R + lane];
-    }
-    __syncthreads();
-    const float al = A.alpha[ut + t], be = A.beta[ut + t];
-    const float g = act ? A.go[(ut + t) * d_v + c] : 0.f;
-    const float vc = act ? ld_val((const InT*)v, (size_t)t * d_v + c) : 0.f;
-    // read after the write (slots outside [0, N) carry no weight and are skipped)
-    for (int r = 0; r < R; ++r) {
-      const bool ok = sm[r] >= 0 && sm[r] < A.N;
-      const size_t e = ok ? (size_t)sm[r] * d_v + c : 0;
-      float pr = 0.f;
-      if (act && ok) {
-        pr = g * ld_val((const MemT*)M, e);
-        G[e] += su[r] * g;
-      }
-      part[W + r][lane] = pr;
-    }
-    // write: x_j from the log, dy_j the gradient of the written values
-    float s = 0.f, dd = 0.f;
+  auto group_sum = [](float x) {
 #pragma unroll
-    for (int j = 0; j < kMaxSel; ++j) {
-      if (j < W) {
-        const bool ok = act && sn[j] >= 0 && sn[j] < A.N;
-        x[j] = ok ? ld_val(xlog, ((size_t)t * W + j) * d_v + c) : 0.f;
-        dy[j] = ok ? G[(size_t)sn[j] * d_v + c] : 0.f;
-        s = fmaf(sa[j], x[j], s);
-        dd = fmaf(sa[j], dy[j], dd);
+    for (int m = C; m < 64; m *= 2) x += shfl_xor_f32(x, m);
+    return x;
+  };
+  auto column_sum = [](float x) {
+#pragma unroll
+    for (int m = 1; m < C; m *= 2) x += shfl_xor_f32(x, m);
+    return x;
+  };
+  auto sync = [] {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  };
+
+  // slot lists and tables of a token, lane-distributed, from global memory to LDS; list
+  // positions past W or R get slot -1 (no row)
+  int qn, qm;
+  float qa, qwd, qrc, qal, qbe;
+  uint32_t qdep;
+  unsigned long long qrst;
+  auto fetch = [&](int tt) {
+    const size_t bw = (ut + tt) * W, br = (ut + tt) * R;
+    const bool lw = lane < W, lr = lane < R;
+    qn = lw ? A.widx[bw + lane] : -1;
+    qa = lw ? A.wgt[bw + lane] : 0.f;
+    qwd = lw ? A.wadd[bw + lane] : 0.f;
+    qm = lr ? A.ridx[br + lane] : -1;
+    qrc = lr ? A.rc[br + lane] : 0.f;
+    qal = A.alpha[ut + tt];
+    qbe = A.beta[ut + tt];
+    qdep = A.dep[ut + tt];
+    qrst = A.rst[ut + tt];
+  };
+  auto put = [&](Meta& mt) {
+    if (lane < LIST) {
+      mt.n[lane] = qn;
+      mt.a[lane] = qa;
+      mt.wadd[lane] = qwd;
+      mt.m[lane] = qm;
+      mt.rc[lane] = qrc;
+    }
+    if (lane == 0) {
+      mt.al = qal;
+      mt.be = qbe;
+      mt.dep = qdep;
+      mt.rlo = (uint32_t)qrst;
+      mt.rhi = (uint32_t)(qrst >> 32);
+    }
+  };
+  // this group's row slots of a token (kNone: no such row, slot outside [0, N), or an
+  // inactive column); every load uses slot 0 in place of kNone, so it is in bounds
+  uint32_t rn[MH], rm[MH];
+  auto rows_of = [&](const Meta& mt) {
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      const uint32_t n = (uint32_t)mt.n[hb + i], m = (uint32_t)mt.m[hb + i];
+      rn[i] = act && n < N ? n : kNone;
+      rm[i] = act && m < N ? m : kNone;
+    }
+  };
+  // sums over this wave's columns of one token's row partials, added into the outputs
+  auto reduce = [&](int tt) {
+#pragma unroll
+    for (int k = 0; k < (2 * LIST + 63) / 64; ++k) {
+      const int i = lane + 64 * k;
+      const bool wr = i < W, rd = i >= LIST && i - LIST < R;
+      if (wr || rd) {
+        float sum = 0.f;
+#pragma unroll 8
+        for (int q = 0; q < C; ++q) sum += part[i][q];
+        atomicAdd(wr ? A.dwgt + (ut + tt) * W + i : A.drgt + (ut + tt) * R + (i - LIST), sum);
       }
     }
-    const float resid = vc - al * s, delta = be * resid, drho = -be * dd;
-    float pal = drho * s;
-#pragma unroll
-    for (int j = 0; j < kMaxSel; ++j) {
-      if (j < W) {
-        part[j][lane] = dy[j] * delta + al * drho * x[j];
-        pal = fmaf(dy[j], x[j], pal);
-        if (act && sn[j] >= 0 && sn[j] < A.N) {
-          const size_t e = (size_t)sn[j] * d_v + c;
-          G[e] = al * dy[j] + al * sa[j] * drho;
-          st_val(M, e, x[j]);
+  };
+  auto give_up = [&] {
+    if (lane == 0) {
+      lds_st(&ctrl[0], 1);
+      atomicAdd(A.err, 1ull);
+    }
+  };
+
+  int t = T - 1 - wave;
+  if (t < 0) return;
+  fetch(t);
+  put(meta[0]);
+  sync();
+  rows_of(meta[0]);
+  fetch(t >= K ? t - K : 0);
+  if (t >= K) put(meta[1]);
+  sync();
+
+  int b0 = 0;  // buffer of token t; t - K uses (b0 + 1) % 3, t - 2K (b0 + 2) % 3
+  long long budget = kSpinBudget;
+  int prev = -1;  // this wave's previous token, whose column sums are still due
+  for (; t >= 0; t -= K) {
+    Meta& mt = meta[b0];
+    Meta& m1 = meta[b0 == 2 ? 0 : b0 + 1];
+    Meta& m2 = meta[b0 == 0 ? 2 : b0 - 1];
+    // 1. the lists two own tokens ahead (independent of everything running)
+    fetch(t >= 2 * K ? t - 2 * K : 0);
+    // 2. wait for the later tokens this one depends on: those sharing a slot among the next
+    //    K - 1, and every token from t + K on
+    {
+      const uint32_t dm = mt.dep;
+      const int tau = t + 1 + lane;
+      const bool need = lane < 2 * K - 1 && tau < T && (lane >= K - 1 || ((dm >> lane) & 1u));
+      bool gave_up = false;
+      while (true) {
+        const bool pending = need && lds_ld(&fin[tau & (kFinRing - 1)]) != tau;
+        if (ballot(pending) == 0ull) break;
+        if (--budget <= 0) {
+          give_up();
+          gave_up = true;
+          break;
         }
+        if (lds_ld(&ctrl[0])) {
+          gave_up = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
+      if (gave_up) return;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     }
-    part[W + R][lane] = pal;
-    part[W + R + 1][lane] = dd * resid;
-    if (act) A.dv[(ut + t) * d_v + c] = be * dd;
-    __syncthreads();
-    // sums over this wave's columns: lane i adds row i, then one atomic per block
-    for (int i = lane; i < W + R + 2; i += kCols) {
-      float sum = 0.f;
-      for (int k = 0; k < kCols; ++k) sum += part[i][k];
-      float* dst = i < W ? A.dwgt + (ut + t) * W + i
-                         : i < W + R ? A.drgt + (ut + t) * R + (i - W)
-                                     : i == W + R ? A.dalpha + ut + t : A.dbeta + ut + t;
-      atomicAdd(dst, sum);
+    // 3. every row load of token t at once (a row past W reads a neighbouring log row, or
+    //    zeros past the end of the log, and is discarded)
+    uint32_t xr[MH], mrr[MH], gy[MH], gr[MH];
+    const uint32_t xo = ((uint32_t)t * W + hb) * rowM + cc * ms;
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      const uint32_t n = rn[i] != kNone ? rn[i] : 0u, m = rm[i] != kNone ? rm[i] : 0u;
+      xr[i] = bld<MemT>(rX, xo + i * rowM);
+      gy[i] = bld<float>(rG, n * rowG + cc * 4);
+      mrr[i] = bld<MemT>(rM, m * rowM + cc * ms);
+      gr[i] = bld<float>(rG, m * rowG + cc * 4);
     }
-    __syncthreads();
+    const uint32_t graw = bld<float>(rO, (uint32_t)t * rowG + cc * 4);
+    const uint32_t vraw = bld<InT>(rV, ((uint32_t)t * d_v + cc) * is);
+    // 4. while they are in flight: the previous token's column sums
+    const unsigned long long rstm = ((unsigned long long)mt.rlo | ((unsigned long long)mt.rhi << 32)) >> hb;
+    const float al = mt.al, be = mt.be;
+    if (prev >= 0) reduce(prev);
+    sync();
+    // 5. token t
+    const float g = act ? __uint_as_float(graw) : 0.f, vc = act ? cvt<InT>(vraw) : 0.f;
+    float s = 0.f, dd = 0.f;
+    float x[MH], dy[MH];
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      const bool wv = rn[i] != kNone;
+      const float aj = wv ? mt.a[hb + i] : 0.f;
+      x[i] = wv ? cvt<MemT>(xr[i]) : 0.f;
+      dy[i] = wv ? __uint_as_float(gy[i]) + mt.wadd[hb + i] * g : 0.f;
+      s = fmaf(aj, x[i], s);
+      dd = fmaf(aj, dy[i], dd);
+    }
+    s = group_sum(s);
+    dd = group_sum(dd);
+    const float resid = vc - al * s, delta = be * resid, drho = -be * dd;
+    float pal = 0.f;
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      part[hb + i][cl] = dy[i] * delta + al * drho * x[i];
+      pal = fmaf(dy[i], x[i], pal);
+      part[LIST + hb + i][cl] = rm[i] != kNone ? g * cvt<MemT>(mrr[i]) : 0.f;
+    }
+    // dalpha and dbeta: sums over rows (groups) and over this wave's columns
+    const float sal = column_sum(act ? group_sum(pal) + drho * s : 0.f);
+    const float sbe = column_sum(act ? dd * resid : 0.f);
+    if (lane == 0) {
+      atomicAdd(A.dalpha + ut + t, sal);
+      atomicAdd(A.dbeta + ut + t, sbe);
+    }
+    // the lists two own tokens ahead go to LDS (their loads were issued before this token's)
+    if (t >= 2 * K) put(m2);
+    // stores of token t: G and the undone rows of M; G of the reads that store it
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      if (rn[i] != kNone) {
+        bst<float>(rG, rn[i] * rowG + c * 4, al * (dy[i] + mt.a[hb + i] * drho));
+        bst<MemT>(rM, rn[i] * rowM + c * ms, x[i]);
+      }
+      if (rm[i] != kNone && ((rstm >> i) & 1ull))
+        bst<float>(rG, rm[i] * rowG + c * 4, __uint_as_float(gr[i]) + mt.rc[hb + i] * g);
+    }
+    if (h == 0 && act) bst<float>(rD, (uint32_t)t * rowG + c * 4, be * dd);
+    // 6. publish token t once its stores are complete
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) lds_st(&fin[t & (kFinRing - 1)], t);
+    sync();
+    if (t >= K) rows_of(m1);
+    prev = t;
+    b0 = b0 == 2 ? 0 : b0 + 1;
   }
+  reduce(prev);
 }
 
 __global__ void __launch_bounds__(256) zero_f32_kernel(float* p, size_t n) {
@@ -154,22 +458,77 @@ hipError_t zero_f32(float* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename MemT, typename InT>
-hipError_t launch_bwd(const BwdArgs& A, int U, hipStream_t st) {
-  hipLaunchKernelGGL((backward_kernel<MemT, InT>), dim3(U * A.P), dim3(64), 0, st, A);
+// Workspace of the backward: the error word first (offset 0, as every workspace of the
+// library), then the preparation pass outputs.
+struct BwdWs {
+  size_t err, dep, rst, wadd, rc, total;
+};
+size_t bws_align(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdWs bwd_layout(const sdm_shape& S) {
+  const size_t tok = (size_t)S.B * S.H * (size_t)S.T;
+  BwdWs L;
+  size_t o = 0;
+  L.err = o;
+  o = bws_align(o + 8);
+  L.dep = o;
+  o = bws_align(o + tok * 4);
+  L.rst = o;
+  o = bws_align(o + tok * 8);
+  L.wadd = o;
+  o = bws_align(o + tok * S.W * 4);
+  L.rc = o;
+  o = bws_align(o + tok * S.R * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename MemT, typename InT, int NG>
+hipError_t launch_cfg(BwdArgs A, const PrepArgs& Pa0, hipStream_t st) {
+  A.P = (A.d_v + 64 / NG - 1) / (64 / NG);
+  const long long wgs = (long long)((A.U + kXcd - 1) / kXcd) * kXcd * A.P;
+  // K waves per workgroup: 8, or 16 when fewer than two workgroups per CU would run
+  A.K = wgs >= 2ll * device_cus() ? 8 : kMaxWaves;
+  PrepArgs Pa = Pa0;
+  Pa.win = A.K - 1;
+  const int entries = (kPrepBlk + Pa.win) * (A.W + A.R);
+  Pa.bits = 6;
+  while ((1 << Pa.bits) < 2 * entries) ++Pa.bits;
+  const size_t plds = ((size_t)4 << Pa.bits) + ((size_t)2 << Pa.bits) + 3 * kPrepBlk * 4;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((A.T + kPrepBlk - 1) / kPrepBlk), (unsigned)A.U), dim3(256),
+                     plds, st, Pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = kCtrlBytes + (size_t)A.K * wave_lds_bytes<NG>();
+  hipLaunchKernelGGL((backward_kernel<MemT, InT, NG>), dim3((unsigned)wgs), dim3(64 * A.K), lds, st, A);
   return hipGetLastError();
+}
+
+// As many row groups as 8 rows per group need: 64 / NG columns per wave.
+template <typename MemT, typename InT>
+hipError_t launch_bwd(const BwdArgs& A, const PrepArgs& Pa, hipStream_t st) {
+  const int list = A.W > A.R ? A.W : A.R;
+  if (list <= MH) return launch_cfg<MemT, InT, 1>(A, Pa, st);
+  if (list <= 2 * MH) return launch_cfg<MemT, InT, 2>(A, Pa, st);
+  if (list <= 4 * MH) return launch_cfg<MemT, InT, 4>(A, Pa, st);
+  return launch_cfg<MemT, InT, 8>(A, Pa, st);
 }
 
 }  // namespace
 
+size_t backward_workspace_bytes(const sdm_shape& S) { return bwd_layout(S).total; }
+
 hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
                            const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
-                           float* dwgt, float* drgt, hipStream_t stream) {
+                           float* dwgt, float* drgt, void* ws, hipStream_t stream) {
   if (S.W > kMaxSel || S.R > kMaxSel) return hipErrorInvalidValue;
   const int U = S.B * S.H;
   const size_t tok = (size_t)U * S.T;
-  hipError_t e = zero_f32(dalpha, tok, stream);
+  const BwdWs L = bwd_layout(S);
+  char* w = (char*)ws;
+  hipError_t e = zero_f32((float*)(w + L.err), 2, stream);
+  if (e != hipSuccess) return e;
+  e = zero_f32(dalpha, tok, stream);
   if (e != hipSuccess) return e;
   e = zero_f32(dbeta, tok, stream);
   if (e != hipSuccess) return e;
@@ -177,11 +536,23 @@ hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float*
   if (e != hipSuccess) return e;
   e = zero_f32(drgt, tok * S.R, stream);
   if (e != hipSuccess) return e;
+  if (tok == 0) return hipSuccess;
+  PrepArgs Pa;
+  Pa.widx = widx;
+  Pa.ridx = ridx;
+  Pa.rgt = rgt;
+  Pa.dep = (uint32_t*)(w + L.dep);
+  Pa.rst = (unsigned long long*)(w + L.rst);
+  Pa.wadd = (float*)(w + L.wadd);
+  Pa.rc = (float*)(w + L.rc);
+  Pa.T = S.T;
+  Pa.W = S.W;
+  Pa.R = S.R;
+  Pa.N = S.N;
   BwdArgs A;
   A.widx = widx;
   A.wgt = wgt;
   A.ridx = ridx;
-  A.rgt = rgt;
   A.v = v;
   A.alpha = alpha;
   A.beta = beta;
@@ -194,17 +565,22 @@ hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float*
   A.dbeta = dbeta;
   A.dwgt = dwgt;
   A.drgt = drgt;
+  A.dep = Pa.dep;
+  A.rst = Pa.rst;
+  A.wadd = Pa.wadd;
+  A.rc = Pa.rc;
+  A.err = (unsigned long long*)(w + L.err);
+  A.U = U;
   A.T = S.T;
   A.W = S.W;
   A.R = S.R;
   A.d_v = S.d_v;
-  A.P = (S.d_v + kCols - 1) / kCols;
   A.N = S.N;
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
-  if (mb && ib) return launch_bwd<uint16_t, uint16_t>(A, U, stream);
-  if (mb && !ib) return launch_bwd<uint16_t, float>(A, U, stream);
-  if (!mb && ib) return launch_bwd<float, uint16_t>(A, U, stream);
-  return launch_bwd<float, float>(A, U, stream);
+  if (mb && ib) return launch_bwd<uint16_t, uint16_t>(A, Pa, stream);
+  if (mb && !ib) return launch_bwd<uint16_t, float>(A, Pa, stream);
+  if (!mb && ib) return launch_bwd<float, uint16_t>(A, Pa, stream);
+  return launch_bwd<float, float>(A, Pa, stream);
 }
 
 }  // namespace sdm

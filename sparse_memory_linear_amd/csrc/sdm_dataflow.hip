@@ -874,16 +874,6 @@ bool pipe_config(const sdm_shape& S, int cus, bool decay, PipeCfg* out) {
   return any;
 }
 
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  }
-  return cus;
-}
-
 template <typename MemT, typename InT, int RB, int LB>
 hipError_t pipe_launch_rb(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
   const int groups = (A.U + 7) / 8;
@@ -920,6 +910,16 @@ hipError_t pipe_launch(const PipeArgs& A, const PipeCfg& c, hipStream_t st) {
 }
 
 }  // namespace
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  }
+  return cus;
+}
 
 bool dataflow_supported(const sdm_shape& S, bool decay) {
   if (S.W % 4 || S.R % 4) return false;  // weight lists move in 16-byte pieces

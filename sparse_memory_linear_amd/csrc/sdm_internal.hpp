@@ -56,10 +56,12 @@ size_t dataflow_sched_words(const sdm_shape& S);
 hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                            void* ws, const WsLayout& L, const DecayState* dk, void* xlog, hipStream_t stream);
+int device_cus();  // compute units of the current device
+size_t backward_workspace_bytes(const sdm_shape& S);
 hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
                            const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
-                           float* dwgt, float* drgt, hipStream_t stream);
+                           float* dwgt, float* drgt, void* ws, hipStream_t stream);
 
 hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun, hipStream_t stream);
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,

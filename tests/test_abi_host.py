@@ -217,12 +217,18 @@ def test_backward_calls_validate(sdm, no_gpu):
     need = sdm.workspace_bytes(S)
     assert L.sdm_recurrent_log(sp, *p[:9], None, p[10], need, None) == -1            # no log buffer
     assert L.sdm_recurrent_log(sp, *p[:9], p[7] + 4096, p[10], need, None) == -1     # log inside the table
-    args = list(p[:16])
+    bneed = sdm.backward_workspace_bytes(S)
+    assert bneed > 0
+    args = list(p[:16]) + [p[16], bneed]
     args[10] = args[7] + 64                                                            # G overlaps M
     assert L.sdm_recurrent_backward(sp, *args, None) == -1
-    args = list(p[:16])
+    args = list(p[:16]) + [p[16], bneed]
     args[11] = args[9]                                                                 # dv overlaps go
     assert L.sdm_recurrent_backward(sp, *args, None) == -1
-    args = list(p[:16])
+    args = list(p[:16]) + [p[16], bneed]
     args[0] = None
     assert L.sdm_recurrent_backward(sp, *args, None) == -1
+    args = list(p[:16]) + [p[10] + 128, bneed]                                         # workspace inside G
+    assert L.sdm_recurrent_backward(sp, *args, None) == -1
+    args = list(p[:16]) + [p[16], bneed - 1]                                           # workspace too small
+    assert L.sdm_recurrent_backward(sp, *args, None) == -3

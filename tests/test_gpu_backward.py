@@ -1,7 +1,9 @@
 """Memory-efficient backward on the GPU against the oracle: the forward's log of pre-update
 write rows, the reverse walk's gradients (v, alpha, beta, write and read weights, M0) and the
 in-place undo that restores M0. The oracle runs its own forward and backward on the same
-inputs (slots and weights from the oracle's addressing)."""
+inputs (slots and weights from the oracle's addressing). The coupled case edits the read
+lists so that reads hit the token's own write slots, repeat a slot, or share a slot's low
+16 bits without being equal: the kernel's exact coupling path and its bitmap test."""
 import numpy as np
 import pytest
 
@@ -16,7 +18,24 @@ CASES = {
     "tiny_fp32": W_["tiny_fp32"],
     "small_T128": W_["small"].replace(B=1, H=2, T=128),
     "layer_8b_T100": W_["layer_8b_long"].replace(B=1, H=2, T=100),
+    "coupled_T96": W_["layer_8b_long"].replace(B=1, H=2, T=96),
 }
+
+
+def couple(wi, ri, N):
+    """Reads that hit their token's write slots (t % 3 == 0), repeat a read slot (1), or
+    collide with a write or read slot in the low 16 bits only (2). Returns a new ridx."""
+    ri = ri.copy()
+    for t in range(len(ri)):
+        if t % 3 == 0:
+            ri[t, 0:4] = wi[t, 5:9]
+        elif t % 3 == 1:
+            ri[t, 10] = ri[t, 3]
+            ri[t, 11] = ri[t, 3]
+        else:
+            ri[t, 7] = (wi[t, 2] + 65536) % N
+            ri[t, 8] = (ri[t, 9] + 131072) % N
+    return ri
 
 
 @pytest.fixture(scope="module")
@@ -52,6 +71,8 @@ def test_log_and_backward(sdm, name):
             M0 = SI.widen(inp["M0"][h], sh.mem_dtype)
             wi, ww, _ = O.address(k, sk[0], sk[1], sh.kappa, sh.W)
             ri, rw, _ = O.address(q, sk[0], sk[1], sh.kappa, sh.R)
+            if name.startswith("coupled"):
+                ri = couple(wi, ri, sh.N)
             ww, rw = ww.astype(np.float32), rw.astype(np.float32)
             widx[b, h], wgt[b, h], ridx[b, h], rgt[b, h] = wi, ww, ri, rw
             o, MT = O.recurrence(M0, wi, ww.astype(np.float64), ri, rw.astype(np.float64), v, al, be, sh.mem_dtype)
@@ -85,9 +106,11 @@ def test_log_and_backward(sdm, name):
     dbe = torch.empty_like(dal)
     dwg = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.float32, device="cuda")
     drg = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
+    bws = torch.empty(sdm.backward_workspace_bytes(S), dtype=torch.uint8, device="cuda")
     sdm.recurrent_backward(S, dW, aW, dR, aR, dev["v"], alpha, beta, M, xlog, to_dev(go, "f32"), G, dv, dal, dbe,
-                           dwg, drg)
+                           dwg, drg, bws)
     torch.cuda.synchronize()
+    assert sdm.workspace_error(bws) == 0, "a workgroup of the backward gave up waiting"
     assert torch.equal(M, M0_dev), "the undo did not restore M0 bit for bit"
     out = {"dv": dv, "dalpha": dal, "dbeta": dbe, "dwgt": dwg, "drgt": drg, "dM0": G}
     for (b, h), (_, _, _, g) in ref.items():

@@ -172,7 +172,7 @@ size_t sdm_backward_workspace_bytes(const sdm_shape* shape);
  *   go, dv [B,H,T,d_v] f32; dalpha, dbeta [B,H,T] f32; dwgt [B,H,T,W], drgt [B,H,T,R] f32
  * Other arguments as for sdm_recurrent; W, R <= 64; read slots may repeat and may equal the
  * token's write slots; a slot outside [0, N) touches nothing and gets zero gradients.
- * Per unit, N*d_v*4, T*d_v*4 and T*W*d_v*sizeof(mem) bytes must each stay below 2^32.
+ * Per unit, N*d_v*4, T*d_v*4 and T*W*d_v*sizeof(mem) bytes must each stay below 2^31 - 16.
  * ws: at least sdm_backward_workspace_bytes(shape) bytes, apart from every other buffer; its
  * error word counts workgroups that gave up waiting (about 3.6 s; the result is then
  * invalid). Floating-point sums over columns are added with atomics: the summation order of

@@ -319,9 +319,9 @@ sdm_status sdm_recurrent_backward(const sdm_shape* S, const int32_t* widx, const
   if (!ws || ws_bytes < backward_workspace_bytes(*S)) return SDM_ERR_WORKSPACE;
   if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
   const size_t U = (size_t)S->B * S->H;
-  // per-unit row traffic uses 32-bit byte offsets
-  if ((size_t)S->N * S->d_v * 4 > 0xFFFFFFFFull || (size_t)S->T * S->d_v * 4 > 0xFFFFFFFFull ||
-      (size_t)S->T * S->W * S->d_v * dtype_size(S->mem_dtype) > 0xFFFFFFFFull)
+  // per-unit row traffic uses byte offsets below 2^31, with a sentinel past every table
+  if ((size_t)S->N * S->d_v * 4 >= 0x7FFFFFF0ull || (size_t)S->T * S->d_v * 4 >= 0x7FFFFFF0ull ||
+      (size_t)S->T * S->W * S->d_v * dtype_size(S->mem_dtype) >= 0x7FFFFFF0ull)
     return SDM_ERR_INVALID_ARG;
   const size_t mb = U * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype), gb = U * (size_t)S->N * S->d_v * 4;
   const size_t lb = tensor_bytes(*S, (int64_t)S->W * S->d_v, dtype_size(S->mem_dtype));

@@ -41,7 +41,8 @@ namespace {
 
 constexpr int kMaxSel = 64;        // W, R <= 64
 constexpr int kXcd = 8;            // workgroups are dealt round-robin to this many L2 domains
-constexpr uint32_t kNone = ~0u;    // row slot of a row that touches nothing
+constexpr uint32_t kNone = 0x1FFFFFFCu;  // element index of a row that touches nothing: its
+                                         // byte offset (x 2 or 4) lies past every table
 constexpr int MH = 8;              // rows of each kind per row group
 constexpr int kMaxWaves = 16;      // waves per workgroup (K)
 constexpr int kFinRing = 128;      // finished-token ring (> 4 K: a token waits on at most
@@ -200,17 +201,18 @@ struct BwdArgs {
 
 // Slot lists of one token and its coupling tables.
 template <int LIST>
-struct TokMeta {
+struct alignas(16) TokMeta {
   int n[LIST], m[LIST];
   float a[LIST], wadd[LIST], rc[LIST];
   float al, be;
-  uint32_t dep, rlo, rhi, pad;
+  uint32_t dep, rlo, rhi;
 };
+static_assert(sizeof(TokMeta<8>) % 16 == 0 && sizeof(TokMeta<64>) % 16 == 0, "LDS layout keeps 16-byte rows");
 
 template <int NG>
 constexpr size_t wave_lds_bytes() {
   constexpr int C = 64 / NG, LIST = MH * NG;
-  return 3 * sizeof(TokMeta<LIST>) + (size_t)2 * LIST * (C + 1) * 4;
+  return (3 * sizeof(TokMeta<LIST>) + (size_t)2 * LIST * (C + 1) * 4 + 15) / 16 * 16;
 }
 constexpr size_t kCtrlBytes = (kFinRing + 16) * 4;
 
@@ -226,8 +228,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
   Meta* meta = (Meta*)(smem + kCtrlBytes + wave * wave_lds_bytes<NG>());
   // per-column partials of one token: write rows [0, LIST), read rows [LIST, 2 LIST)
   float(*part)[C + 1] = (float(*)[C + 1])((unsigned char*)(meta + 3));
-  for (int i = threadIdx.x; i < kFinRing + 16; i += blockDim.x) fin[i] = -1;
-  if (threadIdx.x == 0) ctrl[0] = 0;
+  for (int i = threadIdx.x; i < kFinRing; i += blockDim.x) fin[i] = -1;
+  if (threadIdx.x < 16) ctrl[threadIdx.x] = 0;
   __syncthreads();
   const int h = lane / C, cl = lane % C, hb = h * MH;
   // blockIdx -> (unit, column block) with all column blocks of a unit in one L2 domain
@@ -248,6 +250,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
   const rsrc_t rD = make_rs(A.dv + (size_t)u * T * d_v, (size_t)T * d_v * 4);
   const uint32_t rowG = (uint32_t)d_v * 4, rowM = (uint32_t)d_v * ms;
   const size_t ut = (size_t)u * T;
+  const rsrc_t rDW = make_rs(A.dwgt + ut * W, (size_t)T * W * 4);  // this unit's weight gradients
+  const rsrc_t rDR = make_rs(A.drgt + ut * R, (size_t)T * R * 4);
   auto group_sum = [](float x) {
 #pragma unroll
     for (int m = C; m < 64; m *= 2) x += shfl_xor_f32(x, m);
@@ -298,15 +302,18 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
       mt.rhi = (uint32_t)(qrst >> 32);
     }
   };
-  // this group's row slots of a token (kNone: no such row, slot outside [0, N), or an
-  // inactive column); every load uses slot 0 in place of kNone, so it is in bounds
+  // this group's rows of a token as element indices slot * d_v + c into the unit's table;
+  // kNone for no such row, a slot outside [0, N) or an inactive column. N * d_v < kNone
+  // (tables stay below 2^31 - 16 bytes per unit), so kNone times the element size lies past
+  // the end of the table's resource: a load of it returns zero and a store of it is dropped.
+  const uint32_t N32 = (uint32_t)N;
   uint32_t rn[MH], rm[MH];
   auto rows_of = [&](const Meta& mt) {
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      const uint32_t n = (uint32_t)mt.n[hb + i], m = (uint32_t)mt.m[hb + i];
-      rn[i] = act && n < N ? n : kNone;
-      rm[i] = act && m < N ? m : kNone;
+      const uint32_t n = (uint32_t)mt.n[hb + i], m = (uint32_t)mt.m[hb + i];  // hb + i < LIST
+      rn[i] = act && n < N32 ? n * (uint32_t)d_v + (uint32_t)c : kNone;
+      rm[i] = act && m < N32 ? m * (uint32_t)d_v + (uint32_t)c : kNone;
     }
   };
   // sums over this wave's columns of one token's row partials, added into the outputs
@@ -319,7 +326,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
         float sum = 0.f;
 #pragma unroll 8
         for (int q = 0; q < C; ++q) sum += part[i][q];
-        atomicAdd(wr ? A.dwgt + (ut + tt) * W + i : A.drgt + (ut + tt) * R + (i - LIST), sum);
+        const uint32_t off = wr ? ((uint32_t)tt * W + i) * 4 : ((uint32_t)tt * R + (i - LIST)) * 4;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, wr ? rDW : rDR, off, 0, 0);
       }
     }
   };
@@ -379,11 +387,10 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     const uint32_t xo = ((uint32_t)t * W + hb) * rowM + cc * ms;
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      const uint32_t n = rn[i] != kNone ? rn[i] : 0u, m = rm[i] != kNone ? rm[i] : 0u;
       xr[i] = bld<MemT>(rX, xo + i * rowM);
-      gy[i] = bld<float>(rG, n * rowG + cc * 4);
-      mrr[i] = bld<MemT>(rM, m * rowM + cc * ms);
-      gr[i] = bld<float>(rG, m * rowG + cc * 4);
+      gy[i] = bld<float>(rG, rn[i] * 4);
+      mrr[i] = bld<MemT>(rM, rm[i] * ms);
+      gr[i] = bld<float>(rG, rm[i] * 4);
     }
     const uint32_t graw = bld<float>(rO, (uint32_t)t * rowG + cc * 4);
     const uint32_t vraw = bld<InT>(rV, ((uint32_t)t * d_v + cc) * is);
@@ -391,19 +398,25 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     const unsigned long long rstm = ((unsigned long long)mt.rlo | ((unsigned long long)mt.rhi << 32)) >> hb;
     const float al = mt.al, be = mt.be;
     if (prev >= 0) reduce(prev);
+    // the lists two own tokens ahead go to LDS (their loads were issued before this token's
+    // row loads, so waiting for them does not wait for the rows)
+    if (t >= 2 * K) put(m2);
     sync();
-    // 5. token t
+    // 5. token t (rows without a slot loaded zeros: dy = 0 there since wadd = 0)
     const float g = act ? __uint_as_float(graw) : 0.f, vc = act ? cvt<InT>(vraw) : 0.f;
+    float aj[MH], wd[MH];
+    *(float4*)&aj[0] = *(const float4*)&mt.a[hb];
+    *(float4*)&aj[4] = *(const float4*)&mt.a[hb + 4];
+    *(float4*)&wd[0] = *(const float4*)&mt.wadd[hb];
+    *(float4*)&wd[4] = *(const float4*)&mt.wadd[hb + 4];
     float s = 0.f, dd = 0.f;
     float x[MH], dy[MH];
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      const bool wv = rn[i] != kNone;
-      const float aj = wv ? mt.a[hb + i] : 0.f;
-      x[i] = wv ? cvt<MemT>(xr[i]) : 0.f;
-      dy[i] = wv ? __uint_as_float(gy[i]) + mt.wadd[hb + i] * g : 0.f;
-      s = fmaf(aj, x[i], s);
-      dd = fmaf(aj, dy[i], dd);
+      x[i] = rn[i] != kNone ? cvt<MemT>(xr[i]) : 0.f;
+      dy[i] = __uint_as_float(gy[i]) + wd[i] * g;
+      s = fmaf(aj[i], x[i], s);
+      dd = fmaf(aj[i], dy[i], dd);
     }
     s = group_sum(s);
     dd = group_sum(dd);
@@ -413,7 +426,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     for (int i = 0; i < MH; ++i) {
       part[hb + i][cl] = dy[i] * delta + al * drho * x[i];
       pal = fmaf(dy[i], x[i], pal);
-      part[LIST + hb + i][cl] = rm[i] != kNone ? g * cvt<MemT>(mrr[i]) : 0.f;
+      part[LIST + hb + i][cl] = g * cvt<MemT>(mrr[i]);
     }
     // dalpha and dbeta: sums over rows (groups) and over this wave's columns
     const float sal = column_sum(act ? group_sum(pal) + drho * s : 0.f);
@@ -422,17 +435,17 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
       atomicAdd(A.dalpha + ut + t, sal);
       atomicAdd(A.dbeta + ut + t, sbe);
     }
-    // the lists two own tokens ahead go to LDS (their loads were issued before this token's)
-    if (t >= 2 * K) put(m2);
-    // stores of token t: G and the undone rows of M; G of the reads that store it
+    // stores of token t (dropped for rows without a slot): G and the undone rows of M; G of
+    // the reads that store it
+    float rcv[MH];
+    *(float4*)&rcv[0] = *(const float4*)&mt.rc[hb];
+    *(float4*)&rcv[4] = *(const float4*)&mt.rc[hb + 4];
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      if (rn[i] != kNone) {
-        bst<float>(rG, rn[i] * rowG + c * 4, al * (dy[i] + mt.a[hb + i] * drho));
-        bst<MemT>(rM, rn[i] * rowM + c * ms, x[i]);
-      }
-      if (rm[i] != kNone && ((rstm >> i) & 1ull))
-        bst<float>(rG, rm[i] * rowG + c * 4, __uint_as_float(gr[i]) + mt.rc[hb + i] * g);
+      bst<float>(rG, rn[i] * 4, al * (dy[i] + aj[i] * drho));
+      bst<MemT>(rM, rn[i] * ms, x[i]);
+      const uint32_t rs = (rstm >> i) & 1ull ? rm[i] : kNone;
+      bst<float>(rG, rs * 4, __uint_as_float(gr[i]) + rcv[i] * g);
     }
     if (h == 0 && act) bst<float>(rD, (uint32_t)t * rowG + c * 4, be * dd);
     // 6. publish token t once its stores are complete

@@ -118,3 +118,59 @@ def test_log_and_backward(sdm, name):
         log(f"[backward] {name} grads ({b},{h}): " + " ".join(f"{k} {e:.1e}" for k, e in errs.items()) + f" (tol {tol})")
         for k, e in errs.items():
             assert e < tol, k
+
+
+@pytest.mark.parametrize("name", ["coupled_T96", "layer_8b_T100"])
+def test_backward_repeatable(sdm, name):
+    """Every run restores M0 bit for bit and gives the same G and dv bit for bit (no atomics
+    there); the sums over columns added with atomics agree to rounding. Covers the start-up
+    of the workgroups' control words and the completion ring."""
+    import torch
+    sh = CASES[name]
+    log(f"[backward] repeat {name}")
+    inp = SI.make_inputs(sh)
+    S = lib_shape(sh)
+    shp_w, shp_r = (sh.B, sh.H, sh.T, sh.W), (sh.B, sh.H, sh.T, sh.R)
+    widx, wgt = np.zeros(shp_w, np.int32), np.zeros(shp_w, np.float32)
+    ridx, rgt = np.zeros(shp_r, np.int32), np.zeros(shp_r, np.float32)
+    for b in range(sh.B):
+        for h in range(sh.H):
+            sk = SI.widen(inp["subkeys"][h], sh.in_dtype)
+            wi, ww, _ = O.address(SI.widen(inp["k"][b, h], sh.in_dtype), sk[0], sk[1], sh.kappa, sh.W)
+            ri, rw, _ = O.address(SI.widen(inp["q"][b, h], sh.in_dtype), sk[0], sk[1], sh.kappa, sh.R)
+            if name.startswith("coupled"):
+                ri = couple(wi, ri, sh.N)
+            widx[b, h], wgt[b, h], ridx[b, h], rgt[b, h] = wi, ww, ri, rw
+    v = to_dev(inp["v"], sh.in_dtype)
+    alpha, beta = to_dev(inp["alpha"], "f32"), to_dev(inp["beta"], "f32")
+    dW, dR, aW, aR = to_dev(widx, "i32"), to_dev(ridx, "i32"), to_dev(wgt, "f32"), to_dev(rgt, "f32")
+    M0 = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, to_dev(inp["M0"], sh.mem_dtype), M0)
+    ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(sdm.backward_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(23)
+    go = to_dev(rng.standard_normal((sh.B, sh.H, sh.T, sh.d_v)).astype(np.float32), "f32")
+    first = None
+    for it in range(4):
+        M = M0.clone()
+        o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+        xlog = empty_mem((sh.B, sh.H, sh.T, sh.W, sh.d_v), sh.mem_dtype)
+        sdm.recurrent_log(S, dW, aW, dR, aR, v, alpha, beta, M, o, xlog, ws)
+        G = torch.zeros((sh.B, sh.H, sh.N, sh.d_v), dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(go)
+        dal = torch.empty((sh.B, sh.H, sh.T), dtype=torch.float32, device="cuda")
+        dbe = torch.empty_like(dal)
+        dwg = torch.empty(shp_w, dtype=torch.float32, device="cuda")
+        drg = torch.empty(shp_r, dtype=torch.float32, device="cuda")
+        sdm.recurrent_backward(S, dW, aW, dR, aR, v, alpha, beta, M, xlog, go, G, dv, dal, dbe, dwg, drg, bws)
+        torch.cuda.synchronize()
+        assert sdm.workspace_error(bws) == 0
+        assert torch.equal(M, M0), f"run {it}: the undo did not restore M0"
+        out = (G, dv, dal, dbe, dwg, drg)
+        if first is None:
+            first = out
+            continue
+        assert torch.equal(G, first[0]) and torch.equal(dv, first[1]), f"run {it}: G or dv changed"
+        for a, b in zip(out[2:], first[2:]):
+            assert rel_err(a.cpu().numpy(), b.cpu().numpy()) < 1e-5, f"run {it}: an atomic sum changed"
+        log(f"[backward] repeat {name} run {it}: identical")

@@ -363,3 +363,34 @@ def recurrence_backward(MT, xlog, widx, wgt, ridx, rgt, v, alpha, beta, go, dMT=
         M[n] = x
     return {"dv": dv, "dalpha": dal, "dbeta": dbe, "dwgt": dw, "drgt": du, "dM0": G, "M0": M}
 
+
+
+def address_backward(x, C1, C2, idx, weight, dweight):
+    """Gradients of L = sum <dweight, weight> through the addressing of x with the selected
+    slots held fixed (the selection itself carries no gradient): the weights are the softmax
+    of the selected scores (PL §4 "SDM Configuration"; READING R6) and slot n = i*s + j
+    scores x[:h].C1[i] + x[h:].C2[j] (PL §2 "Product Key Memory"; READING R5).
+
+      dscore_k = weight_k (dweight_k - sum_l weight_l dweight_l)     (softmax Jacobian)
+      dx[:h]   = sum_k dscore_k C1[i_k];   dx[h:] = sum_k dscore_k C2[j_k]
+      dC1[i]  += dscore_k x[:h] for every k with i_k = i;  dC2[j] likewise with x[h:]
+
+    x [T, d_k]; C1, C2 [s, h]; idx, weight, dweight [T, n_sel].
+    Returns dx [T, d_k], dC1 [s, h], dC2 [s, h] (float64)."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    C1 = np.asarray(C1, dtype=np.float64)
+    C2 = np.asarray(C2, dtype=np.float64)
+    s, h = C1.shape
+    idx = np.atleast_2d(np.asarray(idx, dtype=np.int64))
+    w = np.atleast_2d(np.asarray(weight, dtype=np.float64))
+    dw = np.atleast_2d(np.asarray(dweight, dtype=np.float64))
+    dsc = w * (dw - np.sum(w * dw, axis=-1, keepdims=True))
+    i1, i2 = idx // s, idx % s
+    dx = np.zeros_like(x)
+    dx[:, :h] = np.einsum("tk,tkc->tc", dsc, C1[i1])
+    dx[:, h:] = np.einsum("tk,tkc->tc", dsc, C2[i2])
+    dC1 = np.zeros_like(C1)
+    dC2 = np.zeros_like(C2)
+    np.add.at(dC1, i1.ravel(), (dsc[:, :, None] * x[:, None, :h]).reshape(-1, h))
+    np.add.at(dC2, i2.ravel(), (dsc[:, :, None] * x[:, None, h:]).reshape(-1, h))
+    return dx, dC1, dC2

@@ -494,6 +494,39 @@ def pin_backward_finite_differences(O):
         assert np.allclose(g[name], num, rtol=1e-6, atol=1e-7), name
 
 
+def pin_address_backward_finite_differences(O):
+    """The addressing's gradients with the selection held fixed equal central finite
+    differences of the forward oracle's own addressing (its softmax weights at unchanged
+    slots) for the input rows and both sub-key sets; several selected slots share a sub-key
+    of a half (the kappa x kappa staircase), so the scatter-add into the sub-key gradients
+    is exercised."""
+    rng = np.random.default_rng(43)
+    s, h, T, kappa, n_sel = 6, 3, 5, 3, 4
+    C1, C2 = rng.standard_normal((s, h)), rng.standard_normal((s, h))
+    x = rng.standard_normal((T, 2 * h))
+    idx, w, _ = O.address(x, C1, C2, kappa, n_sel)
+    assert len(np.unique(idx // s)) < idx.size  # shared first-half sub-keys
+    dw = rng.standard_normal(w.shape)
+    dx, dC1, dC2 = O.address_backward(x, C1, C2, idx, w, dw)
+
+    def loss(x_, C1_, C2_):
+        i, ww, _ = O.address(x_, C1_, C2_, kappa, n_sel)
+        assert np.array_equal(i, idx), "a perturbation changed the selection"
+        return float(np.sum(dw * ww))
+
+    args = [x, C1, C2]
+    hstep = 1e-6
+    for k, g in enumerate([dx, dC1, dC2]):
+        num = np.zeros_like(args[k])
+        for ii in np.ndindex(args[k].shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[k][ii] += hstep
+            minus[k][ii] -= hstep
+            num[ii] = (loss(*plus) - loss(*minus)) / (2 * hstep)
+        assert np.allclose(g, num, rtol=1e-6, atol=1e-8), ["dx", "dC1", "dC2"][k]
+
+
 ALL_PINS = [
     pin_round_bf16,
     pin_pk_equals_brute_force,
@@ -516,4 +549,5 @@ ALL_PINS = [
     pin_output_gate,
     pin_head_mix,
     pin_backward_finite_differences,
+    pin_address_backward_finite_differences,
 ]

@@ -71,6 +71,12 @@ MUTANTS = {
     "bwd_dw_no_alpha": ("dw[t] += alpha[t] * (x @ drho)", "dw[t] += (x @ drho)"),
     # backward: the table's gradient accumulated instead of replaced at the written rows
     "bwd_g_accumulate": ("        G[n] = dx\n", "        G[n] += dx\n"),
+    # addressing backward: the softmax Jacobian without its centring term
+    "abwd_no_centring": ("dsc = w * (dw - np.sum(w * dw, axis=-1, keepdims=True))", "dsc = w * dw"),
+    # addressing backward: the second half's gradient taken from the first sub-key set
+    "abwd_wrong_codebook": ('dx[:, h:] = np.einsum("tk,tkc->tc", dsc, C2[i2])', 'dx[:, h:] = np.einsum("tk,tkc->tc", dsc, C1[i2])'),
+    # addressing backward: sub-key gradients scattered with the other half's index
+    "abwd_swapped_index": ("np.add.at(dC1, i1.ravel(),", "np.add.at(dC1, i2.ravel(),"),
     # per-half top-k keeps too few sub-keys
     "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
 }

@@ -182,6 +182,22 @@ sdm_status sdm_recurrent_backward(const sdm_shape* shape, const int32_t* widx, c
                                   const void* xlog, const float* go, float* G, float* dv, float* dalpha, float* dbeta,
                                   float* dwgt, float* drgt, void* ws, size_t ws_bytes, void* stream);
 
+/* Gradients through the addressing (PL §4 "SDM Configuration": softmax over the selected
+ * scores; PL §2 "Product Key Memory": slot n = i*s + j scores x[:h].C1[i] + x[h:].C2[j] with
+ * h = d_k/2, C1 = subkeys[h,0], C2 = subkeys[h,1]), the selected slots held fixed:
+ *   dscore_k = weight_k (dweight_k - sum_l weight_l dweight_l)
+ *   dx[:h] = sum_k dscore_k C1[i_k];  dx[h:] = sum_k dscore_k C2[j_k]
+ *   dsub[h,0,i] += sum over tokens and k with i_k = i of dscore_k x[:h]; dsub[h,1,j] likewise
+ *   x [B,H,T,d_k] in_dtype (k for the write slots, q for the read slots); subkeys as for
+ *   sdm_address; idx, weight [B,H,T,n_sel] as sdm_address returns them; dweight
+ *   [B,H,T,n_sel] f32 (dwgt or drgt of sdm_recurrent_backward); dx [B,H,T,d_k] f32 out;
+ *   dsub [H,2,s,d_k/2] f32 in/out: the sub-key gradient is added to it (zero it once, then
+ *   call for k and for q). A slot outside [0, N) adds nothing. Float32 sums; the order of
+ *   the additions into dsub can differ from run to run. */
+sdm_status sdm_address_backward(const sdm_shape* shape, const void* x, const void* subkeys, int32_t n_sel,
+                                const int32_t* idx, const float* weight, const float* dweight, float* dx,
+                                float* dsub, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * The steps on either side of the recurrence (PL App. B "Gate dynamics": forget gate
  * exp(g), input gate sigma(b); PL §4 "SDM Configuration": gate and time-step bias as in

@@ -302,6 +302,31 @@ sdm_status sdm_recurrent_log(const sdm_shape* S, const int32_t* widx, const floa
   return recurrent_impl(S, widx, wgt, ridx, rgt, v, alpha, beta, M, nullptr, nullptr, o, ws, ws_bytes, stream, xlog);
 }
 
+sdm_status sdm_address_backward(const sdm_shape* S, const void* x, const void* subkeys, int32_t n_sel,
+                                const int32_t* idx, const float* weight, const float* dweight, float* dx,
+                                float* dsub, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (n_sel < 1 || (int64_t)n_sel > (int64_t)S->kappa * S->kappa) return SDM_ERR_INVALID_ARG;
+  if (n_sel > kMaxSel) return SDM_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, subkeys, idx, weight, dweight, dx, dsub};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SDM_ERR_INVALID_ARG;
+  const int64_t s = isqrt64(S->N);
+  const size_t xb = tensor_bytes(*S, S->d_k, dtype_size(S->in_dtype));
+  const size_t kb = (size_t)S->H * 2 * (size_t)s * (S->d_k / 2) * dtype_size(S->in_dtype);
+  const size_t ib = tensor_bytes(*S, n_sel, 4);
+  const size_t dxb = tensor_bytes(*S, S->d_k, 4), dsb = (size_t)S->H * 2 * (size_t)s * (S->d_k / 2) * 4;
+  const void* ins[] = {x, subkeys, idx, weight, dweight};
+  const size_t isz[] = {xb, kb, ib, ib, ib};
+  for (int j = 0; j < 5; ++j)
+    if (overlaps(dx, dxb, ins[j], isz[j]) || overlaps(dsub, dsb, ins[j], isz[j])) return SDM_ERR_INVALID_ARG;
+  if (overlaps(dx, dxb, dsub, dsb)) return SDM_ERR_INVALID_ARG;
+  if (S->T == 0) return SDM_OK;
+  return hip_status(launch_address_backward(*S, x, subkeys, n_sel, idx, weight, dweight, dx, dsub,
+                                            (hipStream_t)stream));
+}
+
 size_t sdm_backward_workspace_bytes(const sdm_shape* shape) {
   if (check_shape(shape, true) != SDM_OK) return 0;
   return backward_workspace_bytes(*shape);

@@ -460,6 +460,94 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
   reduce(prev);
 }
 
+// ------------------------------------------------------------------ addressing backward
+// Gradients of the selected slots' softmax weights (PL §4 "SDM Configuration") with respect
+// to the addressed rows x and the sub-keys (PL §2 "Product Key Memory": slot n = i*s + j
+// scores x[:h].C1[i] + x[h:].C2[j]), the selection held fixed:
+//   dscore_k = w_k (dw_k - sum_l w_l dw_l)
+//   dx[half] = sum_k dscore_k C_half[i_half(k)];   dC_half[i_half(k)] += dscore_k x[half]
+// A workgroup owns one head, one half, one slice of 64 sub-key columns and a chunk of that
+// head's tokens; its 16 waves take one token at a time (a lane per column), and the chunk's
+// sub-key gradient slice [s][64] is accumulated in LDS with conflict-free atomics (the 64
+// lanes of one add hit 64 consecutive words), then added to the output once.
+constexpr int kAbChunk = 4096;   // tokens per workgroup
+constexpr int kAbWaves = 16;
+
+struct AddrBwdArgs {
+  const void* x;        // [B][H][T][d_k]
+  const void* sub;      // [H][2][s][hd]
+  const int32_t* idx;   // [B][H][T][n_sel]
+  const float* w;
+  const float* dw;
+  float* dx;            // [B][H][T][d_k]
+  float* dsub;          // [H][2][s][hd], added to
+  int B, H, T, d_k, hd, s, n_sel, nslice;
+  long long N;
+};
+
+template <typename InT>
+__global__ void __launch_bounds__(kAbWaves * 64) addr_backward_kernel(AddrBwdArgs A) {
+  extern __shared__ float acc[];  // [s][64]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.z, hf = blockIdx.y / A.nslice, slice = blockIdx.y % A.nslice;
+  const int c = slice * 64 + lane;  // column within the half
+  const bool act = c < A.hd;
+  const int s = A.s, n_sel = A.n_sel, T = A.T, H = A.H, d_k = A.d_k;
+  for (int i = threadIdx.x; i < s * 64; i += blockDim.x) acc[i] = 0.f;
+  __syncthreads();
+  const InT* C = (const InT*)A.sub + ((size_t)h * 2 + hf) * s * A.hd;
+  const long long Th = (long long)A.B * T;
+  const long long t0 = (long long)blockIdx.x * kAbChunk;
+  const long long t1 = t0 + kAbChunk < Th ? t0 + kAbChunk : Th;
+  auto ld = [](const InT* p, size_t i) -> float {
+    if constexpr (sizeof(InT) == 2) return bf16_to_f32(p[i]);
+    else return p[i];
+  };
+  for (long long tt = t0 + wave; tt < t1; tt += kAbWaves) {
+    const long long b = tt / T, t = tt - b * T;
+    const size_t row = ((size_t)b * H + h) * T + t;  // token row of x, idx, w, dx
+    const bool lk = lane < n_sel;
+    const float wl = lk ? A.w[row * n_sel + lane] : 0.f;
+    const float dwl = lk ? A.dw[row * n_sel + lane] : 0.f;
+    const int il = lk ? A.idx[row * n_sel + lane] : -1;
+    const float S = wave_sum_f32(wl * dwl);
+    const float dsc = wl * (dwl - S);
+    // this half's sub-key of each selected slot; -1 for a slot outside [0, N)
+    const int ii = il >= 0 && il < A.N ? (hf == 0 ? il / s : il % s) : -1;
+    const int cc = act ? c : 0;  // inactive lanes read column 0, add zeros, store nothing
+    const float xv = act ? ld((const InT*)A.x, row * d_k + hf * A.hd + c) : 0.f;
+    float dxv = 0.f;
+    // eight selected slots at a time, every load unguarded (a slot outside [0, N) reads
+    // row 0 with coefficient 0), so that eight row loads are in flight together
+    for (int k0 = 0; k0 < n_sel; k0 += 8) {
+      int rk[8];
+      float dk[8], cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = min(k0 + u, 63);
+        const int ik = k0 + u < n_sel ? __builtin_amdgcn_readlane(ii, k) : -1;
+        const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dsc), k));
+        rk[u] = ik >= 0 ? ik : 0;
+        dk[u] = ik >= 0 ? d : 0.f;
+        cv[u] = ld(C, (size_t)rk[u] * A.hd + cc);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        dxv = fmaf(dk[u], cv[u], dxv);
+        atomicAdd(&acc[rk[u] * 64 + lane], dk[u] * xv);
+      }
+    }
+    if (act) A.dx[row * d_k + hf * A.hd + c] = dxv;
+  }
+  __syncthreads();
+  float* out = A.dsub + ((size_t)h * 2 + hf) * s * A.hd;
+  for (int i = threadIdx.x; i < s * 64; i += blockDim.x) {
+    const int r = i >> 6, cc = slice * 64 + (i & 63);
+    const float v = acc[i];
+    if (cc < A.hd && v != 0.f) atomicAdd(&out[(size_t)r * A.hd + cc], v);
+  }
+}
+
 __global__ void __launch_bounds__(256) zero_f32_kernel(float* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -594,6 +682,37 @@ hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float*
   if (mb && !ib) return launch_bwd<uint16_t, float>(A, Pa, stream);
   if (!mb && ib) return launch_bwd<float, uint16_t>(A, Pa, stream);
   return launch_bwd<float, float>(A, Pa, stream);
+}
+
+hipError_t launch_address_backward(const sdm_shape& S, const void* x, const void* subkeys, int n_sel,
+                                   const int32_t* idx, const float* w, const float* dw, float* dx, float* dsub,
+                                   hipStream_t stream) {
+  AddrBwdArgs A;
+  A.x = x;
+  A.sub = subkeys;
+  A.idx = idx;
+  A.w = w;
+  A.dw = dw;
+  A.dx = dx;
+  A.dsub = dsub;
+  A.B = S.B;
+  A.H = S.H;
+  A.T = S.T;
+  A.d_k = S.d_k;
+  A.hd = S.d_k / 2;
+  A.s = (int)isqrt64(S.N);
+  A.n_sel = n_sel;
+  A.nslice = (A.hd + 63) / 64;
+  A.N = S.N;
+  const long long Th = (long long)S.B * S.T;
+  if (Th == 0) return hipSuccess;
+  const dim3 grid((unsigned)((Th + kAbChunk - 1) / kAbChunk), (unsigned)(2 * A.nslice), (unsigned)S.H);
+  const size_t lds = (size_t)A.s * 64 * 4;
+  if (S.in_dtype == SDM_BF16)
+    hipLaunchKernelGGL(addr_backward_kernel<uint16_t>, grid, dim3(kAbWaves * 64), lds, stream, A);
+  else
+    hipLaunchKernelGGL(addr_backward_kernel<float>, grid, dim3(kAbWaves * 64), lds, stream, A);
+  return hipGetLastError();
 }
 
 }  // namespace sdm

@@ -232,3 +232,32 @@ def test_backward_calls_validate(sdm, no_gpu):
     assert L.sdm_recurrent_backward(sp, *args, None) == -1
     args = list(p[:16]) + [p[16], bneed - 1]                                           # workspace too small
     assert L.sdm_recurrent_backward(sp, *args, None) == -3
+
+
+def test_address_backward_validates(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    p = [FAKE + i * (1 << 36) for i in range(10)]
+    ok = [p[0], p[1], 16, p[2], p[3], p[4], p[5], p[6]]
+    args = list(ok)
+    args[2] = 0                                                # no slots
+    assert L.sdm_address_backward(sp, *args, None) == -1
+    args = list(ok)
+    args[2] = 17 * 17                                          # more than kappa^2
+    assert L.sdm_address_backward(sp, *args, None) == -1
+    args = list(ok)
+    args[6] = p[0] + 64                                        # dx inside x
+    assert L.sdm_address_backward(sp, *args, None) == -1
+    args = list(ok)
+    args[7] = p[1] + 32                                        # dsub inside the sub-keys
+    assert L.sdm_address_backward(sp, *args, None) == -1
+    args = list(ok)
+    args[7] = args[6] + 16                                     # dsub inside dx
+    assert L.sdm_address_backward(sp, *args, None) == -1
+    args = list(ok)
+    args[3] = None
+    assert L.sdm_address_backward(sp, *args, None) == -1
+    Z = base(T=0)
+    assert L.sdm_address_backward(ctypes.byref(Z), *ok, None) == 0   # nothing to do
+

@@ -118,6 +118,29 @@ def test_log_and_backward(sdm, name):
         log(f"[backward] {name} grads ({b},{h}): " + " ".join(f"{k} {e:.1e}" for k, e in errs.items()) + f" (tol {tol})")
         for k, e in errs.items():
             assert e < tol, k
+    # the chain continues through the addressing: dk from dwgt, dq from drgt, both into the
+    # sub-key gradient; the oracle does the same with its own weight gradients
+    s = int(round(sh.N ** 0.5))
+    dsub = torch.zeros((sh.H, 2, s, sh.d_k // 2), dtype=torch.float32, device="cuda")
+    ref_dsub = np.zeros((sh.H, 2, s, sh.d_k // 2))
+    sub = to_dev(inp["subkeys"], sh.in_dtype)
+    for xname, n_sel, didx, dwt, dgrad, key, hidx, hwt in (("k", sh.W, dW, aW, dwg, "dwgt", widx, wgt),
+                                                           ("q", sh.R, dR, aR, drg, "drgt", ridx, rgt)):
+        dx = torch.empty((sh.B, sh.H, sh.T, sh.d_k), dtype=torch.float32, device="cuda")
+        sdm.address_backward(S, to_dev(inp[xname], sh.in_dtype), sub, n_sel, didx, dwt, dgrad, dx, dsub)
+        torch.cuda.synchronize()
+        for (b, h), (_, _, _, g) in ref.items():
+            sk = SI.widen(inp["subkeys"][h], sh.in_dtype)
+            rdx, dC1, dC2 = O.address_backward(SI.widen(inp[xname][b, h], sh.in_dtype), sk[0], sk[1], hidx[b, h],
+                                               hwt[b, h].astype(np.float64), g[key])
+            ref_dsub[h, 0] += dC1
+            ref_dsub[h, 1] += dC2
+            e = rel_err(dx[b, h].cpu().numpy(), rdx)
+            log(f"[backward] {name} d{xname} ({b},{h}): {e:.1e}")
+            assert e < tol, f"d{xname}"
+    e = rel_err(dsub.cpu().numpy(), ref_dsub)
+    log(f"[backward] {name} dsubkeys: {e:.1e}")
+    assert e < tol
 
 
 @pytest.mark.parametrize("name", ["coupled_T96", "layer_8b_T100"])

@@ -465,13 +465,21 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
 // to the addressed rows x and the sub-keys (PL §2 "Product Key Memory": slot n = i*s + j
 // scores x[:h].C1[i] + x[h:].C2[j]), the selection held fixed:
 //   dscore_k = w_k (dw_k - sum_l w_l dw_l)
-//   dx[half] = sum_k dscore_k C_half[i_half(k)];   dC_half[i_half(k)] += dscore_k x[half]
-// A workgroup owns one head, one half, one slice of 64 sub-key columns and a chunk of that
-// head's tokens; its 16 waves take one token at a time (a lane per column), and the chunk's
-// sub-key gradient slice [s][64] is accumulated in LDS with conflict-free atomics (the 64
-// lanes of one add hit 64 consecutive words), then added to the output once.
+//   dx[half] = sum_k dscore_k C_half[i_half(k)];   dC_half = D^T X_half
+// with D [tokens][s] holding each token's score gradients at its sub-keys of that half. A
+// workgroup owns one head, one half, one slice of 64 sub-key columns and a chunk of that
+// head's tokens. In steps of 32 tokens its 16 waves take two tokens each: the score
+// gradients (one wave reduction), dx by gathering the selected sub-key rows eight at a
+// time, and the token's row of D (one LDS atomic per selected slot, so equal sub-keys of
+// one token add up) and of X. Then each wave adds D[:, its 32 sub-keys]^T X to its 32x64
+// block of the sub-key gradient on the float32 MFMA (v_mfma_f32_32x32x2f32, K = 32 tokens
+// in steps of 2; any split of K works as long as both operands use the same one), and the
+// block is added to the output once at the end.
 constexpr int kAbChunk = 4096;   // tokens per workgroup
 constexpr int kAbWaves = 16;
+constexpr int kAbStep = 32;      // tokens per MFMA step (two per wave)
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct AddrBwdArgs {
   const void* x;        // [B][H][T][d_k]
@@ -487,14 +495,16 @@ struct AddrBwdArgs {
 
 template <typename InT>
 __global__ void __launch_bounds__(kAbWaves * 64) addr_backward_kernel(AddrBwdArgs A) {
-  extern __shared__ float acc[];  // [s][64]
+  extern __shared__ float sm[];
+  const int s = A.s, n_sel = A.n_sel, T = A.T, H = A.H, d_k = A.d_k;
+  float* Dm = sm;                      // [kAbStep][s]: score gradients by sub-key
+  float* Xm = sm + kAbStep * s;        // [kAbStep][64]: this slice of x's half
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.z, hf = blockIdx.y / A.nslice, slice = blockIdx.y % A.nslice;
   const int c = slice * 64 + lane;  // column within the half
   const bool act = c < A.hd;
-  const int s = A.s, n_sel = A.n_sel, T = A.T, H = A.H, d_k = A.d_k;
-  for (int i = threadIdx.x; i < s * 64; i += blockDim.x) acc[i] = 0.f;
-  __syncthreads();
+  const int cc = act ? c : 0;       // inactive lanes read column 0, add zeros, store nothing
+  for (int i = threadIdx.x; i < kAbStep * s; i += blockDim.x) Dm[i] = 0.f;
   const InT* C = (const InT*)A.sub + ((size_t)h * 2 + hf) * s * A.hd;
   const long long Th = (long long)A.B * T;
   const long long t0 = (long long)blockIdx.x * kAbChunk;
@@ -503,48 +513,77 @@ __global__ void __launch_bounds__(kAbWaves * 64) addr_backward_kernel(AddrBwdArg
     if constexpr (sizeof(InT) == 2) return bf16_to_f32(p[i]);
     else return p[i];
   };
-  for (long long tt = t0 + wave; tt < t1; tt += kAbWaves) {
-    const long long b = tt / T, t = tt - b * T;
-    const size_t row = ((size_t)b * H + h) * T + t;  // token row of x, idx, w, dx
-    const bool lk = lane < n_sel;
-    const float wl = lk ? A.w[row * n_sel + lane] : 0.f;
-    const float dwl = lk ? A.dw[row * n_sel + lane] : 0.f;
-    const int il = lk ? A.idx[row * n_sel + lane] : -1;
-    const float S = wave_sum_f32(wl * dwl);
-    const float dsc = wl * (dwl - S);
-    // this half's sub-key of each selected slot; -1 for a slot outside [0, N)
-    const int ii = il >= 0 && il < A.N ? (hf == 0 ? il / s : il % s) : -1;
-    const int cc = act ? c : 0;  // inactive lanes read column 0, add zeros, store nothing
-    const float xv = act ? ld((const InT*)A.x, row * d_k + hf * A.hd + c) : 0.f;
-    float dxv = 0.f;
-    // eight selected slots at a time, every load unguarded (a slot outside [0, N) reads
-    // row 0 with coefficient 0), so that eight row loads are in flight together
-    for (int k0 = 0; k0 < n_sel; k0 += 8) {
-      int rk[8];
-      float dk[8], cv[8];
+  const int r0 = wave * 32;  // this wave's block of sub-keys
+  f32x16_t acc0 = {}, acc1 = {};
+  __syncthreads();
+  for (long long c0 = t0; c0 < t1; c0 += kAbStep) {
+    int mine[2];  // D entry this lane wrote for each of its tokens (-1: none)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = min(k0 + u, 63);
-        const int ik = k0 + u < n_sel ? __builtin_amdgcn_readlane(ii, k) : -1;
-        const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dsc), k));
-        rk[u] = ik >= 0 ? ik : 0;
-        dk[u] = ik >= 0 ? d : 0.f;
-        cv[u] = ld(C, (size_t)rk[u] * A.hd + cc);
+    for (int q = 0; q < 2; ++q) {
+      const int tl = wave * 2 + q;
+      const long long tt = c0 + tl;
+      const bool live = tt < t1;
+      const long long b = tt / T, t = tt - b * T;
+      const size_t row = live ? ((size_t)b * H + h) * T + t : 0;  // token row of x, idx, w, dx
+      const bool lk = live && lane < n_sel;
+      const float wl = lk ? A.w[row * n_sel + lane] : 0.f;
+      const float dwl = lk ? A.dw[row * n_sel + lane] : 0.f;
+      const int il = lk ? A.idx[row * n_sel + lane] : -1;
+      const float S = wave_sum_f32(wl * dwl);
+      const float dsc = wl * (dwl - S);
+      // this half's sub-key of each selected slot; -1 for a slot outside [0, N)
+      const int ii = il >= 0 && il < A.N ? (hf == 0 ? il / s : il % s) : -1;
+      const float xv = live && act ? ld((const InT*)A.x, row * d_k + hf * A.hd + c) : 0.f;
+      float dxv = 0.f;
+      // eight selected slots at a time, every load unguarded (a slot outside [0, N) reads
+      // row 0 with coefficient 0), so that eight row loads are in flight together
+      for (int k0 = 0; k0 < n_sel; k0 += 8) {
+        int rk[8];
+        float dk[8], cv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = min(k0 + u, 63);
+          const int ik = k0 + u < n_sel ? __builtin_amdgcn_readlane(ii, k) : -1;
+          const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dsc), k));
+          rk[u] = ik >= 0 ? ik : 0;
+          dk[u] = ik >= 0 ? d : 0.f;
+          cv[u] = ld(C, (size_t)rk[u] * A.hd + cc);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dxv = fmaf(dk[u], cv[u], dxv);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        dxv = fmaf(dk[u], cv[u], dxv);
-        atomicAdd(&acc[rk[u] * 64 + lane], dk[u] * xv);
+      if (live && act) A.dx[row * d_k + hf * A.hd + c] = dxv;
+      Xm[tl * 64 + lane] = xv;
+      mine[q] = ii;
+      if (ii >= 0) atomicAdd(&Dm[tl * s + ii], dsc);
+    }
+    __syncthreads();
+    if (r0 < s) {
+      const int rr = r0 + (lane & 31);
+#pragma unroll 4
+      for (int k0 = 0; k0 < kAbStep; k0 += 2) {
+        const int kk = k0 + (lane >> 5);
+        const float a = rr < s ? Dm[kk * s + rr] : 0.f;
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Xm[kk * 64 + (lane & 31)], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Xm[kk * 64 + 32 + (lane & 31)], acc1, 0, 0, 0);
       }
     }
-    if (act) A.dx[row * d_k + hf * A.hd + c] = dxv;
+    __syncthreads();
+    // clear this wave's entries of D for the next step (rows of its own tokens)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (mine[q] >= 0) Dm[(wave * 2 + q) * s + mine[q]] = 0.f;
   }
-  __syncthreads();
-  float* out = A.dsub + ((size_t)h * 2 + hf) * s * A.hd;
-  for (int i = threadIdx.x; i < s * 64; i += blockDim.x) {
-    const int r = i >> 6, cc = slice * 64 + (i & 63);
-    const float v = acc[i];
-    if (cc < A.hd && v != 0.f) atomicAdd(&out[(size_t)r * A.hd + cc], v);
+  // D[row][col]: lane holds col = lane % 32, rows 8*(e/4) + 4*(lane/32) + e%4
+  if (r0 < s) {
+    float* out = A.dsub + ((size_t)h * 2 + hf) * s * A.hd;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = r0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int c0 = slice * 64 + (lane & 31), c1 = c0 + 32;
+      if (r < s && c0 < A.hd && acc0[e] != 0.f) atomicAdd(&out[(size_t)r * A.hd + c0], acc0[e]);
+      if (r < s && c1 < A.hd && acc1[e] != 0.f) atomicAdd(&out[(size_t)r * A.hd + c1], acc1[e]);
+    }
   }
 }
 
@@ -707,7 +746,7 @@ hipError_t launch_address_backward(const sdm_shape& S, const void* x, const void
   const long long Th = (long long)S.B * S.T;
   if (Th == 0) return hipSuccess;
   const dim3 grid((unsigned)((Th + kAbChunk - 1) / kAbChunk), (unsigned)(2 * A.nslice), (unsigned)S.H);
-  const size_t lds = (size_t)A.s * 64 * 4;
+  const size_t lds = ((size_t)kAbStep * A.s + (size_t)kAbStep * 64) * 4;
   if (S.in_dtype == SDM_BF16)
     hipLaunchKernelGGL(addr_backward_kernel<uint16_t>, grid, dim3(kAbWaves * 64), lds, stream, A);
   else

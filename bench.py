@@ -16,7 +16,14 @@ With --decay the step runs the whole-table decay variant instead (decay state re
 the table every step; the recurrence call then includes the log-decay scan and the decay
 pass).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay]
+With --backward the step is a training step of the layer: init, addressing of keys and
+queries, the recurrence with its log of pre-update rows, the memory-efficient backward of
+the recurrence (which restores M0 in place) and the addressing backward for keys and
+queries, from a synthetic output gradient. ``roofline`` then describes the recurrence
+backward call (preparation pass and reverse walk) and ``value`` counts layer tokens per
+training step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay | --backward]
 """
 from __future__ import annotations
 
@@ -38,6 +45,7 @@ import sdm_inputs as SI  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "layer_8b_long"
 METRIC = "SDM layer tokens/s on 1 MI355X; gather/scatter HBM GB/s vs peak"
+METRIC_BACKWARD = "SDM layer training tokens/s (forward with log + backward) on 1 MI355X; backward HBM GB/s vs peak"
 
 
 def log(*a):
@@ -51,6 +59,17 @@ def recurrence_bytes_per_token_head(sh: SI.Shape) -> int:
     mem = 2 if sh.mem_dtype == "bf16" else 4
     inb = 2 if sh.in_dtype == "bf16" else 4
     return (2 * sh.W + sh.R) * sh.d_v * mem + sh.d_v * inb + sh.d_v * 4 + 8
+
+
+def backward_bytes_per_token_head(sh: SI.Shape) -> int:
+    """Algorithmic HBM bytes of the recurrence backward per (batch, head, token): the W
+    logged rows, the W + R rows of G read and written (float32), the R read rows and W
+    restored rows of the table, go_t read and dv_t written (float32), v_t read, the weight,
+    alpha and beta gradients written and the slot lists, weights and gates read."""
+    mem = 2 if sh.mem_dtype == "bf16" else 4
+    inb = 2 if sh.in_dtype == "bf16" else 4
+    rows = sh.W * sh.d_v * mem + 2 * (sh.W + sh.R) * sh.d_v * 4 + sh.R * sh.d_v * mem + sh.W * sh.d_v * mem
+    return rows + 8 * sh.d_v + sh.d_v * inb + 4 * (sh.W + sh.R + 2) + 8 * (sh.W + sh.R) + 8
 
 
 RECURRENCE_SOURCES = ("sdm_dataflow.hip", "sdm_device.hpp")
@@ -134,7 +153,11 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(SI.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decay", action="store_true", help="whole-table decay variant")
+    ap.add_argument("--backward", action="store_true", help="training step: forward with log and backward")
     args = ap.parse_args()
+    if args.decay and args.backward:
+        print("--decay and --backward are separate modes", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -146,8 +169,8 @@ def main():
     sh = SI.WORKLOADS[args.workload]
     if sh.T == 1:
         return bench_decode(args, sh)
-    if args.decay:
-        args.no_cpu_baseline = True  # the oracle baseline times the default rule
+    if args.decay or args.backward:
+        args.no_cpu_baseline = True  # the oracle baseline times the default forward
     log(f"[bench] generating {sh.name} inputs")
     t0 = time.time()
     inp = SI.make_inputs(sh)
@@ -182,8 +205,41 @@ def main():
     ridx = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.int32, device="cuda")
     rgt = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.backward:
+        s_ = int(round(sh.N ** 0.5))
+        xlog = torch.empty((sh.B, sh.H, sh.T, sh.W, sh.d_v), dtype=mdt, device="cuda")
+        go = torch.randn((sh.B, sh.H, sh.T, sh.d_v), device="cuda",
+                         generator=torch.Generator("cuda").manual_seed(11))
+        G = torch.empty((sh.B, sh.H, sh.N, sh.d_v), dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(go)
+        dal = torch.empty((sh.B, sh.H, sh.T), dtype=torch.float32, device="cuda")
+        dbe = torch.empty_like(dal)
+        dwg = torch.empty_like(wgt)
+        drg = torch.empty_like(rgt)
+        dq = torch.empty((sh.B, sh.H, sh.T, sh.d_k), dtype=torch.float32, device="cuda")
+        dk = torch.empty_like(dq)
+        dsub = torch.empty((sh.H, 2, s_, sh.d_k // 2), dtype=torch.float32, device="cuda")
+        bws = torch.empty(S.backward_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+
+    def train_step(ev=None):
+        S.init_from_M0(shape, M0, M)
+        S.address(shape, k, subkeys, sh.W, widx, wgt)
+        S.address(shape, q, subkeys, sh.R, ridx, rgt)
+        S.recurrent_log(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, xlog, ws)
+        G.zero_()
+        dsub.zero_()
+        if ev is not None:
+            ev[0].record(stream)
+        S.recurrent_backward(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, xlog, go, G, dv, dal, dbe, dwg, drg,
+                             bws)
+        if ev is not None:
+            ev[1].record(stream)
+        S.address_backward(shape, k, subkeys, sh.W, widx, wgt, dwg, dk, dsub)
+        S.address_backward(shape, q, subkeys, sh.R, ridx, rgt, drg, dq, dsub)
 
     def step(ev=None):
+        if args.backward:
+            return train_step(ev)
         S.init_from_M0(shape, M0, M)
         if args.decay:
             S.decay_state_init(shape, lam, lrun)
@@ -214,14 +270,17 @@ def main():
     rec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     tokens = sh.B * sh.T
     value = tokens / (ms_step / 1e3)
-    per_th = recurrence_bytes_per_token_head(sh)
+    per_th = backward_bytes_per_token_head(sh) if args.backward else recurrence_bytes_per_token_head(sh)
     launch_bytes = per_th * sh.B * sh.H * sh.T
     achieved = launch_bytes / (rec_ms / 1e3) / 1e9
-    log(f"[bench] {ms_step:.3f} ms/step, recurrence {rec_ms:.3f} ms, {achieved:.1f} GB/s")
+    log(f"[bench] {ms_step:.3f} ms/step, {'backward' if args.backward else 'recurrence'} {rec_ms:.3f} ms, "
+        f"{achieved:.1f} GB/s")
+    if args.backward:
+        assert S.workspace_error(bws) == 0, "a workgroup of the backward gave up waiting"
 
-    traffic = None if args.decay else traffic_from_profile(sh.name)
+    traffic = None if (args.decay or args.backward) else traffic_from_profile(sh.name)
     out = {
-        "metric": METRIC,
+        "metric": (METRIC_BACKWARD if args.backward else METRIC),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -235,9 +294,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": sh.T, "N": sh.N, "d_k": sh.d_k, "d_v": sh.d_v,
                    "kappa": sh.kappa, "W": sh.W, "R": sh.R, "in_dtype": sh.in_dtype, "mem_dtype": sh.mem_dtype,
-                   "arith": "fp32", **({"decay": "whole table"} if args.decay else {})},
+                   "arith": "fp32", **({"decay": "whole table"} if args.decay else {}),
+                   **({"step": "forward with log + backward"} if args.backward else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "recurrence",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "recurrence backward" if args.backward else "recurrence",
                      "ms_per_launch": rec_ms, "bytes_per_launch": launch_bytes},
         "cpu_baseline": cpu,
     }

@@ -43,7 +43,6 @@ constexpr int kMaxSel = 64;        // W, R <= 64
 constexpr int kXcd = 8;            // workgroups are dealt round-robin to this many L2 domains
 constexpr uint32_t kNone = 0x1FFFFFFCu;  // element index of a row that touches nothing: its
                                          // byte offset (x 2 or 4) lies past every table
-constexpr int MH = 8;              // rows of each kind per row group
 constexpr int kMaxWaves = 16;      // waves per workgroup (K)
 constexpr int kFinRing = 128;      // finished-token ring (> 4 K: a token waits on at most
                                    // 2K - 1 later tokens, none older than 2K is running)
@@ -209,14 +208,16 @@ struct alignas(16) TokMeta {
 };
 static_assert(sizeof(TokMeta<8>) % 16 == 0 && sizeof(TokMeta<64>) % 16 == 0, "LDS layout keeps 16-byte rows");
 
-template <int NG>
+template <int NG, int MH>
 constexpr size_t wave_lds_bytes() {
   constexpr int C = 64 / NG, LIST = MH * NG;
   return (3 * sizeof(TokMeta<LIST>) + (size_t)2 * LIST * (C + 1) * 4 + 15) / 16 * 16;
 }
 constexpr size_t kCtrlBytes = (kFinRing + 16) * 4;
 
-template <typename MemT, typename InT, int NG>
+// NG row groups of C = 64 / NG lanes: each group holds the same C columns and takes up to MH
+// write rows and MH read rows of every token.
+template <typename MemT, typename InT, int NG, int MH>
 __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
   constexpr int C = 64 / NG;
   constexpr int LIST = MH * NG;  // longest slot list handled; group h holds rows h*MH + i
@@ -225,7 +226,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
   int* fin = (int*)smem;       // [kFinRing]: token that finished in each ring position
   int* ctrl = fin + kFinRing;  // [0]: give-up flag
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, K = A.K;
-  Meta* meta = (Meta*)(smem + kCtrlBytes + wave * wave_lds_bytes<NG>());
+  Meta* meta = (Meta*)(smem + kCtrlBytes + wave * wave_lds_bytes<NG, MH>());
   // per-column partials of one token: write rows [0, LIST), read rows [LIST, 2 LIST)
   float(*part)[C + 1] = (float(*)[C + 1])((unsigned char*)(meta + 3));
   for (int i = threadIdx.x; i < kFinRing; i += blockDim.x) fin[i] = -1;
@@ -316,19 +317,20 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
       rm[i] = act && m < N32 ? m * (uint32_t)d_v + (uint32_t)c : kNone;
     }
   };
-  // sums over this wave's columns of one token's row partials, added into the outputs
+  // sums over this wave's columns of one token's row partials, added into the outputs: lane
+  // j sums write row j and read row j (W, R <= 64), each into its own output resource
   auto reduce = [&](int tt) {
-#pragma unroll
-    for (int k = 0; k < (2 * LIST + 63) / 64; ++k) {
-      const int i = lane + 64 * k;
-      const bool wr = i < W, rd = i >= LIST && i - LIST < R;
-      if (wr || rd) {
-        float sum = 0.f;
+    if (lane < W) {
+      float sum = 0.f;
 #pragma unroll 8
-        for (int q = 0; q < C; ++q) sum += part[i][q];
-        const uint32_t off = wr ? ((uint32_t)tt * W + i) * 4 : ((uint32_t)tt * R + (i - LIST)) * 4;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, wr ? rDW : rDR, off, 0, 0);
-      }
+      for (int q = 0; q < C; ++q) sum += part[lane][q];
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, rDW, ((uint32_t)tt * W + lane) * 4, 0, 0);
+    }
+    if (lane < R) {
+      float sum = 0.f;
+#pragma unroll 8
+      for (int q = 0; q < C; ++q) sum += part[LIST + lane][q];
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, rDR, ((uint32_t)tt * R + lane) * 4, 0, 0);
     }
   };
   auto give_up = [&] {
@@ -405,10 +407,19 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     // 5. token t (rows without a slot loaded zeros: dy = 0 there since wadd = 0)
     const float g = act ? __uint_as_float(graw) : 0.f, vc = act ? cvt<InT>(vraw) : 0.f;
     float aj[MH], wd[MH];
-    *(float4*)&aj[0] = *(const float4*)&mt.a[hb];
-    *(float4*)&aj[4] = *(const float4*)&mt.a[hb + 4];
-    *(float4*)&wd[0] = *(const float4*)&mt.wadd[hb];
-    *(float4*)&wd[4] = *(const float4*)&mt.wadd[hb + 4];
+    if constexpr (MH % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < MH; i += 4) {
+        *(float4*)&aj[i] = *(const float4*)&mt.a[hb + i];
+        *(float4*)&wd[i] = *(const float4*)&mt.wadd[hb + i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MH; ++i) {
+        aj[i] = mt.a[hb + i];
+        wd[i] = mt.wadd[hb + i];
+      }
+    }
     float s = 0.f, dd = 0.f;
     float x[MH], dy[MH];
 #pragma unroll
@@ -438,8 +449,13 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     // stores of token t (dropped for rows without a slot): G and the undone rows of M; G of
     // the reads that store it
     float rcv[MH];
-    *(float4*)&rcv[0] = *(const float4*)&mt.rc[hb];
-    *(float4*)&rcv[4] = *(const float4*)&mt.rc[hb + 4];
+    if constexpr (MH % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < MH; i += 4) *(float4*)&rcv[i] = *(const float4*)&mt.rc[hb + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < MH; ++i) rcv[i] = mt.rc[hb + i];
+    }
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
       bst<float>(rG, rn[i] * 4, al * (dy[i] + aj[i] * drho));
@@ -622,10 +638,9 @@ BwdWs bwd_layout(const sdm_shape& S) {
   return L;
 }
 
-template <typename MemT, typename InT, int NG>
-hipError_t launch_cfg(BwdArgs A, const PrepArgs& Pa0, hipStream_t st) {
+template <typename MemT, typename InT, int NG, int MH>
+hipError_t launch_cfg(BwdArgs A, const PrepArgs& Pa0, long long wgs, hipStream_t st) {
   A.P = (A.d_v + 64 / NG - 1) / (64 / NG);
-  const long long wgs = (long long)((A.U + kXcd - 1) / kXcd) * kXcd * A.P;
   // K waves per workgroup: 8, or 16 when fewer than two workgroups per CU would run
   A.K = wgs >= 2ll * device_cus() ? 8 : kMaxWaves;
   PrepArgs Pa = Pa0;
@@ -638,19 +653,45 @@ hipError_t launch_cfg(BwdArgs A, const PrepArgs& Pa0, hipStream_t st) {
                      plds, st, Pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = kCtrlBytes + (size_t)A.K * wave_lds_bytes<NG>();
-  hipLaunchKernelGGL((backward_kernel<MemT, InT, NG>), dim3((unsigned)wgs), dim3(64 * A.K), lds, st, A);
+  const size_t lds = kCtrlBytes + (size_t)A.K * wave_lds_bytes<NG, MH>();
+  hipLaunchKernelGGL((backward_kernel<MemT, InT, NG, MH>), dim3((unsigned)wgs), dim3(64 * A.K), lds, st, A);
   return hipGetLastError();
 }
 
-// As many row groups as 8 rows per group need: 64 / NG columns per wave.
+// Column blocks of C = 64 / NG columns, each row group taking MH in {2, 4, 8} rows of each
+// kind (NG * MH >= max(W, R)): the widest block whose grid still gives every CU a
+// workgroup, else the narrowest (units with few heads fill the chip with narrow blocks).
 template <typename MemT, typename InT>
 hipError_t launch_bwd(const BwdArgs& A, const PrepArgs& Pa, hipStream_t st) {
   const int list = A.W > A.R ? A.W : A.R;
-  if (list <= MH) return launch_cfg<MemT, InT, 1>(A, Pa, st);
-  if (list <= 2 * MH) return launch_cfg<MemT, InT, 2>(A, Pa, st);
-  if (list <= 4 * MH) return launch_cfg<MemT, InT, 4>(A, Pa, st);
-  return launch_cfg<MemT, InT, 8>(A, Pa, st);
+  const int cus = device_cus();
+  int pick = -1;
+  long long pick_wgs = 0;
+  for (int lg = 0; lg <= 4; ++lg) {  // NG = 1, 2, 4, 8, 16
+    const int NG = 1 << lg, C = 64 / NG;
+    if ((list + NG - 1) / NG > 8) continue;
+    pick = lg;
+    pick_wgs = (long long)((A.U + kXcd - 1) / kXcd) * kXcd * ((A.d_v + C - 1) / C);
+    if (pick_wgs >= cus) break;
+  }
+  if (pick < 0) return hipErrorInvalidValue;
+  const int NG = 1 << pick, mh = (list + NG - 1) / NG;
+  const int MH = mh <= 2 ? 2 : mh <= 4 ? 4 : 8;
+  if (NG == 1 && MH == 2) return launch_cfg<MemT, InT, 1, 2>(A, Pa, pick_wgs, st);
+  if (NG == 1 && MH == 4) return launch_cfg<MemT, InT, 1, 4>(A, Pa, pick_wgs, st);
+  if (NG == 1 && MH == 8) return launch_cfg<MemT, InT, 1, 8>(A, Pa, pick_wgs, st);
+  if (NG == 2 && MH == 2) return launch_cfg<MemT, InT, 2, 2>(A, Pa, pick_wgs, st);
+  if (NG == 2 && MH == 4) return launch_cfg<MemT, InT, 2, 4>(A, Pa, pick_wgs, st);
+  if (NG == 2 && MH == 8) return launch_cfg<MemT, InT, 2, 8>(A, Pa, pick_wgs, st);
+  if (NG == 4 && MH == 2) return launch_cfg<MemT, InT, 4, 2>(A, Pa, pick_wgs, st);
+  if (NG == 4 && MH == 4) return launch_cfg<MemT, InT, 4, 4>(A, Pa, pick_wgs, st);
+  if (NG == 4 && MH == 8) return launch_cfg<MemT, InT, 4, 8>(A, Pa, pick_wgs, st);
+  if (NG == 8 && MH == 2) return launch_cfg<MemT, InT, 8, 2>(A, Pa, pick_wgs, st);
+  if (NG == 8 && MH == 4) return launch_cfg<MemT, InT, 8, 4>(A, Pa, pick_wgs, st);
+  if (NG == 8 && MH == 8) return launch_cfg<MemT, InT, 8, 8>(A, Pa, pick_wgs, st);
+  if (NG == 16 && MH == 2) return launch_cfg<MemT, InT, 16, 2>(A, Pa, pick_wgs, st);
+  if (NG == 16 && MH == 4) return launch_cfg<MemT, InT, 16, 4>(A, Pa, pick_wgs, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -19,7 +19,11 @@ CASES = {
     "small_T128": W_["small"].replace(B=1, H=2, T=128),
     "layer_8b_T100": W_["layer_8b_long"].replace(B=1, H=2, T=100),
     "coupled_T96": W_["layer_8b_long"].replace(B=1, H=2, T=96),
+    # every head of the 1.4B shape: the launch picks the configuration the full size uses
+    # (16-column blocks, 8 rows per group); the oracle checks three units
+    "layer_1p4b_allheads_T40": W_["layer_1p4b"].replace(T=40),
 }
+SAMPLED = {"layer_1p4b_allheads_T40": [(0, 0), (3, 7), (7, 15)]}
 
 
 def couple(wi, ri, N):
@@ -61,6 +65,7 @@ def test_log_and_backward(sdm, name):
     widx, wgt = np.zeros(shp_w, np.int32), np.zeros(shp_w, np.float32)
     ridx, rgt = np.zeros(shp_r, np.int32), np.zeros(shp_r, np.float32)
     ref = {}
+    check = set(SAMPLED.get(name, [(b, h) for b in range(sh.B) for h in range(sh.H)]))
     for b in range(sh.B):
         for h in range(sh.H):
             sk = SI.widen(inp["subkeys"][h], sh.in_dtype)
@@ -75,6 +80,8 @@ def test_log_and_backward(sdm, name):
                 ri = couple(wi, ri, sh.N)
             ww, rw = ww.astype(np.float32), rw.astype(np.float32)
             widx[b, h], wgt[b, h], ridx[b, h], rgt[b, h] = wi, ww, ri, rw
+            if (b, h) not in check:
+                continue
             o, MT = O.recurrence(M0, wi, ww.astype(np.float64), ri, rw.astype(np.float64), v, al, be, sh.mem_dtype)
             xl = O.recurrence_log(M0, wi, ww.astype(np.float64), v, al, be, sh.mem_dtype)
             g = O.recurrence_backward(MT, xl, wi, ww.astype(np.float64), ri, rw.astype(np.float64), v, al, be,
@@ -138,9 +145,10 @@ def test_log_and_backward(sdm, name):
             e = rel_err(dx[b, h].cpu().numpy(), rdx)
             log(f"[backward] {name} d{xname} ({b},{h}): {e:.1e}")
             assert e < tol, f"d{xname}"
-    e = rel_err(dsub.cpu().numpy(), ref_dsub)
-    log(f"[backward] {name} dsubkeys: {e:.1e}")
-    assert e < tol
+    if name not in SAMPLED:  # the sub-key gradient sums over every unit
+        e = rel_err(dsub.cpu().numpy(), ref_dsub)
+        log(f"[backward] {name} dsubkeys: {e:.1e}")
+        assert e < tol
 
 
 @pytest.mark.parametrize("name", ["coupled_T96", "layer_8b_T100"])

@@ -148,7 +148,9 @@ sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_co
 
 /* sdm_recurrent that also logs, for the backward, the pre-update value of every written row
  * as its token read it: xlog [B,H,T,W,d_v] mem_dtype out (rows of slots outside [0, N) are
- * 0). T*W*d_v*sizeof(mem) must stay below 2^31 bytes per unit. Written-rows rule only. */
+ * 0). T*W*d_v*sizeof(mem) must stay below 2^31 bytes per unit. Written-rows rule only; any W,
+ * R that sdm_recurrent takes (shapes the pipelined path does not take log on the sequential
+ * path). */
 sdm_status sdm_recurrent_log(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
                              const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                              void* xlog, void* ws, size_t ws_bytes, void* stream);

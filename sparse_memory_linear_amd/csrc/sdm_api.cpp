@@ -296,9 +296,6 @@ sdm_status sdm_recurrent_log(const sdm_shape* S, const int32_t* widx, const floa
                              const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                              void* xlog, void* ws, size_t ws_bytes, void* stream) {
   if (!xlog) return SDM_ERR_INVALID_ARG;
-  sdm_status st = check_shape(S, true);
-  if (st != SDM_OK) return st;
-  if (!dataflow_supported(*S)) return SDM_ERR_UNSUPPORTED;
   return recurrent_impl(S, widx, wgt, ridx, rgt, v, alpha, beta, M, nullptr, nullptr, o, ws, ws_bytes, stream, xlog);
 }
 

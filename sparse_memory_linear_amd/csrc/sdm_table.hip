@@ -64,6 +64,7 @@ struct RecArgs {
   const float* beta;
   void* M;
   float* o;
+  uint32_t* xlog;  // optional [U][T][W][d_v] log of the pre-update written rows
   unsigned long long* err;
   int U, T, W, R, d_v;
   long long N;
@@ -111,13 +112,17 @@ __global__ void __launch_bounds__(64) recurrent_seq_kernel(RecArgs A) {
     // gated delta write of the W slots (old values re-read; they are unchanged)
     for (int j = 0; j < A.W; ++j) {
       const int n = wi[j];
+      uint32_t* lg = A.xlog ? A.xlog + (ut * A.W + j) * rowdw + dwc : nullptr;
       if (n < 0 || n >= N) {
         if (lane == 0 && blockIdx.x == 0) atomicAdd(A.err, 1ull);
+        if (lg && active) *lg = 0u;  // no row: the log holds zeros
         continue;
       }
       uint32_t* p = &Mu[(size_t)n * rowdw + dwc];
       float x[CPL], y[CPL];
-      MT::unpack(*p, x);
+      const uint32_t old = *p;
+      if (lg && active) *lg = old;  // the row as this token reads it, before its write
+      MT::unpack(old, x);
       const float a = ww[j];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) y[c] = fmaf(al, x[c], a * delta[c]);
@@ -194,6 +199,7 @@ hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float
   A.beta = beta;
   A.M = M;
   A.o = o;
+  A.xlog = (uint32_t*)xlog;
   A.err = (unsigned long long*)((char*)ws + L.err);
   A.U = S.B * S.H;
   A.T = S.T;
@@ -204,7 +210,7 @@ hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float
   if (A.U == 0 || A.T == 0) return hipSuccess;
   if (dataflow_supported(S, dk != nullptr))
     return launch_dataflow(S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, dk, xlog, stream);
-  if (dk || xlog) return hipErrorInvalidValue;  // whole-table decay and the row log run on the pipeline only
+  if (dk) return hipErrorInvalidValue;  // the whole-table decay runs on the pipeline only
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
   if (mb && ib) return launch_seq<uint16_t, uint16_t>(A, stream);
   if (mb && !ib) return launch_seq<uint16_t, float>(A, stream);

@@ -22,8 +22,14 @@ CASES = {
     # every head of the 1.4B shape: the launch picks the configuration the full size uses
     # (16-column blocks, 8 rows per group); the oracle checks three units
     "layer_1p4b_allheads_T40": W_["layer_1p4b"].replace(T=40),
+    # edges: one token; fewer tokens than waves, lists that leave padding rows in the last
+    # row group (float32 table, bf16 inputs); a d_v that leaves the last 16-column block
+    # half empty
+    "edge_T1": W_["small"].replace(B=1, H=2, T=1),
+    "edge_T5_W3_R5": W_["small"].replace(B=2, H=1, T=5, W=3, R=5),
+    "ragged_dv40_allheads_T24": W_["layer_1p4b"].replace(T=24, d_v=40),
 }
-SAMPLED = {"layer_1p4b_allheads_T40": [(0, 0), (3, 7), (7, 15)]}
+SAMPLED = {"layer_1p4b_allheads_T40": [(0, 0), (3, 7), (7, 15)], "ragged_dv40_allheads_T24": [(0, 0), (7, 15)]}
 
 
 def couple(wi, ri, N):

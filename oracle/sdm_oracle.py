@@ -394,3 +394,86 @@ def address_backward(x, C1, C2, idx, weight, dweight):
     np.add.at(dC1, i1.ravel(), (dsc[:, :, None] * x[:, None, :h]).reshape(-1, h))
     np.add.at(dC2, i2.ravel(), (dsc[:, :, None] * x[:, None, h:]).reshape(-1, h))
     return dx, dC1, dC2
+
+
+def chunkwise_recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, chunk: int, mem_dtype: str):
+    """The chunkwise two-phase form of ``recurrence`` (written-rows rule, R1; PL App. A.1,
+    "Phase 1" / "Phase 2", and App. A.2's sparse inner products between tokens' slot lists).
+
+    Inside a chunk a row changes only at the tokens that write it, so with delta_t the write
+    residual of token t (delta_t = beta_t (v_t - rho_t)) every quantity is the chunk-start
+    table M0 plus a linear combination of the chunk's deltas. For a slot n and tokens
+    tau < t, let dec(n; tau, t) be the product of alpha over the chunk's writers of n
+    strictly between tau and t (tau = -1: from the chunk start). Then
+
+      rho_t = alpha_t sum_j a_tj dec(n_tj; -1, t) M0[n_tj] + sum_{tau<t} K[t,tau] delta_tau
+      K[t,tau] = alpha_t sum_{j: n_tj written by tau} a_tj dec(n_tj; tau, t) a_{tau,n_tj}
+      o_t = sum_r u_tr dec(m_tr; -1, t+1) M0[m_tr] + sum_{tau<=t} Q[t,tau] delta_tau
+      Q[t,tau] = sum_{r: m_tr written by tau} u_tr dec(m_tr; tau, t+1) a_{tau,m_tr}
+
+    so (I + diag(beta) K) delta = beta (v - P), a unit lower-triangular system. Phase 1 needs
+    only slots, weights and gates (parallel across chunks); Phase 2 gathers the chunk's rows,
+    solves for delta, forms o, and writes each written row once:
+      M[n] <- dec(n; -1, end) M0[n] + sum_{writers tau of n} dec(n; tau, end) a_{tau,n} delta_tau
+
+    READING R26: rows are rounded to the table dtype once per chunk, when written back (the
+    token-by-token rule rounds at every write; with a float64 or float32 table the two agree
+    up to summation order). Returns o [T, d_v] and the final table [N, d_v] (float64)."""
+    M = np.array(M0, dtype=np.float64, copy=True)
+    T, d_v = len(widx), M.shape[1]
+    o = np.zeros((T, d_v))
+    for c0 in range(0, T, chunk):
+        tok = list(range(c0, min(c0 + chunk, T)))
+        L = len(tok)
+        n = [np.asarray(widx[t]) for t in tok]
+        a = [np.asarray(wgt[t], dtype=np.float64) for t in tok]
+        m = [np.asarray(ridx[t]) for t in tok]
+        u = [np.asarray(rgt[t], dtype=np.float64) for t in tok]
+        al = np.array([alpha[t] for t in tok], dtype=np.float64)
+        be = np.array([beta[t] for t in tok], dtype=np.float64)
+        # writers of each slot in the chunk, in token order: slot -> [(local token, weight)]
+        writers = {}
+        for i in range(L):
+            for slot, w in zip(n[i].tolist(), a[i].tolist()):
+                writers.setdefault(slot, []).append((i, w))
+
+        def dec(slot, lo, hi):
+            """Product of alpha over the chunk's writers of slot strictly between lo and hi."""
+            p = 1.0
+            for i, _ in writers.get(slot, []):
+                if lo < i < hi:
+                    p *= al[i]
+            return p
+
+        # Phase 1: interactions and coefficients (no table values)
+        K = np.zeros((L, L))
+        Q = np.zeros((L, L))
+        for i in range(L):
+            for slot, w in zip(n[i].tolist(), a[i].tolist()):
+                for k, wk in writers[slot]:
+                    if k < i:
+                        K[i, k] += al[i] * w * dec(slot, k, i) * wk
+            for slot, w in zip(m[i].tolist(), u[i].tolist()):
+                for k, wk in writers.get(slot, []):
+                    if k <= i:
+                        Q[i, k] += w * dec(slot, k, i + 1) * wk
+        # Phase 2: gather, solve, read, write back
+        P = np.zeros((L, d_v))
+        O0 = np.zeros((L, d_v))
+        for i in range(L):
+            for slot, w in zip(n[i].tolist(), a[i].tolist()):
+                P[i] += al[i] * w * dec(slot, -1, i) * M[slot]
+            for slot, w in zip(m[i].tolist(), u[i].tolist()):
+                O0[i] += w * dec(slot, -1, i + 1) * M[slot]
+        V = np.asarray([v[t] for t in tok], dtype=np.float64)
+        delta = np.linalg.solve(np.eye(L) + be[:, None] * K, be[:, None] * (V - P))
+        o[tok] = O0 + Q @ delta
+        new = {}
+        for slot, ws in writers.items():
+            row = dec(slot, -1, L) * M[slot]
+            for k, wk in ws:
+                row = row + dec(slot, k, L) * wk * delta[k]
+            new[slot] = row
+        for slot, row in new.items():
+            M[slot] = round_mem(row, mem_dtype)
+    return o, M

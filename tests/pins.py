@@ -527,6 +527,32 @@ def pin_address_backward_finite_differences(O):
         assert np.allclose(g, num, rtol=1e-6, atol=1e-8), ["dx", "dC1", "dC2"][k]
 
 
+def pin_chunkwise_equals_sequential(O):
+    """The chunkwise two-phase form (PL App. A.1-A.2) gives the token-by-token rule's output
+    and final table (float64, no rounding) for any chunk length: many tokens per slot so
+    that rows are written several times inside a chunk and read after, gates at 0 and 1,
+    chunk lengths that do and do not divide T."""
+    rng = np.random.default_rng(47)
+    for trial in range(12):
+        N, d_v = int(rng.integers(5, 11)), 3
+        T = int(rng.integers(2, 13))
+        W, R = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        widx = [rng.choice(N, W, replace=False) for _ in range(T)]
+        ridx = [rng.choice(N, R, replace=False) for _ in range(T)]
+        wgt, rgt = rng.random((T, W)) + 0.05, rng.random((T, R)) + 0.05
+        v = rng.standard_normal((T, d_v))
+        alpha = rng.uniform(0.2, 0.99, T)
+        alpha[rng.random(T) < 0.15] = 0.0
+        alpha[rng.random(T) < 0.15] = 1.0
+        beta = rng.uniform(0.05, 1.0, T)
+        M0 = rng.standard_normal((N, d_v))
+        o1, M1 = O.recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, "f64")
+        for C in (1, 2, 3, T):
+            o2, M2 = O.chunkwise_recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, C, "f64")
+            assert np.allclose(o1, o2, rtol=1e-10, atol=1e-10), (trial, C)
+            assert np.allclose(M1, M2, rtol=1e-10, atol=1e-10), (trial, C)
+
+
 ALL_PINS = [
     pin_round_bf16,
     pin_pk_equals_brute_force,
@@ -550,4 +576,5 @@ ALL_PINS = [
     pin_head_mix,
     pin_backward_finite_differences,
     pin_address_backward_finite_differences,
+    pin_chunkwise_equals_sequential,
 ]

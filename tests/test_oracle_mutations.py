@@ -77,6 +77,14 @@ MUTANTS = {
     "abwd_wrong_codebook": ('dx[:, h:] = np.einsum("tk,tkc->tc", dsc, C2[i2])', 'dx[:, h:] = np.einsum("tk,tkc->tc", dsc, C1[i2])'),
     # addressing backward: sub-key gradients scattered with the other half's index
     "abwd_swapped_index": ("np.add.at(dC1, i1.ravel(),", "np.add.at(dC1, i2.ravel(),"),
+    # chunkwise form: reads miss the chunk's own writes
+    "chunk_no_q": ("        o[tok] = O0 + Q @ delta\n", "        o[tok] = O0\n"),
+    # chunkwise form: a read sees its token's write undecayed by nothing (window one short)
+    "chunk_q_window": ("Q[i, k] += w * dec(slot, k, i + 1) * wk", "Q[i, k] += w * dec(slot, k, i) * wk"),
+    # chunkwise form: the interaction without the token's own gate
+    "chunk_k_no_alpha": ("K[i, k] += al[i] * w * dec(slot, k, i) * wk", "K[i, k] += w * dec(slot, k, i) * wk"),
+    # chunkwise form: the written-back row forgets the decay of its chunk-start value
+    "chunk_no_start_decay": ("row = dec(slot, -1, L) * M[slot]", "row = M[slot]"),
     # per-half top-k keeps too few sub-keys
     "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
 }

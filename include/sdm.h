@@ -142,6 +142,26 @@ sdm_status sdm_decode_step(const sdm_shape* shape, const void* q, const void* k,
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Chunkwise two-phase form of the recurrence (PL App. A.1 "Phase 1" / "Phase 2", App. A.2:
+ * inside a chunk of 64 tokens every quantity is the chunk-start table plus a combination of
+ * the chunk's write residuals; Phase 1 forms the tokens' interactions over shared slots and
+ * solves the unit lower-triangular system's inverse, in parallel over chunks; Phase 2
+ * gathers each chunk's rows, forms the residuals and outputs and writes each row back once).
+ * --------------------------------------------------------------------------------------- */
+
+/* Bytes of device memory sdm_recurrent_chunked needs as workspace (0 for a shape it does not
+ * take: W or R above 32, or an invalid shape). */
+size_t sdm_workspace_bytes_chunked(const sdm_shape* shape);
+
+/* The recurrence of sdm_recurrent (written-rows rule), computed chunk by chunk: same
+ * arguments, same o and final table up to float32 summation order, except that written rows
+ * are rounded to mem_dtype once per chunk (when written back) instead of at every write.
+ * W, R <= 32; ws: at least sdm_workspace_bytes_chunked(shape) bytes. */
+sdm_status sdm_recurrent_chunked(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                                 const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                                 float* o, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Memory-efficient backward of the recurrence (PL App. A.3: the forward's sparse updates
  * are undone in place during the backward, so memory stays O(N d + T W d)).
  * --------------------------------------------------------------------------------------- */

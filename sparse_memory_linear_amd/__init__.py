@@ -20,7 +20,7 @@ __all__ = [
     "forward", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
     "materialize", "gates", "output_gate", "head_mix", "recurrent_log", "recurrent_backward",
-    "backward_workspace_bytes", "address_backward",
+    "backward_workspace_bytes", "address_backward", "workspace_bytes_chunked", "recurrent_chunked",
 ]
 
 SDM_F32 = 0
@@ -78,6 +78,8 @@ _SIGS = {
     "sdm_head_mix": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
     "sdm_recurrent_log": (ctypes.c_int, [_SP] + [_P] * 11 + [ctypes.c_size_t, _P]),
     "sdm_backward_workspace_bytes": (ctypes.c_size_t, [_SP]),
+    "sdm_workspace_bytes_chunked": (ctypes.c_size_t, [_SP]),
+    "sdm_recurrent_chunked": (ctypes.c_int, [_SP] + [_P] * 10 + [ctypes.c_size_t, _P]),
     "sdm_address_backward": (ctypes.c_int, [_SP, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "sdm_recurrent_backward": (ctypes.c_int, [_SP] + [_P] * 17 + [ctypes.c_size_t, _P]),
 }
@@ -256,3 +258,13 @@ def address_backward(shape: Shape, x, subkeys, n_sel: int, idx, weight, dweight,
     _check(lib().sdm_address_backward(ctypes.byref(shape), _ptr(x), _ptr(subkeys), int(n_sel), _ptr(idx),
                                       _ptr(weight), _ptr(dweight), _ptr(dx), _ptr(dsub), _stream(stream)),
            "sdm_address_backward")
+
+
+def workspace_bytes_chunked(shape: Shape) -> int:
+    return lib().sdm_workspace_bytes_chunked(ctypes.byref(shape))
+
+
+def recurrent_chunked(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, stream=None):
+    _check(lib().sdm_recurrent_chunked(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(M), _ptr(o), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)), "sdm_recurrent_chunked")

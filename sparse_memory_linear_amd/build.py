@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsdm.so")
 ARCH = "gfx950"
 
-SOURCES = ["sdm_api.cpp", "sdm_table.hip", "sdm_address.hip", "sdm_decode.hip", "sdm_dataflow.hip", "sdm_decay.hip", "sdm_epilogue.hip", "sdm_backward.hip"]
+SOURCES = ["sdm_api.cpp", "sdm_table.hip", "sdm_address.hip", "sdm_decode.hip", "sdm_dataflow.hip", "sdm_decay.hip", "sdm_epilogue.hip", "sdm_backward.hip", "sdm_chunked.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}",

@@ -324,6 +324,40 @@ sdm_status sdm_address_backward(const sdm_shape* S, const void* x, const void* s
                                             (hipStream_t)stream));
 }
 
+size_t sdm_workspace_bytes_chunked(const sdm_shape* shape) {
+  if (check_shape(shape, true) != SDM_OK || !chunked_supported(*shape)) return 0;
+  return chunked_workspace_bytes(*shape);
+}
+
+sdm_status sdm_recurrent_chunked(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                                 const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
+                                 float* o, void* ws, size_t ws_bytes, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!chunked_supported(*S)) return SDM_ERR_UNSUPPORTED;
+  const void* ptrs[] = {widx, wgt, ridx, rgt, v, alpha, beta, M, o};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SDM_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < chunked_workspace_bytes(*S)) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
+  const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
+  const size_t ob = tensor_bytes(*S, S->d_v, 4);
+  const size_t wb = tensor_bytes(*S, S->W, 4), rb = tensor_bytes(*S, S->R, 4), sb = tensor_bytes(*S, 1, 4);
+  const size_t vb = tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype));
+  const void* outs[] = {M, o, ws};
+  const size_t osz[] = {mb, ob, ws_bytes};
+  const void* ins[] = {widx, wgt, ridx, rgt, v, alpha, beta};
+  const size_t isz[] = {wb, wb, rb, rb, vb, sb, sb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SDM_ERR_INVALID_ARG;
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return SDM_ERR_INVALID_ARG;
+  }
+  if (S->T == 0) return SDM_OK;
+  return hip_status(launch_chunked(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, (hipStream_t)stream));
+}
+
 size_t sdm_backward_workspace_bytes(const sdm_shape* shape) {
   if (check_shape(shape, true) != SDM_OK) return 0;
   return backward_workspace_bytes(*shape);

@@ -57,6 +57,11 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
                            const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                            void* ws, const WsLayout& L, const DecayState* dk, void* xlog, hipStream_t stream);
 int device_cus();  // compute units of the current device
+size_t chunked_workspace_bytes(const sdm_shape& S);
+bool chunked_supported(const sdm_shape& S);
+hipError_t launch_chunked(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
+                          const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
+                          void* ws, hipStream_t stream);
 hipError_t launch_address_backward(const sdm_shape& S, const void* x, const void* subkeys, int n_sel,
                                    const int32_t* idx, const float* w, const float* dw, float* dx, float* dsub,
                                    hipStream_t stream);

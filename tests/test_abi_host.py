@@ -261,3 +261,27 @@ def test_address_backward_validates(sdm, no_gpu):
     Z = base(T=0)
     assert L.sdm_address_backward(ctypes.byref(Z), *ok, None) == 0   # nothing to do
 
+
+def test_chunked_validates(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    need = sdm.workspace_bytes_chunked(S)
+    assert need > 0
+    assert sdm.workspace_bytes_chunked(base(W=40, kappa=16)) == 0                 # lists longer than 32
+    p = [FAKE + i * (1 << 36) for i in range(12)]
+    ok = list(p[:9]) + [p[9], need]
+    args = list(ok)
+    args[10] = need - 1                                                            # workspace too small
+    assert L.sdm_recurrent_chunked(sp, *args, None) == -3
+    args = list(ok)
+    args[8] = args[7] + 64                                                         # o inside the table
+    assert L.sdm_recurrent_chunked(sp, *args, None) == -1
+    args = list(ok)
+    args[9] = args[0]                                                              # workspace over widx
+    assert L.sdm_recurrent_chunked(sp, *args, None) == -1
+    args = list(ok)
+    args[2] = None
+    assert L.sdm_recurrent_chunked(sp, *args, None) == -1
+    assert L.sdm_recurrent_chunked(ctypes.byref(base(W=40, kappa=16)), *ok, None) == -2   # unsupported
+

@@ -39,7 +39,6 @@ namespace {
 
 constexpr int kC = 64;                   // tokens per chunk
 constexpr int kMaxList = 32;             // W, R <= 32 on this path
-constexpr int kOcc = kC * kMaxList;
 constexpr int kBuckets = 4096;           // LDS hash: at most 2048 distinct slots, at most half full
 constexpr uint32_t kFree = 0xFFFFFFFFu;
 constexpr int kKMax = kC * (kC - 1) / 2;  // distinct (t, tau < t) pairs
@@ -48,12 +47,13 @@ constexpr int kXcd = 8;                  // workgroups are dealt round-robin to 
 constexpr uint32_t kNoneByte = 0x7FFFFFF0u;  // byte offset past every table (tables < 2^31 - 16 bytes)
 
 // Per-(unit, chunk) block of Phase 1 results, in 4-byte words. Per-occurrence arrays are
-// [kC][LIST] (LIST >= W, R; unused entries hold zeros and wb = -1).
+// [kC][LIST] (LIST >= W, R; unused entries hold zeros and wb = -1). The list area holds the
+// K and Q row starts and, from word kLa0 on, the write-back lists, then K's and Q's entries.
+constexpr int kLa0 = 132;
 struct MetaLayout {
   int list;
-  size_t gw, wc, ge, wb, gr, hdr, kp, ke, qp, qe, wl, words;
+  size_t gw, wc, ge, wb, gr, hdr, la, words;
 };
-__host__ __device__ inline size_t up4(size_t x) { return (x + 3) & ~(size_t)3; }
 __host__ __device__ inline MetaLayout meta_layout(int list) {
   MetaLayout m;
   m.list = list;
@@ -61,15 +61,12 @@ __host__ __device__ inline MetaLayout meta_layout(int list) {
   m.gw = 0;               // alpha_t a_tj dec(n_tj; start, t)
   m.wc = m.gw + occ;      // a_tj dec(n_tj; t, end): the occurrence's own write-back coefficient
   m.ge = m.wc + occ;      // dec(n_tj; start, end) for the slot's last writer
-  m.wb = m.ge + occ;      // -1, or for the slot's last writer (start << 8 | count) of its other writers in wl
+  m.wb = m.ge + occ;      // -1, or for the slot's last writer (start << 8 | count) of its other writers
   m.gr = m.wb + occ;      // u_tr dec(m_tr; start, t+1)
-  m.hdr = m.gr + occ;     // [0] K entries, [1] Q entries, [2..3] 64-bit mask of rows with K entries
-  m.kp = m.hdr + 4;       // [kC + 1] K row starts
-  m.ke = up4(m.kp + kC + 1);   // [kKMax] (tau, beta_t K[t][tau]) sorted by t
-  m.qp = m.ke + 2 * kKMax;     // [kC + 1] Q row starts
-  m.qe = up4(m.qp + kC + 1);   // [kQMax] (tau, Q[t][tau]) sorted by t
-  m.wl = m.qe + 2 * kQMax;     // [occ] (tau, a_tau dec(n; tau, end)): other writers of owned slots
-  m.words = (m.wl + 2 * occ + 63) & ~(size_t)63;
+  m.hdr = m.gr + occ;     // [0] write-back entries, [1] K entries, [2] Q entries, [3..4] rows with K entries
+  m.la = m.hdr + 8;       // [0, 65) K row starts, [65, 130) Q row starts, [kLa0, ...) entries (tau, coef):
+                          // write-back lists, then K (coef beta_t K[t][tau]), then Q, each sorted by t
+  m.words = (m.la + kLa0 + 2 * (occ + kKMax + kQMax) + 63) & ~(size_t)63;
   return m;
 }
 inline int list_for(const sdm_shape& S) {
@@ -95,24 +92,41 @@ struct ChunkArgs {
 
 __device__ __forceinline__ uint32_t chunk_hash(uint32_t s) { return (s * 2654435761u) >> 20; }  // 12 bits
 
+template <int LIST>
 __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
-  __shared__ int sn[kOcc];         // slot of each write occurrence, -1 for none
-  __shared__ float sa[kOcc];       // its weight
-  __shared__ short snx[kOcc];      // next occurrence of the same slot, -1 at the end
-  __shared__ short sbk[kOcc];      // its hash bucket
+  constexpr int NOC = kC * LIST;
+  constexpr int NO = NOC / 256;  // occurrences per thread, write and read each
+  constexpr int SH = LIST == 8 ? 3 : LIST == 16 ? 4 : 5;
+  __shared__ int sn[NOC];          // slot of each write occurrence [t][LIST], -1 for none
+  __shared__ float sa[NOC];        // its weight
+  __shared__ short snx[NOC];       // next occurrence of the same slot, -1 at the end
+  __shared__ short sbk[NOC];       // its hash bucket
   __shared__ uint32_t keys[kBuckets];
   __shared__ int head[kBuckets];
   // couplings: K[t][tau] at [t][tau] (tau < t), Q[t][tau] at [tau][t] (tau <= t)
   __shared__ float KQ[kC][kC + 1];
   __shared__ unsigned long long kmask[kC], qmask[kC];
   __shared__ float sal[kC], sbe[kC];
-  __shared__ int wlcnt;
+  __shared__ int wlcnt, tot[2];
   const int chunk = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const int W = A.W, R = A.R, T = A.T, LIST = A.ml.list;
+  const int W = A.W, R = A.R, T = A.T;
   const int t0 = chunk * kC, L = min(kC, T - t0);
   const long long N = A.N;
   const size_t ut0 = (size_t)u * T + t0;
   uint32_t* blk = A.meta + ((size_t)u * A.nchunk + chunk) * A.ml.words;
+  uint32_t* la = blk + A.ml.la;
+  // this thread's occurrences i = tid + 256 k, all loads in flight at once
+  int ws[NO], rs[NO];
+  float wa[NO], ra[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int i = tid + 256 * k, t = i >> SH, j = i & (LIST - 1);
+    const bool okw = t < L && j < W, okr = t < L && j < R;
+    ws[k] = okw ? A.widx[(ut0 + t) * W + j] : -1;
+    wa[k] = okw ? A.wgt[(ut0 + t) * W + j] : 0.f;
+    rs[k] = okr ? A.ridx[(ut0 + t) * R + j] : -1;
+    ra[k] = okr ? A.rgt[(ut0 + t) * R + j] : 0.f;
+  }
   for (int i = tid; i < kBuckets; i += 256) {
     keys[i] = kFree;
     head[i] = -1;
@@ -125,11 +139,12 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     sbe[tid] = tid < L ? A.beta[ut0 + tid] : 0.f;
   }
   if (tid == 0) wlcnt = 0;
-  for (int i = tid; i < kC * W; i += 256) {
-    const bool ok = i < L * W;
-    const int s = ok ? A.widx[ut0 * W + i] : -1;
-    sn[i] = s >= 0 && s < N ? s : -1;
-    sa[i] = ok ? A.wgt[ut0 * W + i] : 0.f;
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int i = tid + 256 * k;
+    if (ws[k] < 0 || ws[k] >= N) ws[k] = -1;
+    sn[i] = ws[k];
+    sa[i] = wa[k];
   }
   __syncthreads();
   auto find = [&](uint32_t s, bool insert) -> int {
@@ -145,37 +160,42 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
       b = (b + 1) & (kBuckets - 1);
     }
   };
-  for (int i = tid; i < kC * W; i += 256) {
-    if (sn[i] < 0) {
+  int bk[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int i = tid + 256 * k;
+    bk[k] = -1;
+    if (ws[k] >= 0) {
+      bk[k] = find((uint32_t)ws[k], true);
+      snx[i] = (short)atomicExch(&head[bk[k]], i);
+    } else {
       snx[i] = -1;
-      sbk[i] = -1;
-      continue;
     }
-    const int b = find((uint32_t)sn[i], true);
-    sbk[i] = (short)b;
-    snx[i] = (short)atomicExch(&head[b], i);
+    sbk[i] = (short)bk[k];
   }
   __syncthreads();
   // write occurrences: couplings to earlier writers, gathered decay, write-back terms
-  for (int i = tid; i < kC * LIST; i += 256) {
-    const int t = i / LIST, j = i % LIST, oi = t * W + j;
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int i = tid + 256 * k, t = i >> SH;
     float gwv = 0.f, wcv = 0.f, gev = 0.f;
     int wbv = -1;
-    if (j < W && t < L && sn[oi] >= 0) {
-      const int b = sbk[oi];
+    if (ws[k] >= 0) {
+      const int b = bk[k];
+      const float a = wa[k];
       float before = 1.f, after = 1.f, all = 1.f;
       int others = 0;
-      for (int k = head[b]; k >= 0; k = snx[k]) {
-        const int tk = k / W;
+      for (int q = head[b]; q >= 0; q = snx[q]) {
+        const int tk = q >> SH;
         all *= sal[tk];
         if (tk < t) {
           before *= sal[tk];
           float between = 1.f;  // dec(n; tk, t)
           for (int l = head[b]; l >= 0; l = snx[l]) {
-            const int tl = l / W;
+            const int tl = l >> SH;
             if (tl > tk && tl < t) between *= sal[tl];
           }
-          atomicAdd(&KQ[t][tk], sal[t] * sa[oi] * between * sa[k]);
+          atomicAdd(&KQ[t][tk], sal[t] * a * between * sa[q]);
           atomicOr(&kmask[t], 1ull << tk);
           ++others;
         } else if (tk > t) {
@@ -183,20 +203,20 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
           others = -1000;  // not the last writer
         }
       }
-      gwv = sal[t] * sa[oi] * before;
-      wcv = sa[oi] * after;
+      gwv = sal[t] * a * before;
+      wcv = a * after;
       if (others >= 0) {  // the slot's last writer writes it back
         gev = all;
         const int start = others ? atomicAdd(&wlcnt, others) : 0;
         int e = start;
-        for (int k = head[b]; k >= 0; k = snx[k]) {
-          const int tk = k / W;
+        for (int q = head[b]; q >= 0; q = snx[q]) {
+          const int tk = q >> SH;
           if (tk >= t) continue;  // the same writers that were counted
-          float aft = 1.f;  // dec(n; tk, end)
+          float aft = 1.f;        // dec(n; tk, end)
           for (int l = head[b]; l >= 0; l = snx[l])
-            if (l / W > tk) aft *= sal[l / W];
-          blk[A.ml.wl + 2 * e] = (uint32_t)tk;
-          blk[A.ml.wl + 2 * e + 1] = __float_as_uint(sa[k] * aft);
+            if ((l >> SH) > tk) aft *= sal[l >> SH];
+          la[kLa0 + 2 * e] = (uint32_t)tk;
+          la[kLa0 + 2 * e + 1] = __float_as_uint(sa[q] * aft);
           ++e;
         }
         wbv = start << 8 | others;
@@ -208,67 +228,74 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     blk[A.ml.wb + i] = (uint32_t)wbv;
   }
   // read occurrences: couplings to the chunk's writers up to and including the token
-  for (int i = tid; i < kC * LIST; i += 256) {
-    const int t = i / LIST, j = i % LIST;
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int i = tid + 256 * k, t = i >> SH;
     float grv = 0.f;
-    if (j < R && t < L) {
-      const int s = A.ridx[(ut0 + t) * R + j];
-      const float w = A.rgt[(ut0 + t) * R + j];
-      if (s >= 0 && s < N) {
-        const int b = find((uint32_t)s, false);
-        float upto = 1.f;
-        if (b >= 0) {
-          for (int k = head[b]; k >= 0; k = snx[k]) {
-            const int tk = k / W;
-            if (tk > t) continue;
-            upto *= sal[tk];
-            float between = 1.f;  // dec(m; tk, t + 1)
-            for (int l = head[b]; l >= 0; l = snx[l]) {
-              const int tl = l / W;
-              if (tl > tk && tl <= t) between *= sal[tl];
-            }
-            atomicAdd(&KQ[tk][t], w * between * sa[k]);
-            atomicOr(&qmask[t], 1ull << tk);
+    const int s = rs[k];
+    if (s >= 0 && s < N) {
+      const float w = ra[k];
+      const int b = find((uint32_t)s, false);
+      float upto = 1.f;
+      if (b >= 0) {
+        for (int q = head[b]; q >= 0; q = snx[q]) {
+          const int tk = q >> SH;
+          if (tk > t) continue;
+          upto *= sal[tk];
+          float between = 1.f;  // dec(m; tk, t + 1)
+          for (int l = head[b]; l >= 0; l = snx[l]) {
+            const int tl = l >> SH;
+            if (tl > tk && tl <= t) between *= sal[tl];
           }
+          atomicAdd(&KQ[tk][t], w * between * sa[q]);
+          atomicOr(&qmask[t], 1ull << tk);
         }
-        grv = w * upto;
       }
+      grv = w * upto;
     }
     blk[A.ml.gr + i] = __float_as_uint(grv);
   }
   __syncthreads();
   // couplings out as row-sorted lists: wave 0 for K, wave 1 for Q (lane = row)
   const int wave = tid >> 6, lane = tid & 63;
+  unsigned long long m0 = 0;
+  int off = 0;
   if (wave < 2) {
-    const unsigned long long m0 = wave == 0 ? kmask[lane] : qmask[lane];
+    m0 = wave == 0 ? kmask[lane] : qmask[lane];
     const int cnt = __popcll(m0);
-    int off = cnt;  // inclusive scan over the 64 rows
+    off = cnt;  // inclusive scan over the 64 rows
     for (int s = 1; s < 64; s <<= 1) {
       const int x = __shfl_up(off, s, 64);
       if (lane >= s) off += x;
     }
-    const int total = __shfl(off, 63, 64);
+    if (lane == 63) tot[wave] = off;
     off -= cnt;
-    const size_t rp = wave == 0 ? A.ml.kp : A.ml.qp, ep = wave == 0 ? A.ml.ke : A.ml.qe;
-    blk[rp + lane] = (uint32_t)off;
-    if (lane == 63) blk[rp + 64] = (uint32_t)total;
+    const unsigned long long rows = __ballot(cnt > 0);
+    if (wave == 0 && lane == 0) {
+      blk[A.ml.hdr + 3] = (uint32_t)rows;
+      blk[A.ml.hdr + 4] = (uint32_t)(rows >> 32);
+    }
+  }
+  __syncthreads();
+  if (wave < 2) {
+    const int wn = wlcnt, kn = tot[0], qn = tot[1];
+    const int rp = wave == 0 ? 0 : 65, ep = kLa0 + 2 * wn + (wave == 0 ? 0 : 2 * kn);
+    la[rp + lane] = (uint32_t)off;
+    if (lane == 63) la[rp + 64] = (uint32_t)(wave == 0 ? kn : qn);
     unsigned long long m = m0;
     int e = off;
     while (m) {
       const int tk = __builtin_ctzll(m);
       m &= m - 1;
       const float c = wave == 0 ? sbe[lane] * KQ[lane][tk] : KQ[tk][lane];
-      blk[ep + 2 * e] = (uint32_t)tk;
-      blk[ep + 2 * e + 1] = __float_as_uint(c);
+      la[ep + 2 * e] = (uint32_t)tk;
+      la[ep + 2 * e + 1] = __float_as_uint(c);
       ++e;
     }
-    const unsigned long long rows = __ballot(cnt > 0);
-    if (lane == 0) {
-      blk[A.ml.hdr + wave] = (uint32_t)total;
-      if (wave == 0) {
-        blk[A.ml.hdr + 2] = (uint32_t)rows;
-        blk[A.ml.hdr + 3] = (uint32_t)(rows >> 32);
-      }
+    if (wave == 0 && lane == 0) {
+      blk[A.ml.hdr] = (uint32_t)wn;
+      blk[A.ml.hdr + 1] = (uint32_t)kn;
+      blk[A.ml.hdr + 2] = (uint32_t)qn;
     }
   }
 }
@@ -276,6 +303,36 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rs(const void* p, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+// A row piece of CBD dwords: buffer load and store in one instruction.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int CBD>
+__device__ __forceinline__ void piece_ld(rsrc_t rs, uint32_t off, uint32_t* w) {
+  if constexpr (CBD == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+  } else if constexpr (CBD == 2) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    w[0] = x.x, w[1] = x.y;
+  } else {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
+  }
+}
+template <int CBD>
+__device__ __forceinline__ void piece_st(rsrc_t rs, uint32_t off, const uint32_t* w) {
+  if constexpr (CBD == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, off, 0, 0);
+  } else if constexpr (CBD == 2) {
+    u32x2 x;
+    x.x = w[0], x.y = w[1];
+    __builtin_amdgcn_raw_buffer_store_b64(x, rs, off, 0, 0);
+  } else {
+    u32x4 x;
+    x.x = w[0], x.y = w[1], x.z = w[2], x.w = w[3];
+    __builtin_amdgcn_raw_buffer_store_b128(x, rs, off, 0, 0);
+  }
 }
 
 template <typename MemT>
@@ -293,217 +350,296 @@ struct RowWord<uint16_t> {
   __device__ static uint32_t pack(const float* x) { return pack_bf16x2(x[0], x[1]); }
 };
 
-template <typename InT, int CPL>
-__device__ __forceinline__ void load_v(const InT* p, float* x) {
-  if constexpr (sizeof(InT) == 2) {
-    if constexpr (CPL == 2) {
-      const uint32_t w = *(const uint32_t*)p;
-      x[0] = bf16lo(w);
-      x[1] = bf16hi(w);
-    } else {
-      x[0] = bf16_to_f32(*p);
-    }
+// N consecutive words from a 4N-byte aligned address (N = 2, 4 or 8)
+template <int N>
+__device__ __forceinline__ void ld_words(const uint32_t* p, uint32_t* w) {
+  if constexpr (N == 2) {
+    const uint2 x = *(const uint2*)p;
+    w[0] = x.x, w[1] = x.y;
   } else {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) x[c] = p[c];
+    for (int k = 0; k < N / 4; ++k) {
+      const uint4 x = ((const uint4*)p)[k];
+      w[4 * k] = x.x, w[4 * k + 1] = x.y, w[4 * k + 2] = x.z, w[4 * k + 3] = x.w;
+    }
   }
 }
 
-template <typename MemT, typename InT, int CBD, int LIST>
-__global__ void __launch_bounds__(64 * CBD) chunk_apply_kernel(ChunkArgs A) {
+template <typename InT>
+__device__ __forceinline__ float in_ld(const InT* p) {
+  if constexpr (sizeof(InT) == 2) return bf16_to_f32(*p);
+  else return *p;
+}
+
+#ifndef SDM_CHUNK_CFG
+#define SDM_CHUNK_CFG 0  // lane map of the apply kernel: 0 picks by shape
+#endif
+
+// Phase 2. A workgroup owns a block of NQ * QD row dwords of one unit; the lanes of a token
+// are (occurrence group g < G, quad q < NQ): lane (g, q) gathers dwords [q QD, q QD + QD) of
+// the block for the token's occurrences [g OPL, g OPL + OPL), so the NQ lanes of one
+// occurrence read NQ * QD contiguous dwords. P and O0 are summed over the G groups. With PRE
+// the next chunk's slots are loaded while the current chunk runs (registers for latency).
+template <typename MemT, typename InT, int QD, int NQ, int G, bool PRE, int LIST>
+__global__ void __launch_bounds__(64 * NQ * G) chunk_apply_kernel(ChunkArgs A) {
   using RW = RowWord<MemT>;
+  constexpr int LPT = NQ * G;            // lanes per token
+  constexpr int NT = 64 * LPT;
+  constexpr int OPL = LIST / G;          // occurrences per lane, write and read each
   constexpr int CPL = RW::kCols;
-  constexpr int NCOL = CBD * CPL;
-  constexpr int NT = 64 * CBD;
-  constexpr int PF = (2 * kC * LIST + NT - 1) / NT;  // prefetched slot indices per thread
-  __shared__ float D[kC][NCOL + 1];                  // delta of the chunk's tokens
-  __shared__ int sidx[2 * kC * LIST];                // the chunk's write and read slots, [kC][LIST] each
+  constexpr int CBD = QD * NQ;           // row dwords per workgroup
+  constexpr int NCOL = CBD * CPL;        // table columns per workgroup
+  constexpr int QC = QD * CPL;           // columns of one lane's piece
+  constexpr int CPLN = QC >= G ? QC / G : 1;  // columns of delta and o per lane
+  constexpr int NLA = kLa0 + 2 * (kC * LIST + kKMax + kQMax);
+  static_assert(NCOL <= 64 && OPL >= 2 && LPT <= 64, "lane map");
+  __shared__ float D[kC][NCOL];          // delta of the chunk's tokens
+  __shared__ uint32_t lst[NLA];          // the chunk's list area
   // blockIdx -> (unit, column block) with all column blocks of a unit in one L2 domain
   const int xcd = blockIdx.x % kXcd, y = blockIdx.x / kXcd;
   const int p = y % A.ncb, u = (y / A.ncb) * kXcd + xcd;
   if (u >= A.U) return;
-  const int tid = threadIdx.x, t = tid / CBD, d = tid % CBD;
+  const int tid = threadIdx.x, t = tid / LPT, g = (tid % LPT) / NQ, q = tid % NQ;
   const int T = A.T, W = A.W, R = A.R, d_v = A.d_v;
-  const int rowdw = d_v / CPL, dw = p * CBD + d;  // rowdw is a multiple of CBD
+  const int rowdw = d_v / CPL;  // a multiple of CBD
   const long long N = A.N;
   const rsrc_t rM = make_rs((const char*)A.M + (size_t)u * N * d_v * sizeof(MemT), (size_t)N * d_v * sizeof(MemT));
-  const InT* v = (const InT*)A.v + (size_t)u * T * d_v + (size_t)dw * CPL;
-  float* o = A.o + (size_t)u * T * d_v + (size_t)dw * CPL;
+  const int qc0 = q * QC;                          // this lane's first column inside the block
+  const int lc0 = qc0 + g * CPLN;                  // its first column of delta and o
+  const bool cl = g * CPLN < QC;
+  const InT* v = (const InT*)A.v + (size_t)u * T * d_v + p * NCOL + lc0;
+  float* o = A.o + (size_t)u * T * d_v + p * NCOL + lc0;
   const int32_t* widx = A.widx + (size_t)u * T * W;
   const int32_t* ridx = A.ridx + (size_t)u * T * R;
   const float* beta = A.beta + (size_t)u * T;
   const uint32_t* meta = A.meta + (size_t)u * A.nchunk * A.ml.words;
   const MetaLayout ml = A.ml;
+  const uint32_t pc = (uint32_t)(p * CBD + q * QD) * 4u;  // byte offset of the piece inside a row
 
-  // slot lists of chunk c: entry e < kC*LIST is a write slot, the rest read slots; -1 past the list
-  auto fetch_idx = [&](int c, int* pf) {
-    const int t0 = c * kC, L = min(kC, T - t0);
+  // this lane's slots of chunk c: occurrences j = g OPL + i
+  auto fetch = [&](int c, int* sw, int* sr) {
+    const int tt = c * kC + t;
+    const bool ok = tt < T;
 #pragma unroll
-    for (int k = 0; k < PF; ++k) {
-      const int e = tid + k * NT;
-      const int rd = e >= kC * LIST, f = rd ? e - kC * LIST : e;
-      const int tt = f / LIST, j = f % LIST, n = rd ? R : W;
-      int s = -1;
-      if (e < 2 * kC * LIST && tt < L && j < n) s = rd ? ridx[(size_t)(t0 + tt) * R + j] : widx[(size_t)(t0 + tt) * W + j];
-      pf[k] = s;
+    for (int i = 0; i < OPL; ++i) {
+      const int j = g * OPL + i;
+      sw[i] = ok && j < W ? widx[(size_t)tt * W + j] : -1;
+      sr[i] = ok && j < R ? ridx[(size_t)tt * R + j] : -1;
     }
   };
-  auto store_idx = [&](const int* pf) {
-#pragma unroll
-    for (int k = 0; k < PF; ++k)
-      if (tid + k * NT < 2 * kC * LIST) sidx[tid + k * NT] = pf[k];
-  };
-  int pf[PF];
-  fetch_idx(0, pf);
-  store_idx(pf);
-  __syncthreads();
+  int sw[OPL], sr[OPL];
+  if constexpr (PRE) fetch(0, sw, sr);
+  uint32_t h0 = meta[ml.hdr], h1 = meta[ml.hdr + 1], h2 = meta[ml.hdr + 2], h3 = meta[ml.hdr + 3],
+           h4 = meta[ml.hdr + 4];
 
   for (int chunk = 0; chunk < A.nchunk; ++chunk) {
-    const int t0 = chunk * kC, L = min(kC, T - t0);
-    const bool tv = t < L;
+    const int t0 = chunk * kC;
+    const bool tv = t0 + t < T;
     const uint32_t* mb = meta + (size_t)chunk * ml.words;
+    const int wn = (int)h0, kn = (int)h1, qn = (int)h2;
+    const unsigned long long krows = (unsigned long long)h3 | (unsigned long long)h4 << 32;
+    const int nla = kLa0 + 2 * (wn + kn + qn);
+    if constexpr (!PRE) fetch(chunk, sw, sr);
+    // the list area: the first 2 NT words through registers, alongside the row traffic
+    uint32_t lr0 = 0, lr1 = 0;
+    if (tid < nla) lr0 = mb[ml.la + tid];
+    if (tid + NT < nla) lr1 = mb[ml.la + tid + NT];
     // byte offsets of this lane's row pieces (kNoneByte: no row; loads read 0, stores drop)
-    uint32_t wo[LIST], ro[LIST];
+    uint32_t wo[OPL], ro[OPL];
 #pragma unroll
-    for (int j = 0; j < LIST; ++j) {
-      const int n = sidx[t * LIST + j], m = sidx[kC * LIST + t * LIST + j];
-      wo[j] = n >= 0 && n < N ? ((uint32_t)n * (uint32_t)rowdw + (uint32_t)dw) * 4u : kNoneByte;
-      ro[j] = m >= 0 && m < N ? ((uint32_t)m * (uint32_t)rowdw + (uint32_t)dw) * 4u : kNoneByte;
+    for (int i = 0; i < OPL; ++i) {
+      wo[i] = sw[i] >= 0 && sw[i] < N ? (uint32_t)sw[i] * (uint32_t)rowdw * 4u + pc : kNoneByte;
+      ro[i] = sr[i] >= 0 && sr[i] < N ? (uint32_t)sr[i] * (uint32_t)rowdw * 4u + pc : kNoneByte;
     }
-    if (chunk + 1 < A.nchunk) fetch_idx(chunk + 1, pf);
-    uint32_t mw[LIST], mr[LIST];
+    uint32_t mw[OPL][QD], mr[OPL][QD];
 #pragma unroll
-    for (int j = 0; j < LIST; ++j) mw[j] = __builtin_amdgcn_raw_buffer_load_b32(rM, wo[j], 0, 0);
+    for (int i = 0; i < OPL; ++i) piece_ld<QD>(rM, wo[i], mw[i]);
 #pragma unroll
-    for (int j = 0; j < LIST; ++j) mr[j] = __builtin_amdgcn_raw_buffer_load_b32(rM, ro[j], 0, 0);
-    // per-occurrence coefficients of this token (zeros past the lists and past the chunk)
-    float gw[LIST], gr[LIST], wc[LIST], ge[LIST];
-    int wb[LIST];
-    const uint4* q4 = (const uint4*)(mb + (size_t)t * LIST);
-    const size_t occ4 = (size_t)kC * LIST / 4;
+    for (int i = 0; i < OPL; ++i) piece_ld<QD>(rM, ro[i], mr[i]);
+    // gathered coefficients (zeros past the lists and past the chunk)
+    const uint32_t* mt = mb + (size_t)t * LIST + g * OPL;
+    float gw[OPL], gr[OPL];
+    {
+      uint32_t a[OPL], b[OPL];
+      ld_words<OPL>(mt + ml.gw, a);
+      ld_words<OPL>(mt + ml.gr, b);
 #pragma unroll
-    for (int j4 = 0; j4 < LIST / 4; ++j4) {
-      const uint4 a = q4[ml.gw / 4 + j4], b = q4[ml.gr / 4 + j4], c = q4[ml.wc / 4 + j4], e = q4[ml.ge / 4 + j4],
-                  f = q4[ml.wb / 4 + j4];
-      gw[4 * j4] = __uint_as_float(a.x), gw[4 * j4 + 1] = __uint_as_float(a.y);
-      gw[4 * j4 + 2] = __uint_as_float(a.z), gw[4 * j4 + 3] = __uint_as_float(a.w);
-      gr[4 * j4] = __uint_as_float(b.x), gr[4 * j4 + 1] = __uint_as_float(b.y);
-      gr[4 * j4 + 2] = __uint_as_float(b.z), gr[4 * j4 + 3] = __uint_as_float(b.w);
-      wc[4 * j4] = __uint_as_float(c.x), wc[4 * j4 + 1] = __uint_as_float(c.y);
-      wc[4 * j4 + 2] = __uint_as_float(c.z), wc[4 * j4 + 3] = __uint_as_float(c.w);
-      ge[4 * j4] = __uint_as_float(e.x), ge[4 * j4 + 1] = __uint_as_float(e.y);
-      ge[4 * j4 + 2] = __uint_as_float(e.z), ge[4 * j4 + 3] = __uint_as_float(e.w);
-      wb[4 * j4] = (int)f.x, wb[4 * j4 + 1] = (int)f.y, wb[4 * j4 + 2] = (int)f.z, wb[4 * j4 + 3] = (int)f.w;
+      for (int i = 0; i < OPL; ++i) gw[i] = __uint_as_float(a[i]), gr[i] = __uint_as_float(b[i]);
     }
-    (void)occ4;
-    const int qs = (int)mb[ml.qp + t], qe = (int)mb[ml.qp + t + 1];
-    const int kn = (int)mb[ml.hdr];
-    float vv[CPL];
+    float vv[CPLN], be = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) vv[c] = 0.f;
-    float be = 0.f;
-    if (tv) {
-      load_v<InT, CPL>(v + (size_t)(t0 + t) * d_v, vv);
+    for (int c = 0; c < CPLN; ++c) vv[c] = 0.f;
+    if (tv && cl) {
+#pragma unroll
+      for (int c = 0; c < CPLN; ++c) vv[c] = in_ld<InT>(v + (size_t)(t0 + t) * d_v + c);
       be = beta[t0 + t];
     }
-    // P and O0 from the chunk-start rows
-    float P[CPL], O0[CPL];
+    // P and O0 from the chunk-start rows: partial sums over this lane's occurrences, then the groups
+    float P[QC], O0[QC];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) P[c] = O0[c] = 0.f;
+    for (int c = 0; c < QC; ++c) P[c] = O0[c] = 0.f;
 #pragma unroll
-    for (int j = 0; j < LIST; ++j) {
-      float x[CPL], y[CPL];
-      RW::unpack(mw[j], x);
-      RW::unpack(mr[j], y);
+    for (int i = 0; i < OPL; ++i) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        P[c] = fmaf(gw[j], x[c], P[c]);
-        O0[c] = fmaf(gr[j], y[c], O0[c]);
+      for (int k = 0; k < QD; ++k) {
+        float x[CPL], z[CPL];
+        RW::unpack(mw[i][k], x);
+        RW::unpack(mr[i][k], z);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          P[k * CPL + c] = fmaf(gw[i], x[c], P[k * CPL + c]);
+          O0[k * CPL + c] = fmaf(gr[i], z[c], O0[k * CPL + c]);
+        }
       }
     }
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) D[t][d * CPL + c] = be * (vv[c] - P[c]);
+    for (int c = 0; c < QC; ++c) {
+#pragma unroll
+      for (int s = NQ; s < LPT; s <<= 1) {
+        P[c] += __shfl_xor(P[c], s, 64);
+        O0[c] += __shfl_xor(O0[c], s, 64);
+      }
+    }
+    // this lane's columns g CPLN + cc of its piece, picked by selects (no indexing by a lane value)
+    float ol[CPLN];
+#pragma unroll
+    for (int cc = 0; cc < CPLN; ++cc) {
+      float ps = 0.f, os = 0.f;
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+        if (c == g * CPLN + cc) ps = P[c], os = O0[c];
+      ol[cc] = os;
+      if (cl) D[t][lc0 + cc] = be * (vv[cc] - ps);
+    }
+    // write-back coefficients, the next chunk's slots and header: in flight during the solve
+    float wc[OPL], ge[OPL];
+    int wb[OPL];
+    {
+      uint32_t a[OPL], b[OPL], c[OPL];
+      ld_words<OPL>(mt + ml.wc, a);
+      ld_words<OPL>(mt + ml.ge, b);
+      ld_words<OPL>(mt + ml.wb, c);
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) wc[i] = __uint_as_float(a[i]), ge[i] = __uint_as_float(b[i]), wb[i] = (int)c[i];
+    }
+    int nw_[OPL], nr_[OPL];
+    if (chunk + 1 < A.nchunk) {
+      if constexpr (PRE) fetch(chunk + 1, nw_, nr_);
+      const uint32_t* hn = mb + ml.words + ml.hdr;
+      h0 = hn[0], h1 = hn[1], h2 = hn[2], h3 = hn[3], h4 = hn[4];
+    }
+    lst[tid] = lr0;  // kLa0 > 0 words: always in range
+    if (tid + NT < NLA) lst[tid + NT] = lr1;
+    for (int i = tid + 2 * NT; i < nla; i += NT) lst[i] = mb[ml.la + i];
     __syncthreads();
     // forward sweep over the K list: delta_t -= beta_t K[t][tau] delta_tau, rows in order
     if (kn > 0) {
       if (tid < NCOL) {
-        unsigned long long rows = (unsigned long long)mb[ml.hdr + 2] | (unsigned long long)mb[ml.hdr + 3] << 32;
+        const uint32_t* ke = lst + kLa0 + 2 * wn;
+        unsigned long long rows = krows;
         while (rows) {
           const int r = __builtin_ctzll(rows);
           rows &= rows - 1;
-          const int e0 = (int)mb[ml.kp + r], e1 = (int)mb[ml.kp + r + 1];
           float acc = D[r][tid];
-          for (int e = e0; e < e1; ++e) acc = fmaf(-__uint_as_float(mb[ml.ke + 2 * e + 1]), D[mb[ml.ke + 2 * e]][tid], acc);
+          for (int e = (int)lst[r]; e < (int)lst[r + 1]; ++e)
+            acc = fmaf(-__uint_as_float(ke[2 * e + 1]), D[ke[2 * e]][tid], acc);
           D[r][tid] = acc;
         }
       }
       __syncthreads();
     }
     // o = O0 + Q delta
-    float dt[CPL];
+    if (tv && cl) {
+      const uint32_t* qe = lst + kLa0 + 2 * (wn + kn);
+      for (int e = (int)lst[65 + t]; e < (int)lst[66 + t]; ++e) {
+        const int tk = (int)qe[2 * e];
+        const float qv = __uint_as_float(qe[2 * e + 1]);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) dt[c] = D[t][d * CPL + c];
-    if (tv) {
-      for (int e = qs; e < qe; ++e) {
-        const int tk = (int)mb[ml.qe + 2 * e];
-        const float q = __uint_as_float(mb[ml.qe + 2 * e + 1]);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) O0[c] = fmaf(q, D[tk][d * CPL + c], O0[c]);
+        for (int c = 0; c < CPLN; ++c) ol[c] = fmaf(qv, D[tk][lc0 + c], ol[c]);
       }
-      if constexpr (CPL == 2) {
-        *(float2*)(o + (size_t)(t0 + t) * d_v) = make_float2(O0[0], O0[1]);
+      float* op = o + (size_t)(t0 + t) * d_v;
+      if constexpr (CPLN % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < CPLN; c += 4) *(float4*)(op + c) = make_float4(ol[c], ol[c + 1], ol[c + 2], ol[c + 3]);
+      } else if constexpr (CPLN == 2) {
+        *(float2*)op = make_float2(ol[0], ol[1]);
       } else {
-        o[(size_t)(t0 + t) * d_v] = O0[0];
+#pragma unroll
+        for (int c = 0; c < CPLN; ++c) op[c] = ol[c];
       }
     }
-    // each slot's last writer writes its row back once
+    // each slot's last writer writes its row piece back once
+    float dt[QC];
 #pragma unroll
-    for (int j = 0; j < LIST; ++j) {
-      if (wb[j] < 0) continue;
-      float x[CPL], y[CPL];
-      RW::unpack(mw[j], x);
+    for (int c = 0; c < QC; ++c) dt[c] = D[t][qc0 + c];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) y[c] = fmaf(ge[j], x[c], wc[j] * dt[c]);
-      const int e0 = wb[j] >> 8, e1 = e0 + (wb[j] & 255);
+    for (int i = 0; i < OPL; ++i) {
+      if (wb[i] < 0) continue;
+      float yv[QC];
+#pragma unroll
+      for (int k = 0; k < QD; ++k) {
+        float x[CPL];
+        RW::unpack(mw[i][k], x);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) yv[k * CPL + c] = fmaf(ge[i], x[c], wc[i] * dt[k * CPL + c]);
+      }
+      const int e0 = wb[i] >> 8, e1 = e0 + (wb[i] & 255);
       for (int e = e0; e < e1; ++e) {
-        const int tk = (int)mb[ml.wl + 2 * e];
-        const float a = __uint_as_float(mb[ml.wl + 2 * e + 1]);
+        const int tk = (int)lst[kLa0 + 2 * e];
+        const float a = __uint_as_float(lst[kLa0 + 2 * e + 1]);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) y[c] = fmaf(a, D[tk][d * CPL + c], y[c]);
+        for (int c = 0; c < QC; ++c) yv[c] = fmaf(a, D[tk][qc0 + c], yv[c]);
       }
-      __builtin_amdgcn_raw_buffer_store_b32(RW::pack(y), rM, wo[j], 0, 0);
+      uint32_t pw[QD];
+#pragma unroll
+      for (int k = 0; k < QD; ++k) pw[k] = RW::pack(yv + k * CPL);
+      piece_st<QD>(rM, wo[i], pw);
     }
-    // every lane has read this chunk's slot lists (before the first barrier): the next ones go in
-    if (chunk + 1 < A.nchunk) store_idx(pf);
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) sw[i] = nw_[i], sr[i] = nr_[i];
+    }
     // the next chunk's gathers read these rows: stores complete, then the barrier
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 }
 
-template <typename MemT, typename InT, int CBD>
-hipError_t launch_apply(const ChunkArgs& A, int list, hipStream_t st) {
+template <typename MemT, typename InT, int QD, int NQ, int G, bool PRE>
+hipError_t launch_apply(ChunkArgs& A, int list, hipStream_t st) {
+  constexpr int CPL = RowWord<MemT>::kCols;
+  A.ncb = A.d_v / CPL / (QD * NQ);
   const int wgs = (A.U + kXcd - 1) / kXcd * kXcd * A.ncb;
-  const dim3 g((unsigned)wgs), b(64 * CBD);
-  if (list == 8) hipLaunchKernelGGL((chunk_apply_kernel<MemT, InT, CBD, 8>), g, b, 0, st, A);
-  else if (list == 16) hipLaunchKernelGGL((chunk_apply_kernel<MemT, InT, CBD, 16>), g, b, 0, st, A);
-  else hipLaunchKernelGGL((chunk_apply_kernel<MemT, InT, CBD, 32>), g, b, 0, st, A);
+  const dim3 gr((unsigned)wgs), b(64 * NQ * G);
+  if (list == 8) hipLaunchKernelGGL((chunk_apply_kernel<MemT, InT, QD, NQ, G, PRE, 8>), gr, b, 0, st, A);
+  else if (list == 16) hipLaunchKernelGGL((chunk_apply_kernel<MemT, InT, QD, NQ, G, PRE, 16>), gr, b, 0, st, A);
+  else hipLaunchKernelGGL((chunk_apply_kernel<MemT, InT, QD, NQ, G, PRE, 32>), gr, b, 0, st, A);
   return hipGetLastError();
 }
 
 template <typename MemT, typename InT>
-hipError_t launch_apply_cbd(ChunkArgs& A, int list, hipStream_t st) {
+hipError_t launch_apply_cfg(ChunkArgs& A, int list, hipStream_t st) {
   constexpr int CPL = RowWord<MemT>::kCols;
-  const int rowdw = A.d_v / CPL;
-  // widest column block that still gives every compute unit a workgroup
-  const int cus = device_cus();
+  const int rowdw = A.d_v / CPL;  // a multiple of 4
   const long long ug = (A.U + kXcd - 1) / kXcd * kXcd;
-  if (ug * (rowdw / 4) >= cus) {
-    A.ncb = rowdw / 4;
-    return launch_apply<MemT, InT, 4>(A, list, st);
+  const int cus = device_cus();
+  int cfg = SDM_CHUNK_CFG;
+  if (cfg == 0) {
+    // Units of one L2 domain stream their chunks' rows through it together. With one unit
+    // per domain, narrow pieces keep every compute unit busy and the rows are reused from
+    // L2; with more, each workgroup reads whole 64-byte sectors (16-dword pieces).
+    if (A.U > kXcd && rowdw % 16 == 0 && ug * (rowdw / 16) >= cus) cfg = 1;
+    else if (ug * (rowdw / 4) >= cus) cfg = 2;
+    else cfg = ug * (rowdw / 2) >= cus ? 3 : 4;
   }
-  A.ncb = rowdw / 2;
-  return launch_apply<MemT, InT, 2>(A, list, st);
+  switch (cfg) {
+    case 1: return launch_apply<MemT, InT, 4, 4, 2, false>(A, list, st);  // 16 dwords, 512 lanes
+    case 2: return launch_apply<MemT, InT, 4, 1, 4, true>(A, list, st);   // 4 dwords
+    case 3: return launch_apply<MemT, InT, 2, 1, 4, true>(A, list, st);   // 2 dwords
+    case 5: return launch_apply<MemT, InT, 4, 4, 4, false>(A, list, st);  // 16 dwords, 1024 lanes
+    case 6: return launch_apply<MemT, InT, 4, 2, 4, true>(A, list, st);   // 8 dwords, 512 lanes
+    default: return launch_apply<MemT, InT, 1, 1, 4, true>(A, list, st);  // 1 dword
+  }
 }
 
 }  // namespace
@@ -543,15 +679,18 @@ hipError_t launch_chunked(const sdm_shape& S, const int32_t* widx, const float* 
   A.meta = (uint32_t*)((char*)ws + 256);
   A.ncb = 0;
   if (A.U == 0 || A.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)A.nchunk, (unsigned)A.U), dim3(256), 0, stream, A);
+  const int list = A.ml.list;
+  const dim3 pg((unsigned)A.nchunk, (unsigned)A.U);
+  if (list == 8) hipLaunchKernelGGL(chunk_prep_kernel<8>, pg, dim3(256), 0, stream, A);
+  else if (list == 16) hipLaunchKernelGGL(chunk_prep_kernel<16>, pg, dim3(256), 0, stream, A);
+  else hipLaunchKernelGGL(chunk_prep_kernel<32>, pg, dim3(256), 0, stream, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int list = A.ml.list;
   const bool mb = S.mem_dtype == SDM_BF16, ib = S.in_dtype == SDM_BF16;
-  if (mb && ib) return launch_apply_cbd<uint16_t, uint16_t>(A, list, stream);
-  if (mb) return launch_apply_cbd<uint16_t, float>(A, list, stream);
-  if (ib) return launch_apply_cbd<float, uint16_t>(A, list, stream);
-  return launch_apply_cbd<float, float>(A, list, stream);
+  if (mb && ib) return launch_apply_cfg<uint16_t, uint16_t>(A, list, stream);
+  if (mb) return launch_apply_cfg<uint16_t, float>(A, list, stream);
+  if (ib) return launch_apply_cfg<float, uint16_t>(A, list, stream);
+  return launch_apply_cfg<float, float>(A, list, stream);
 }
 
 }  // namespace sdm

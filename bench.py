@@ -23,7 +23,11 @@ queries, from a synthetic output gradient. ``roofline`` then describes the recur
 backward call (preparation pass and reverse walk) and ``value`` counts layer tokens per
 training step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay | --backward]
+With --chunked the recurrence runs in its chunkwise two-phase form (64-token chunks: the
+preparation kernel over every chunk in parallel, then the apply kernel over the chunks in
+order); ``roofline`` describes that call, priced with the recurrence's algorithmic bytes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay | --backward | --chunked]
 """
 from __future__ import annotations
 
@@ -73,29 +77,31 @@ def backward_bytes_per_token_head(sh: SI.Shape) -> int:
 
 
 RECURRENCE_SOURCES = ("sdm_dataflow.hip", "sdm_device.hpp")
+CHUNKED_SOURCES = ("sdm_chunked.hip", "sdm_device.hpp")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources of the recurrence kernels (dependency pass and pipeline)."""
+def kernel_source_hash(kind: str = "recurrence") -> str:
+    """Hash of the sources of the recurrence kernels (dependency pass and pipeline), or with
+    kind="chunked" of the chunkwise kernels (preparation and apply)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc")
-    for f in RECURRENCE_SOURCES:
+    for f in (CHUNKED_SOURCES if kind == "chunked" else RECURRENCE_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per recurrence launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_recurrence_{workload}.json")
+def traffic_from_profile(workload: str, kind: str = "recurrence"):
+    """HBM bytes per recurrence launch (kind "recurrence" or "chunked") from the committed
+    counter summary, if it was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -154,9 +160,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decay", action="store_true", help="whole-table decay variant")
     ap.add_argument("--backward", action="store_true", help="training step: forward with log and backward")
+    ap.add_argument("--chunked", action="store_true", help="forward with the chunkwise two-phase recurrence")
     args = ap.parse_args()
-    if args.decay and args.backward:
-        print("--decay and --backward are separate modes", file=sys.stderr)
+    if args.decay + args.backward + args.chunked > 1:
+        print("--decay, --backward and --chunked are separate modes", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -169,7 +176,7 @@ def main():
     sh = SI.WORKLOADS[args.workload]
     if sh.T == 1:
         return bench_decode(args, sh)
-    if args.decay or args.backward:
+    if args.decay or args.backward or args.chunked:
         args.no_cpu_baseline = True  # the oracle baseline times the default forward
     log(f"[bench] generating {sh.name} inputs")
     t0 = time.time()
@@ -205,6 +212,8 @@ def main():
     ridx = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.int32, device="cuda")
     rgt = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.chunked:
+        cws = torch.empty(S.workspace_bytes_chunked(shape), dtype=torch.uint8, device="cuda")
     if args.backward:
         s_ = int(round(sh.N ** 0.5))
         xlog = torch.empty((sh.B, sh.H, sh.T, sh.W, sh.d_v), dtype=mdt, device="cuda")
@@ -249,6 +258,8 @@ def main():
             ev[0].record(stream)
         if args.decay:
             S.recurrent_decay(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, lam, lrun, o, ws)
+        elif args.chunked:
+            S.recurrent_chunked(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, cws)
         else:
             S.recurrent(shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws)
         if ev is not None:
@@ -278,7 +289,8 @@ def main():
     if args.backward:
         assert S.workspace_error(bws) == 0, "a workgroup of the backward gave up waiting"
 
-    traffic = None if (args.decay or args.backward) else traffic_from_profile(sh.name)
+    traffic = (None if (args.decay or args.backward) else
+               traffic_from_profile(sh.name, "chunked" if args.chunked else "recurrence"))
     out = {
         "metric": (METRIC_BACKWARD if args.backward else METRIC),
         "value": value,
@@ -295,10 +307,12 @@ def main():
         "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": sh.T, "N": sh.N, "d_k": sh.d_k, "d_v": sh.d_v,
                    "kappa": sh.kappa, "W": sh.W, "R": sh.R, "in_dtype": sh.in_dtype, "mem_dtype": sh.mem_dtype,
                    "arith": "fp32", **({"decay": "whole table"} if args.decay else {}),
-                   **({"step": "forward with log + backward"} if args.backward else {})},
+                   **({"step": "forward with log + backward"} if args.backward else {}),
+                   **({"recurrence": "chunkwise two-phase, 64-token chunks"} if args.chunked else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "recurrence backward" if args.backward else "recurrence",
+                     "kernel": ("recurrence backward" if args.backward else
+                                "chunkwise recurrence (prep + apply)" if args.chunked else "recurrence"),
                      "ms_per_launch": rec_ms, "bytes_per_launch": launch_bytes},
         "cpu_baseline": cpu,
     }

@@ -41,6 +41,7 @@ constexpr int kC = 64;                   // tokens per chunk
 constexpr int kMaxList = 32;             // W, R <= 32 on this path
 constexpr int kBuckets = 4096;           // LDS hash: at most 2048 distinct slots, at most half full
 constexpr uint32_t kFree = 0xFFFFFFFFu;
+constexpr int kFilterWords = 2048;       // 64K-bit filter of the chunk's written slots
 constexpr int kKMax = kC * (kC - 1) / 2;  // distinct (t, tau < t) pairs
 constexpr int kQMax = kC * (kC + 1) / 2;  // distinct (t, tau <= t) pairs
 constexpr int kXcd = 8;                  // workgroups are dealt round-robin to this many L2 domains
@@ -91,6 +92,7 @@ struct ChunkArgs {
 };
 
 __device__ __forceinline__ uint32_t chunk_hash(uint32_t s) { return (s * 2654435761u) >> 20; }  // 12 bits
+__device__ __forceinline__ uint32_t filter_bit(uint32_t s) { return (s * 0x9E3779B1u) >> 16; }  // 16 bits
 
 template <int LIST>
 __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
@@ -107,6 +109,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
   __shared__ float KQ[kC][kC + 1];
   __shared__ unsigned long long kmask[kC], qmask[kC];
   __shared__ float sal[kC], sbe[kC];
+  __shared__ uint32_t filt[kFilterWords];  // a slot whose bit is clear is not written in the chunk
   __shared__ int wlcnt, tot[2];
   const int chunk = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int W = A.W, R = A.R, T = A.T;
@@ -131,6 +134,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     keys[i] = kFree;
     head[i] = -1;
   }
+  for (int i = tid; i < kFilterWords; i += 256) filt[i] = 0u;
   for (int i = tid; i < kC * (kC + 1); i += 256) (&KQ[0][0])[i] = 0.f;
   if (tid < kC) {
     kmask[tid] = 0ull;
@@ -147,40 +151,69 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     sa[i] = wa[k];
   }
   __syncthreads();
-  auto find = [&](uint32_t s, bool insert) -> int {
+  auto find = [&](uint32_t s) -> int {  // bucket of a slot written in the chunk, or -1
     uint32_t b = chunk_hash(s);
     while (true) {
       const uint32_t k = keys[b];
       if (k == s) return (int)b;
-      if (k == kFree) {
-        if (!insert) return -1;
-        const uint32_t old = atomicCAS(&keys[b], kFree, s);
-        if (old == kFree || old == s) return (int)b;
-      }
+      if (k == kFree) return -1;
       b = (b + 1) & (kBuckets - 1);
     }
   };
+  auto insert = [&](uint32_t s) -> int {  // claim (or find) the slot's bucket
+    uint32_t b = chunk_hash(s);
+    while (true) {
+      const uint32_t old = atomicCAS(&keys[b], kFree, s);
+      if (old == kFree || old == s) return (int)b;
+      b = (b + 1) & (kBuckets - 1);
+    }
+  };
+  // Each stage issues this thread's occurrences together (one LDS round trip per stage):
+  // claim the home bucket, then (rarely) probe on, then link into the slot's list.
   int bk[NO];
+  uint32_t old[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    bk[k] = ws[k] >= 0 ? (int)chunk_hash((uint32_t)ws[k]) : -1;
+    old[k] = ws[k] >= 0 ? atomicCAS(&keys[bk[k]], kFree, (uint32_t)ws[k]) : kFree;
+  }
+#pragma unroll
+  for (int k = 0; k < NO; ++k)
+    if (ws[k] >= 0 && old[k] != kFree && old[k] != (uint32_t)ws[k])
+      bk[k] = insert((uint32_t)ws[k]);  // the home bucket holds another slot
+  int nx[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) nx[k] = ws[k] >= 0 ? atomicExch(&head[bk[k]], tid + 256 * k) : -1;
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
     const int i = tid + 256 * k;
-    bk[k] = -1;
-    if (ws[k] >= 0) {
-      bk[k] = find((uint32_t)ws[k], true);
-      snx[i] = (short)atomicExch(&head[bk[k]], i);
-    } else {
-      snx[i] = -1;
-    }
+    snx[i] = (short)nx[k];
     sbk[i] = (short)bk[k];
+    if (ws[k] >= 0) {
+      const uint32_t fb = filter_bit((uint32_t)ws[k]);
+      atomicOr(&filt[fb >> 5], 1u << (fb & 31));
+    }
   }
   __syncthreads();
   // write occurrences: couplings to earlier writers, gathered decay, write-back terms
+  int hd[NO];
+  float st[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    hd[k] = ws[k] >= 0 ? head[bk[k]] : -1;
+    st[k] = sal[(tid + 256 * k) >> SH];
+  }
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
     const int i = tid + 256 * k, t = i >> SH;
     float gwv = 0.f, wcv = 0.f, gev = 0.f;
     int wbv = -1;
-    if (ws[k] >= 0) {
+    if (ws[k] >= 0 && hd[k] == i && nx[k] < 0) {  // the slot's only writer in the chunk
+      gwv = st[k] * wa[k];
+      wcv = wa[k];
+      gev = st[k];
+      wbv = 0;
+    } else if (ws[k] >= 0) {
       const int b = bk[k];
       const float a = wa[k];
       float before = 1.f, after = 1.f, all = 1.f;
@@ -228,14 +261,22 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     blk[A.ml.wb + i] = (uint32_t)wbv;
   }
   // read occurrences: couplings to the chunk's writers up to and including the token
+  uint32_t fw[NO];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const uint32_t fb = filter_bit((uint32_t)rs[k]);
+    fw[k] = (filt[fb >> 5] >> (fb & 31)) & 1u;
+  }
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
     const int i = tid + 256 * k, t = i >> SH;
     float grv = 0.f;
     const int s = rs[k];
-    if (s >= 0 && s < N) {
+    if (s >= 0 && s < N && fw[k] == 0u) {
+      grv = ra[k];  // the slot is not written in the chunk
+    } else if (s >= 0 && s < N) {
       const float w = ra[k];
-      const int b = find((uint32_t)s, false);
+      const int b = find((uint32_t)s);
       float upto = 1.f;
       if (b >= 0) {
         for (int q = head[b]; q >= 0; q = snx[q]) {

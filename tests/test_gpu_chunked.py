@@ -1,8 +1,10 @@
 """Chunkwise two-phase recurrence on the GPU against the oracle's chunkwise form (same
 chunk length, same rounding point: written rows rounded once per chunk) and, for float32
 tables, against the token-by-token rule. Slots and weights come from the oracle's
-addressing; the crowded case (a 256-slot table, 16 slots per token) writes every slot
-several times per chunk, so the per-slot chains and the interactions are long."""
+addressing; the crowded cases (256- and 1024-slot tables, 16 or 32 slots per token) write
+every slot several times per chunk and again in the next chunk, so the per-slot chains and
+the interactions are long and most rows gathered ahead of their chunk are replaced by the
+previous chunk's write-back."""
 import numpy as np
 import pytest
 
@@ -20,6 +22,9 @@ CASES = {
     "layer_1p4b_T150": W_["layer_1p4b"].replace(B=1, H=2, T=150),
     "layer_8b_T300": W_["layer_8b_long"].replace(B=1, H=2, T=300),
     "crowded_N256": SI.Shape("crowded_N256", 1, 2, 160, 256, 32, 32, 16, 16, 16, "f32", "f32", 9),
+    # consecutive chunks rewrite the same rows: the rows a chunk gathers early are mostly stale
+    "crowded_N1024_bf16": SI.Shape("crowded_N1024_bf16", 1, 2, 300, 1024, 64, 128, 32, 32, 32, "bf16", "bf16", 10),
+    "crowded_N1024_f32": SI.Shape("crowded_N1024_f32", 1, 3, 200, 1024, 64, 64, 32, 32, 32, "f32", "f32", 11),
 }
 
 

@@ -7,6 +7,8 @@ checked where the oracle can follow it:
   prefix (o_t depends only on tokens up to t), up to the first tie that changes a slot set;
 * table rows that no token writes stay bit-identical to M0, in every checked unit;
 * the whole sequence in two calls on the carried table equals one call, bit for bit;
+* the chunkwise two-phase recurrence likewise: sampled units' outputs over a prefix against
+  the oracle's chunkwise form, untouched rows still M0;
 * decode: one step over all B x H tables, sampled units checked against the oracle after
   the oracle's own prefill (other tables hold M0 only; units are independent).
 """
@@ -124,6 +126,58 @@ def test_fullsize_forward(sdm, name):
     o2, _, _ = forward(sdm, sh, dev, S, M2, T1, sh.T)
     assert torch.equal(torch.cat([o1, o2], 2), o), "split call differs from the single call"
     assert torch.equal(M2, M), "carried table differs"
+
+
+@pytest.mark.parametrize("name", list(PLAN))
+def test_fullsize_chunked(sdm, name):
+    """The chunkwise two-phase recurrence at full size, launched as ``bench.py --chunked``
+    launches it (addressing of keys and queries, then one sdm_recurrent_chunked call over all
+    units): in sampled units the device's slots are checked against the oracle's addressing
+    of a prefix, and the outputs up to the first slot-set change caused by a tie against the
+    oracle's chunkwise form on the oracle's own slots (o_t depends only on tokens up to t);
+    rows no token writes stay M0."""
+    import torch
+    sh = W_[name]
+    units, prefix, _ = PLAN[name]
+    log(f"[full] chunked {name}: generating inputs")
+    inp = SI.make_inputs(sh)
+    dev = upload(inp, sh)
+    S = lib_shape(sh)
+    M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, dev["M0"], M)
+    wi = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.int32, device="cuda")
+    wg = torch.empty((sh.B, sh.H, sh.T, sh.W), dtype=torch.float32, device="cuda")
+    ri = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.int32, device="cuda")
+    rg = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
+    sdm.address(S, dev["k"], dev["subkeys"], sh.W, wi, wg)
+    sdm.address(S, dev["q"], dev["subkeys"], sh.R, ri, rg)
+    o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sdm.workspace_bytes_chunked(S), dtype=torch.uint8, device="cuda")
+    log(f"[full] chunked {name}: B={sh.B} H={sh.H} T={sh.T}")
+    sdm.recurrent_chunked(S, wi, wg, ri, rg, dev["v"], dev["alpha"], dev["beta"], M, o, ws)
+    torch.cuda.synchronize()
+    tol = tolerance(sh)
+    for (b, h) in units:
+        P = min(prefix, sh.T)
+        Up = unit_inputs(inp, sh, b, h, T=P)
+        owi, oww, _ = O.address(Up["k"], Up["C1"], Up["C2"], sh.kappa, sh.W)
+        ori, orw, _ = O.address(Up["q"], Up["C1"], Up["C2"], sh.kappa, sh.R)
+        gw, gr = wi[b, h, :P].cpu().numpy(), ri[b, h, :P].cpu().numpy()
+        tw, cw, fw = compare_indices(gw, owi, Up["k"], Up["C1"], Up["C2"], sh.N)
+        tr, cr, fr = compare_indices(gr, ori, Up["q"], Up["C1"], Up["C2"], sh.N)
+        assert not fw and not fr
+        first = min(cw + cr) if (cw or cr) else P
+        assert first >= P // 2, f"{name} unit ({b},{h}): slot sets diverge at token {first}"
+        oc, _ = O.chunkwise_recurrence(Up["M0"], owi, oww, ori, orw, Up["v"], Up["alpha"], Up["beta"], 64,
+                                       sh.mem_dtype)
+        eo = rel_err(o[b, h, :first].cpu().numpy(), oc[:first])
+        log(f"[full] chunked {name} unit ({b},{h}): o over {first} tokens rel err {eo:.2e} (tol {tol}); "
+            f"tie positions {tw + tr}")
+        assert eo < tol
+        Mh = SI.widen(from_dev(M[b, h], sh.mem_dtype), sh.mem_dtype)
+        touched = np.zeros(sh.N, bool)
+        touched[wi[b, h].cpu().numpy().ravel()] = True
+        assert np.array_equal(Mh[~touched], Up["M0"][~touched])
 
 
 def test_fullsize_decode(sdm):

@@ -144,19 +144,30 @@ sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_co
 /* ---------------------------------------------------------------------------------------
  * Chunkwise two-phase form of the recurrence (PL App. A.1 "Phase 1" / "Phase 2", App. A.2:
  * inside a chunk of 64 tokens every quantity is the chunk-start table plus a combination of
- * the chunk's write residuals; Phase 1 forms the tokens' interactions over shared slots and
- * solves the unit lower-triangular system's inverse, in parallel over chunks; Phase 2
- * gathers each chunk's rows, forms the residuals and outputs and writes each row back once).
+ * the chunk's write residuals). Phase 1, in parallel over all chunks, forms from slots,
+ * weights and gates alone each occurrence's decay coefficients and the tokens' couplings over
+ * shared slots (kept as sparse row-sorted lists); Phase 2, chunk after chunk, gathers the
+ * chunk's rows, solves the unit lower-triangular system for the residuals by a forward sweep
+ * over those lists, forms the outputs and writes each written row back once.
  * --------------------------------------------------------------------------------------- */
 
 /* Bytes of device memory sdm_recurrent_chunked needs as workspace (0 for a shape it does not
- * take: W or R above 32, or an invalid shape). */
+ * take: W or R above 32, a table of 2^31 - 16 bytes or more per (batch, head), or an invalid
+ * shape). About 90 KB per 64 tokens per (batch, head) at W = R = 32. */
 size_t sdm_workspace_bytes_chunked(const sdm_shape* shape);
 
 /* The recurrence of sdm_recurrent (written-rows rule), computed chunk by chunk: same
- * arguments, same o and final table up to float32 summation order, except that written rows
- * are rounded to mem_dtype once per chunk (when written back) instead of at every write.
- * W, R <= 32; ws: at least sdm_workspace_bytes_chunked(shape) bytes. */
+ * arguments, layouts and stream semantics (the call is asynchronous on `stream`; M is read
+ * and updated in place; o [B,H,T,d_v] float32 is written), same o and final table up to
+ * float32 summation order, except that written rows are rounded to mem_dtype once per chunk
+ * (when written back) instead of at every write. Each token's W write slots must be distinct
+ * (the addressing produces them so); a slot outside [0, N) touches nothing.
+ * W, R <= 32; ws: at least sdm_workspace_bytes_chunked(shape) bytes, 16-byte aligned, owned by
+ * the caller and not shared with a call that may run concurrently.
+ * Errors (nothing is launched): SDM_ERR_INVALID_ARG for a bad shape, a null or misaligned
+ * pointer, or outputs (M, o, ws) that overlap each other or an input; SDM_ERR_UNSUPPORTED
+ * for W or R above 32 or a table too large for 32-bit row offsets; SDM_ERR_WORKSPACE for a
+ * missing or short workspace; SDM_ERR_HIP if a launch fails. */
 sdm_status sdm_recurrent_chunked(const sdm_shape* shape, const int32_t* widx, const float* wgt, const int32_t* ridx,
                                  const float* rgt, const void* v, const float* alpha, const float* beta, void* M,
                                  float* o, void* ws, size_t ws_bytes, void* stream);

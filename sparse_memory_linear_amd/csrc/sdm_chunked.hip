@@ -17,18 +17,21 @@
 // system is solved by a forward sweep over the nonzeros only.
 //
 // Phase 1 (chunk_prep_kernel, one workgroup per (unit, chunk), every chunk in parallel): the
-// chunk's write occurrences go into an LDS hash of per-slot linked lists; each write and read
-// occurrence walks its slot's list for its couplings (accumulated densely in LDS, with a bit
-// mask per row of the pairs that occur), its decay coefficient and its write-back terms. The
-// product over a slot's writers between two tokens is a product over a set, so the list
-// order does not matter. The couplings then leave as row-sorted lists.
+// chunk's write occurrences go into an LDS hash of per-slot linked lists and a bit filter;
+// each write and read occurrence walks its slot's list for its couplings (accumulated
+// densely in LDS, with a bit mask per row of the pairs that occur), its decay coefficient
+// and its write-back terms (a read whose slot the filter rules out, or a slot's only
+// writer, takes a short path). The product over a slot's writers between two tokens is a
+// product over a set, so the list order does not matter. The couplings then leave as
+// row-sorted lists.
 //
-// Phase 2 (chunk_apply_kernel, one workgroup per (unit, block of CBD row dwords), the chunks
-// of a unit in order; lane = (token, dword)): each lane gathers its token's W + R row pieces
-// at once and forms P and O0 in registers; delta starts as beta (V - P) in LDS, one wave
-// sweeps the K list (if any), then o = O0 + Q delta and the last writer of each slot writes
-// its row back once, rounded to the table dtype there. The next chunk's slot lists are
-// prefetched into LDS while the current chunk runs.
+// Phase 2 (chunk_apply_kernel, one workgroup per (unit, block of row dwords), the chunks of
+// a unit in order): the lanes of a token split its occurrences into groups and the block
+// into quads, so that each lane gathers a few whole row pieces at once and the lanes of one
+// occurrence read contiguous bytes; P and O0 are summed across the groups; delta starts as
+// beta (V - P) in LDS, the chunk's lists are staged in LDS and a few lanes sweep K's rows;
+// then o = O0 + Q delta and the last writer of each slot writes its piece back once,
+// rounded to the table dtype there.
 
 #include "sdm_device.hpp"
 #include "sdm_internal.hpp"
@@ -677,8 +680,6 @@ hipError_t launch_apply_cfg(ChunkArgs& A, int list, hipStream_t st) {
     case 1: return launch_apply<MemT, InT, 4, 4, 2, false>(A, list, st);  // 16 dwords, 512 lanes
     case 2: return launch_apply<MemT, InT, 4, 1, 4, true>(A, list, st);   // 4 dwords
     case 3: return launch_apply<MemT, InT, 2, 1, 4, true>(A, list, st);   // 2 dwords
-    case 5: return launch_apply<MemT, InT, 4, 4, 4, false>(A, list, st);  // 16 dwords, 1024 lanes
-    case 6: return launch_apply<MemT, InT, 4, 2, 4, true>(A, list, st);   // 8 dwords, 512 lanes
     default: return launch_apply<MemT, InT, 1, 1, 4, true>(A, list, st);  // 1 dword
   }
 }

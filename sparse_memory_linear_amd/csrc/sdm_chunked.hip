@@ -52,8 +52,11 @@ constexpr uint32_t kNoneByte = 0x7FFFFFF0u;  // byte offset past every table (ta
 
 // Per-(unit, chunk) block of Phase 1 results, in 4-byte words. Per-occurrence arrays are
 // [kC][LIST] (LIST >= W, R; unused entries hold zeros and wb = -1). The list area holds the
-// K and Q row starts and, from word kLa0 on, the write-back lists, then K's and Q's entries.
-constexpr int kLa0 = 132;
+// K and Q row starts, the K rows by dependency level and, from word kLa0 on, the write-back
+// lists, then K's and Q's entries.
+constexpr int kLev = 8;                  // dependency levels of K's rows kept as row masks
+constexpr int kLevAt = 130;              // list-area word: number of levels (kLev + 1: more)
+constexpr int kLa0 = 132 + 2 * kLev;
 struct MetaLayout {
   int list;
   size_t gw, wc, ge, wb, gr, hdr, la, words;
@@ -68,7 +71,8 @@ __host__ __device__ inline MetaLayout meta_layout(int list) {
   m.wb = m.ge + occ;      // -1, or for the slot's last writer (start << 8 | count) of its other writers
   m.gr = m.wb + occ;      // u_tr dec(m_tr; start, t+1)
   m.hdr = m.gr + occ;     // [0] write-back entries, [1] K entries, [2] Q entries, [3..4] rows with K entries
-  m.la = m.hdr + 8;       // [0, 65) K row starts, [65, 130) Q row starts, [kLa0, ...) entries (tau, coef):
+  m.la = m.hdr + 8;       // [0, 65) K row starts, [65, 130) Q row starts, [kLevAt] levels, [132 + 2l, +2) rows
+                          // of level l + 1, [kLa0, ...) entries (tau, coef):
                           // write-back lists, then K (coef beta_t K[t][tau]), then Q, each sorted by t
   m.words = (m.la + kLa0 + 2 * (occ + kKMax + kQMax) + 63) & ~(size_t)63;
   return m;
@@ -315,9 +319,29 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     if (lane == 63) tot[wave] = off;
     off -= cnt;
     const unsigned long long rows = __ballot(cnt > 0);
-    if (wave == 0 && lane == 0) {
-      blk[A.ml.hdr + 3] = (uint32_t)rows;
-      blk[A.ml.hdr + 4] = (uint32_t)(rows >> 32);
+    if (wave == 0) {
+      // dependency level of each K row: 0 without entries, else one more than its deepest
+      // entry's row; rows are final in ascending order (entries point to earlier rows)
+      int lv = 0;
+      for (int r = 0; r < kC; ++r) {
+        const int l = __builtin_amdgcn_readlane(lv, r);
+        if ((m0 >> r) & 1ull) lv = max(lv, l + 1);
+      }
+      int top = lv;
+      for (int s = 32; s >= 1; s >>= 1) top = max(top, __shfl_xor(top, s, 64));
+      unsigned long long lm[kLev];
+#pragma unroll
+      for (int l = 0; l < kLev; ++l) lm[l] = __ballot(lv == l + 1);
+      if (lane == 0) {
+        blk[A.ml.hdr + 3] = (uint32_t)rows;
+        blk[A.ml.hdr + 4] = (uint32_t)(rows >> 32);
+        la[kLevAt] = (uint32_t)min(top, kLev + 1);
+#pragma unroll
+        for (int l = 0; l < kLev; ++l) {
+          la[132 + 2 * l] = (uint32_t)lm[l];
+          la[133 + 2 * l] = (uint32_t)(lm[l] >> 32);
+        }
+      }
     }
   }
   __syncthreads();
@@ -576,21 +600,44 @@ __global__ void __launch_bounds__(64 * NQ * G) chunk_apply_kernel(ChunkArgs A) {
     if (tid + NT < NLA) lst[tid + NT] = lr1;
     for (int i = tid + 2 * NT; i < nla; i += NT) lst[i] = mb[ml.la + i];
     __syncthreads();
-    // forward sweep over the K list: delta_t -= beta_t K[t][tau] delta_tau, rows in order
+    // forward solve over the K list: delta_t -= beta_t K[t][tau] delta_tau. Rows of one
+    // dependency level need only rows of lower levels: each row's own lanes update it, one
+    // barrier per level; past kLev levels a few lanes sweep the rows in order.
     if (kn > 0) {
-      if (tid < NCOL) {
-        const uint32_t* ke = lst + kLa0 + 2 * wn;
-        unsigned long long rows = krows;
-        while (rows) {
-          const int r = __builtin_ctzll(rows);
-          rows &= rows - 1;
-          float acc = D[r][tid];
-          for (int e = (int)lst[r]; e < (int)lst[r + 1]; ++e)
-            acc = fmaf(-__uint_as_float(ke[2 * e + 1]), D[ke[2 * e]][tid], acc);
-          D[r][tid] = acc;
+      const uint32_t* ke = lst + kLa0 + 2 * wn;
+      const int nlev = (int)lst[kLevAt];
+      if (nlev <= kLev) {
+        for (int l = 0; l < nlev; ++l) {
+          const unsigned long long m = (unsigned long long)lst[132 + 2 * l] | (unsigned long long)lst[133 + 2 * l] << 32;
+          if (((m >> t) & 1ull) && cl) {
+            float acc[CPLN];
+#pragma unroll
+            for (int c = 0; c < CPLN; ++c) acc[c] = D[t][lc0 + c];
+            for (int e = (int)lst[t]; e < (int)lst[t + 1]; ++e) {
+              const float kv = __uint_as_float(ke[2 * e + 1]);
+              const int tk = (int)ke[2 * e];
+#pragma unroll
+              for (int c = 0; c < CPLN; ++c) acc[c] = fmaf(-kv, D[tk][lc0 + c], acc[c]);
+            }
+#pragma unroll
+            for (int c = 0; c < CPLN; ++c) D[t][lc0 + c] = acc[c];
+          }
+          __syncthreads();
         }
+      } else {
+        if (tid < NCOL) {
+          unsigned long long rows = krows;
+          while (rows) {
+            const int r = __builtin_ctzll(rows);
+            rows &= rows - 1;
+            float acc = D[r][tid];
+            for (int e = (int)lst[r]; e < (int)lst[r + 1]; ++e)
+              acc = fmaf(-__uint_as_float(ke[2 * e + 1]), D[ke[2 * e]][tid], acc);
+            D[r][tid] = acc;
+          }
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
     // o = O0 + Q delta
     if (tv && cl) {

@@ -74,6 +74,49 @@ __device__ __forceinline__ float cvt(uint32_t r) {
   if constexpr (sizeof(T) == 2) return __uint_as_float(r << 16);
   else return __uint_as_float(r);
 }
+// CW consecutive values of T (CW = 1 or 2) as raw words: a bf16 pair in one word, float32
+// values one word each; loaded and stored in one buffer instruction.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename T, int CW>
+struct Wide {
+  static constexpr int kN = CW == 1 || sizeof(T) == 2 ? 1 : 2;
+  __device__ static void ld(rsrc_t rs, uint32_t off, uint32_t* w) {
+    if constexpr (CW == 1) {
+      w[0] = bld<T>(rs, off);
+    } else if constexpr (sizeof(T) == 2) {
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    } else {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+      w[0] = x.x, w[1] = x.y;
+    }
+  }
+  __device__ static float val(const uint32_t* w, int k) {
+    if constexpr (CW == 1) return cvt<T>(w[0]);
+    else if constexpr (sizeof(T) == 2) return k == 0 ? __uint_as_float(w[0] << 16) : __uint_as_float(w[0] & 0xFFFF0000u);
+    else return __uint_as_float(w[k]);
+  }
+  __device__ static void st_raw(rsrc_t rs, uint32_t off, const uint32_t* w) {
+    if constexpr (CW == 1 || sizeof(T) == 2) {
+      if constexpr (CW == 1 && sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[0], rs, off, 0, 0);
+      else __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, off, 0, 0);
+    } else {
+      u32x2 x;
+      x.x = w[0], x.y = w[1];
+      __builtin_amdgcn_raw_buffer_store_b64(x, rs, off, 0, 0);
+    }
+  }
+};
+template <int CW>
+__device__ __forceinline__ void st_f32w(rsrc_t rs, uint32_t off, const float* v) {
+  if constexpr (CW == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), rs, off, 0, 0);
+  } else {
+    u32x2 x;
+    x.x = __float_as_uint(v[0]), x.y = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(x, rs, off, 0, 0);
+  }
+}
+
 __device__ __forceinline__ int lds_ld(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -215,10 +258,10 @@ constexpr size_t wave_lds_bytes() {
 }
 constexpr size_t kCtrlBytes = (kFinRing + 16) * 4;
 
-// NG row groups of C = 64 / NG lanes: each group holds the same C columns and takes up to MH
-// write rows and MH read rows of every token.
-template <typename MemT, typename InT, int NG, int MH>
-__global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
+// NG row groups of C = 64 / NG lanes: each group holds the same C * CW columns (CW per lane)
+// and takes up to MH write rows and MH read rows of every token.
+template <typename MemT, typename InT, int NG, int MH, int CW>
+__global__ void __launch_bounds__(CW == 1 ? kMaxWaves * 64 : 512) backward_kernel(BwdArgs A) {
   constexpr int C = 64 / NG;
   constexpr int LIST = MH * NG;  // longest slot list handled; group h holds rows h*MH + i
   using Meta = TokMeta<LIST>;
@@ -237,7 +280,7 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
   const int xcd = blockIdx.x % kXcd, y = blockIdx.x / kXcd;
   const int p = y % A.P, u = (y / A.P) * kXcd + xcd;
   if (u >= A.U) return;
-  const int c = p * C + cl;
+  const int c = (p * C + cl) * CW;  // this lane's first column (d_v is a multiple of CW)
   const bool act = c < A.d_v;
   const uint32_t cc = act ? c : 0;  // inactive lanes load column 0 and discard it
   const int T = A.T, W = A.W, R = A.R, d_v = A.d_v;
@@ -385,17 +428,21 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     }
     // 3. every row load of token t at once (a row past W reads a neighbouring log row, or
     //    zeros past the end of the log, and is discarded)
-    uint32_t xr[MH], mrr[MH], gy[MH], gr[MH];
+    using WM = Wide<MemT, CW>;
+    using WF = Wide<float, CW>;
+    using WI = Wide<InT, CW>;
+    uint32_t xr[MH][WM::kN], mrr[MH][WM::kN], gy[MH][WF::kN], gr[MH][WF::kN];
     const uint32_t xo = ((uint32_t)t * W + hb) * rowM + cc * ms;
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      xr[i] = bld<MemT>(rX, xo + i * rowM);
-      gy[i] = bld<float>(rG, rn[i] * 4);
-      mrr[i] = bld<MemT>(rM, rm[i] * ms);
-      gr[i] = bld<float>(rG, rm[i] * 4);
+      WM::ld(rX, xo + i * rowM, xr[i]);
+      WF::ld(rG, rn[i] * 4, gy[i]);
+      WM::ld(rM, rm[i] * ms, mrr[i]);
+      WF::ld(rG, rm[i] * 4, gr[i]);
     }
-    const uint32_t graw = bld<float>(rO, (uint32_t)t * rowG + cc * 4);
-    const uint32_t vraw = bld<InT>(rV, ((uint32_t)t * d_v + cc) * is);
+    uint32_t graw[WF::kN], vraw[WI::kN];
+    WF::ld(rO, (uint32_t)t * rowG + cc * 4, graw);
+    WI::ld(rV, ((uint32_t)t * d_v + cc) * is, vraw);
     // 4. while they are in flight: the previous token's column sums
     const unsigned long long rstm = ((unsigned long long)mt.rlo | ((unsigned long long)mt.rhi << 32)) >> hb;
     const float al = mt.al, be = mt.be;
@@ -405,7 +452,12 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     if (t >= 2 * K) put(m2);
     sync();
     // 5. token t (rows without a slot loaded zeros: dy = 0 there since wadd = 0)
-    const float g = act ? __uint_as_float(graw) : 0.f, vc = act ? cvt<InT>(vraw) : 0.f;
+    float g[CW], vc[CW];
+#pragma unroll
+    for (int k = 0; k < CW; ++k) {
+      g[k] = act ? WF::val(graw, k) : 0.f;
+      vc[k] = act ? WI::val(vraw, k) : 0.f;
+    }
     float aj[MH], wd[MH];
     if constexpr (MH % 4 == 0) {
 #pragma unroll
@@ -420,28 +472,52 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
         wd[i] = mt.wadd[hb + i];
       }
     }
-    float s = 0.f, dd = 0.f;
-    float x[MH], dy[MH];
+    float s[CW], dd[CW];
+    float x[MH][CW], dy[MH][CW];
+#pragma unroll
+    for (int k = 0; k < CW; ++k) s[k] = dd[k] = 0.f;
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      x[i] = rn[i] != kNone ? cvt<MemT>(xr[i]) : 0.f;
-      dy[i] = __uint_as_float(gy[i]) + wd[i] * g;
-      s = fmaf(aj[i], x[i], s);
-      dd = fmaf(aj[i], dy[i], dd);
+#pragma unroll
+      for (int k = 0; k < CW; ++k) {
+        x[i][k] = rn[i] != kNone ? WM::val(xr[i], k) : 0.f;
+        dy[i][k] = WF::val(gy[i], k) + wd[i] * g[k];
+        s[k] = fmaf(aj[i], x[i][k], s[k]);
+        dd[k] = fmaf(aj[i], dy[i][k], dd[k]);
+      }
     }
-    s = group_sum(s);
-    dd = group_sum(dd);
-    const float resid = vc - al * s, delta = be * resid, drho = -be * dd;
-    float pal = 0.f;
+    float resid[CW], delta[CW], drho[CW], pal[CW];
+#pragma unroll
+    for (int k = 0; k < CW; ++k) {
+      s[k] = group_sum(s[k]);
+      dd[k] = group_sum(dd[k]);
+      resid[k] = vc[k] - al * s[k];
+      delta[k] = be * resid[k];
+      drho[k] = -be * dd[k];
+      pal[k] = 0.f;
+    }
+    // row partials summed over this lane's columns
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      part[hb + i][cl] = dy[i] * delta + al * drho * x[i];
-      pal = fmaf(dy[i], x[i], pal);
-      part[LIST + hb + i][cl] = g * cvt<MemT>(mrr[i]);
+      float pw = 0.f, pr = 0.f;
+#pragma unroll
+      for (int k = 0; k < CW; ++k) {
+        pw += dy[i][k] * delta[k] + al * drho[k] * x[i][k];
+        pal[k] = fmaf(dy[i][k], x[i][k], pal[k]);
+        pr += g[k] * WM::val(mrr[i], k);
+      }
+      part[hb + i][cl] = pw;
+      part[LIST + hb + i][cl] = pr;
     }
     // dalpha and dbeta: sums over rows (groups) and over this wave's columns
-    const float sal = column_sum(act ? group_sum(pal) + drho * s : 0.f);
-    const float sbe = column_sum(act ? dd * resid : 0.f);
+    float lal = 0.f, lbe = 0.f;
+#pragma unroll
+    for (int k = 0; k < CW; ++k) {
+      lal += group_sum(pal[k]) + drho[k] * s[k];
+      lbe += dd[k] * resid[k];
+    }
+    const float sal = column_sum(act ? lal : 0.f);
+    const float sbe = column_sum(act ? lbe : 0.f);
     if (lane == 0) {
       atomicAdd(A.dalpha + ut + t, sal);
       atomicAdd(A.dbeta + ut + t, sbe);
@@ -458,12 +534,23 @@ __global__ void __launch_bounds__(kMaxWaves * 64) backward_kernel(BwdArgs A) {
     }
 #pragma unroll
     for (int i = 0; i < MH; ++i) {
-      bst<float>(rG, rn[i] * 4, al * (dy[i] + aj[i] * drho));
-      bst<MemT>(rM, rn[i] * ms, x[i]);
+      float gv[CW], rv[CW];
+#pragma unroll
+      for (int k = 0; k < CW; ++k) {
+        gv[k] = al * (dy[i][k] + aj[i] * drho[k]);
+        rv[k] = WF::val(gr[i], k) + rcv[i] * g[k];
+      }
+      st_f32w<CW>(rG, rn[i] * 4, gv);
+      WM::st_raw(rM, rn[i] * ms, xr[i]);  // the undone row is the logged row, bit for bit
       const uint32_t rs = (rstm >> i) & 1ull ? rm[i] : kNone;
-      bst<float>(rG, rs * 4, __uint_as_float(gr[i]) + rcv[i] * g);
+      st_f32w<CW>(rG, rs * 4, rv);
     }
-    if (h == 0 && act) bst<float>(rD, (uint32_t)t * rowG + c * 4, be * dd);
+    if (h == 0 && act) {
+      float dvv[CW];
+#pragma unroll
+      for (int k = 0; k < CW; ++k) dvv[k] = be * dd[k];
+      st_f32w<CW>(rD, (uint32_t)t * rowG + c * 4, dvv);
+    }
     // 6. publish token t once its stores are complete
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -638,11 +725,12 @@ BwdWs bwd_layout(const sdm_shape& S) {
   return L;
 }
 
-template <typename MemT, typename InT, int NG, int MH>
+template <typename MemT, typename InT, int NG, int MH, int CW>
 hipError_t launch_cfg(BwdArgs A, const PrepArgs& Pa0, long long wgs, hipStream_t st) {
-  A.P = (A.d_v + 64 / NG - 1) / (64 / NG);
-  // K waves per workgroup: 8, or 16 when fewer than two workgroups per CU would run
-  A.K = wgs >= 2ll * device_cus() ? 8 : kMaxWaves;
+  A.P = (A.d_v + CW * 64 / NG - 1) / (CW * 64 / NG);
+  // K waves per workgroup: 8, or 16 when fewer than two workgroups per CU would run (8 with
+  // two columns per lane, whose row registers need the larger per-wave register file)
+  A.K = CW == 2 || wgs >= 2ll * device_cus() ? 8 : kMaxWaves;
   PrepArgs Pa = Pa0;
   Pa.win = A.K - 1;
   const int entries = (kPrepBlk + Pa.win) * (A.W + A.R);
@@ -654,9 +742,13 @@ hipError_t launch_cfg(BwdArgs A, const PrepArgs& Pa0, long long wgs, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = kCtrlBytes + (size_t)A.K * wave_lds_bytes<NG, MH>();
-  hipLaunchKernelGGL((backward_kernel<MemT, InT, NG, MH>), dim3((unsigned)wgs), dim3(64 * A.K), lds, st, A);
+  hipLaunchKernelGGL((backward_kernel<MemT, InT, NG, MH, CW>), dim3((unsigned)wgs), dim3(64 * A.K), lds, st, A);
   return hipGetLastError();
 }
+
+#ifndef SDM_BWD_CW
+#define SDM_BWD_CW 0  // columns per lane of the reverse walk: 0 picks by shape
+#endif
 
 // Column blocks of C = 64 / NG columns, each row group taking MH in {2, 4, 8} rows of each
 // kind (NG * MH >= max(W, R)): the widest block whose grid still gives every CU a
@@ -677,20 +769,35 @@ hipError_t launch_bwd(const BwdArgs& A, const PrepArgs& Pa, hipStream_t st) {
   if (pick < 0) return hipErrorInvalidValue;
   const int NG = 1 << pick, mh = (list + NG - 1) / NG;
   const int MH = mh <= 2 ? 2 : mh <= 4 ? 4 : 8;
-  if (NG == 1 && MH == 2) return launch_cfg<MemT, InT, 1, 2>(A, Pa, pick_wgs, st);
-  if (NG == 1 && MH == 4) return launch_cfg<MemT, InT, 1, 4>(A, Pa, pick_wgs, st);
-  if (NG == 1 && MH == 8) return launch_cfg<MemT, InT, 1, 8>(A, Pa, pick_wgs, st);
-  if (NG == 2 && MH == 2) return launch_cfg<MemT, InT, 2, 2>(A, Pa, pick_wgs, st);
-  if (NG == 2 && MH == 4) return launch_cfg<MemT, InT, 2, 4>(A, Pa, pick_wgs, st);
-  if (NG == 2 && MH == 8) return launch_cfg<MemT, InT, 2, 8>(A, Pa, pick_wgs, st);
-  if (NG == 4 && MH == 2) return launch_cfg<MemT, InT, 4, 2>(A, Pa, pick_wgs, st);
-  if (NG == 4 && MH == 4) return launch_cfg<MemT, InT, 4, 4>(A, Pa, pick_wgs, st);
-  if (NG == 4 && MH == 8) return launch_cfg<MemT, InT, 4, 8>(A, Pa, pick_wgs, st);
-  if (NG == 8 && MH == 2) return launch_cfg<MemT, InT, 8, 2>(A, Pa, pick_wgs, st);
-  if (NG == 8 && MH == 4) return launch_cfg<MemT, InT, 8, 4>(A, Pa, pick_wgs, st);
-  if (NG == 8 && MH == 8) return launch_cfg<MemT, InT, 8, 8>(A, Pa, pick_wgs, st);
-  if (NG == 16 && MH == 2) return launch_cfg<MemT, InT, 16, 2>(A, Pa, pick_wgs, st);
-  if (NG == 16 && MH == 4) return launch_cfg<MemT, InT, 16, 4>(A, Pa, pick_wgs, st);
+  // Two columns per lane when the wider blocks still give every CU a workgroup: a wave then
+  // moves 64-byte pieces of bf16 rows, whole sectors, instead of halves that the unit's
+  // other column blocks fetch again at other times.
+  {
+    const int C = 64 / NG;
+    const long long wgs2 = (long long)((A.U + kXcd - 1) / kXcd) * kXcd * ((A.d_v + 2 * C - 1) / (2 * C));
+    int cw = A.d_v % (2 * C) == 0 && wgs2 >= cus ? 2 : 1;
+    if (SDM_BWD_CW) cw = SDM_BWD_CW;
+    if (cw == 2) {
+      if (NG == 2 && MH == 4) return launch_cfg<MemT, InT, 2, 4, 2>(A, Pa, wgs2, st);
+      if (NG == 2 && MH == 8) return launch_cfg<MemT, InT, 2, 8, 2>(A, Pa, wgs2, st);
+      if (NG == 4 && MH == 4) return launch_cfg<MemT, InT, 4, 4, 2>(A, Pa, wgs2, st);
+      if (NG == 4 && MH == 8) return launch_cfg<MemT, InT, 4, 8, 2>(A, Pa, wgs2, st);
+    }
+  }
+  if (NG == 1 && MH == 2) return launch_cfg<MemT, InT, 1, 2, 1>(A, Pa, pick_wgs, st);
+  if (NG == 1 && MH == 4) return launch_cfg<MemT, InT, 1, 4, 1>(A, Pa, pick_wgs, st);
+  if (NG == 1 && MH == 8) return launch_cfg<MemT, InT, 1, 8, 1>(A, Pa, pick_wgs, st);
+  if (NG == 2 && MH == 2) return launch_cfg<MemT, InT, 2, 2, 1>(A, Pa, pick_wgs, st);
+  if (NG == 2 && MH == 4) return launch_cfg<MemT, InT, 2, 4, 1>(A, Pa, pick_wgs, st);
+  if (NG == 2 && MH == 8) return launch_cfg<MemT, InT, 2, 8, 1>(A, Pa, pick_wgs, st);
+  if (NG == 4 && MH == 2) return launch_cfg<MemT, InT, 4, 2, 1>(A, Pa, pick_wgs, st);
+  if (NG == 4 && MH == 4) return launch_cfg<MemT, InT, 4, 4, 1>(A, Pa, pick_wgs, st);
+  if (NG == 4 && MH == 8) return launch_cfg<MemT, InT, 4, 8, 1>(A, Pa, pick_wgs, st);
+  if (NG == 8 && MH == 2) return launch_cfg<MemT, InT, 8, 2, 1>(A, Pa, pick_wgs, st);
+  if (NG == 8 && MH == 4) return launch_cfg<MemT, InT, 8, 4, 1>(A, Pa, pick_wgs, st);
+  if (NG == 8 && MH == 8) return launch_cfg<MemT, InT, 8, 8, 1>(A, Pa, pick_wgs, st);
+  if (NG == 16 && MH == 2) return launch_cfg<MemT, InT, 16, 2, 1>(A, Pa, pick_wgs, st);
+  if (NG == 16 && MH == 4) return launch_cfg<MemT, InT, 16, 4, 1>(A, Pa, pick_wgs, st);
   return hipErrorInvalidValue;
 }
 

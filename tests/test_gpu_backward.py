@@ -20,8 +20,10 @@ CASES = {
     "layer_8b_T100": W_["layer_8b_long"].replace(B=1, H=2, T=100),
     "coupled_T96": W_["layer_8b_long"].replace(B=1, H=2, T=96),
     # every head of the 1.4B shape: the launch picks the configuration the full size uses
-    # (16-column blocks, 8 rows per group); the oracle checks three units
+    # (32-column blocks, two columns per lane, 8 rows per group); the oracle checks three units
     "layer_1p4b_allheads_T40": W_["layer_1p4b"].replace(T=40),
+    # 128 units of the small shape (float32 table): two columns per lane, 4 rows per group
+    "small_128units_T24": W_["small"].replace(B=8, H=16, T=24),
     # edges: one token; fewer tokens than waves, lists that leave padding rows in the last
     # row group (float32 table, bf16 inputs); a d_v that leaves the last 16-column block
     # half empty
@@ -29,7 +31,8 @@ CASES = {
     "edge_T5_W3_R5": W_["small"].replace(B=2, H=1, T=5, W=3, R=5),
     "ragged_dv40_allheads_T24": W_["layer_1p4b"].replace(T=24, d_v=40),
 }
-SAMPLED = {"layer_1p4b_allheads_T40": [(0, 0), (3, 7), (7, 15)], "ragged_dv40_allheads_T24": [(0, 0), (7, 15)]}
+SAMPLED = {"layer_1p4b_allheads_T40": [(0, 0), (3, 7), (7, 15)], "ragged_dv40_allheads_T24": [(0, 0), (7, 15)],
+           "small_128units_T24": [(0, 0), (5, 11), (7, 15)]}
 
 
 def couple(wi, ri, N):
@@ -157,7 +160,7 @@ def test_log_and_backward(sdm, name):
         assert e < tol
 
 
-@pytest.mark.parametrize("name", ["coupled_T96", "layer_8b_T100"])
+@pytest.mark.parametrize("name", ["coupled_T96", "layer_8b_T100", "layer_1p4b_allheads_T40"])
 def test_backward_repeatable(sdm, name):
     """Every run restores M0 bit for bit and gives the same G and dv bit for bit (no atomics
     there); the sums over columns added with atomics agree to rounding. Covers the start-up

@@ -618,8 +618,33 @@ __global__ void __launch_bounds__(kAbWaves * 64) addr_backward_kernel(AddrBwdArg
   };
   const int r0 = wave * 32;  // this wave's block of sub-keys
   f32x16_t acc0 = {}, acc1 = {};
+  // a token's inputs (weights, their gradients, slots, this lane's x column), loaded one step
+  // ahead so that a step waits only for its sub-key row gathers
+  struct TokIn {
+    float wl, dwl, xv;
+    int il;
+  };
+  auto load_tok = [&](long long cs, int q, TokIn& r) {
+    const long long tt = cs + wave * 2 + q;
+    const bool live = tt < t1;
+    const long long b = tt / T, t = tt - b * T;
+    const size_t row = live ? ((size_t)b * H + h) * T + t : 0;
+    const bool lk = live && lane < n_sel;
+    r.wl = lk ? A.w[row * n_sel + lane] : 0.f;
+    r.dwl = lk ? A.dw[row * n_sel + lane] : 0.f;
+    r.il = lk ? A.idx[row * n_sel + lane] : -1;
+    r.xv = live && act ? ld((const InT*)A.x, row * d_k + hf * A.hd + c) : 0.f;
+  };
+  TokIn nx[2];
+  load_tok(t0, 0, nx[0]);
+  load_tok(t0, 1, nx[1]);
   __syncthreads();
   for (long long c0 = t0; c0 < t1; c0 += kAbStep) {
+    TokIn cur[2] = {nx[0], nx[1]};
+    if (c0 + kAbStep < t1) {
+      load_tok(c0 + kAbStep, 0, nx[0]);
+      load_tok(c0 + kAbStep, 1, nx[1]);
+    }
     int mine[2];  // D entry this lane wrote for each of its tokens (-1: none)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -628,23 +653,20 @@ __global__ void __launch_bounds__(kAbWaves * 64) addr_backward_kernel(AddrBwdArg
       const bool live = tt < t1;
       const long long b = tt / T, t = tt - b * T;
       const size_t row = live ? ((size_t)b * H + h) * T + t : 0;  // token row of x, idx, w, dx
-      const bool lk = live && lane < n_sel;
-      const float wl = lk ? A.w[row * n_sel + lane] : 0.f;
-      const float dwl = lk ? A.dw[row * n_sel + lane] : 0.f;
-      const int il = lk ? A.idx[row * n_sel + lane] : -1;
+      const float wl = cur[q].wl, dwl = cur[q].dwl;
+      const int il = cur[q].il;
       const float S = wave_sum_f32(wl * dwl);
       const float dsc = wl * (dwl - S);
       // this half's sub-key of each selected slot; -1 for a slot outside [0, N)
       const int ii = il >= 0 && il < A.N ? (hf == 0 ? il / s : il % s) : -1;
-      const float xv = live && act ? ld((const InT*)A.x, row * d_k + hf * A.hd + c) : 0.f;
       float dxv = 0.f;
-      // eight selected slots at a time, every load unguarded (a slot outside [0, N) reads
-      // row 0 with coefficient 0), so that eight row loads are in flight together
-      for (int k0 = 0; k0 < n_sel; k0 += 8) {
-        int rk[8];
-        float dk[8], cv[8];
+      // sixteen selected slots at a time, every load unguarded (a slot outside [0, N) reads
+      // row 0 with coefficient 0), so that sixteen row loads are in flight together
+      for (int k0 = 0; k0 < n_sel; k0 += 16) {
+        int rk[16];
+        float dk[16], cv[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const int k = min(k0 + u, 63);
           const int ik = k0 + u < n_sel ? __builtin_amdgcn_readlane(ii, k) : -1;
           const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dsc), k));
@@ -653,10 +675,10 @@ __global__ void __launch_bounds__(kAbWaves * 64) addr_backward_kernel(AddrBwdArg
           cv[u] = ld(C, (size_t)rk[u] * A.hd + cc);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dxv = fmaf(dk[u], cv[u], dxv);
+        for (int u = 0; u < 16; ++u) dxv = fmaf(dk[u], cv[u], dxv);
       }
       if (live && act) A.dx[row * d_k + hf * A.hd + c] = dxv;
-      Xm[tl * 64 + lane] = xv;
+      Xm[tl * 64 + lane] = cur[q].xv;
       mine[q] = ii;
       if (ii >= 0) atomicAdd(&Dm[tl * s + ii], dsc);
     }

@@ -484,15 +484,31 @@ __global__ void __launch_bounds__(64 * NQ * G) chunk_apply_kernel(ChunkArgs A) {
   const MetaLayout ml = A.ml;
   const uint32_t pc = (uint32_t)(p * CBD + q * QD) * 4u;  // byte offset of the piece inside a row
 
-  // this lane's slots of chunk c: occurrences j = g OPL + i
-  auto fetch = [&](int c, int* sw, int* sr) {
+  // this lane's slots of chunk c: occurrences j = g OPL + i (with the prefetch, 16-byte loads
+  // when the lists fill LIST: each lane request then carries four slots; a token past T reads
+  // token 0's and discards them. Without it the slots are needed at once and the narrower
+  // loads keep the registers of the wide pieces below the spill point)
+  const bool full = PRE && (OPL % 4 == 0) && W == LIST && R == LIST;
+  auto fetch = [&](int c, int (&sw)[OPL], int (&sr)[OPL]) {
     const int tt = c * kC + t;
     const bool ok = tt < T;
+    if (OPL % 4 == 0 && full) {
+      const size_t base = ok ? (size_t)tt * LIST + g * OPL : 0;
 #pragma unroll
-    for (int i = 0; i < OPL; ++i) {
-      const int j = g * OPL + i;
-      sw[i] = ok && j < W ? widx[(size_t)tt * W + j] : -1;
-      sr[i] = ok && j < R ? ridx[(size_t)tt * R + j] : -1;
+      for (int k = 0; k < (OPL % 4 == 0 ? OPL / 4 : 0); ++k) {
+        const int4 a = ((const int4*)(widx + base))[k], b = ((const int4*)(ridx + base))[k];
+        sw[4 * k] = ok ? a.x : -1, sw[4 * k + 1] = ok ? a.y : -1;
+        sw[4 * k + 2] = ok ? a.z : -1, sw[4 * k + 3] = ok ? a.w : -1;
+        sr[4 * k] = ok ? b.x : -1, sr[4 * k + 1] = ok ? b.y : -1;
+        sr[4 * k + 2] = ok ? b.z : -1, sr[4 * k + 3] = ok ? b.w : -1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < OPL; ++i) {
+        const int j = g * OPL + i;
+        sw[i] = ok && j < W ? widx[(size_t)tt * W + j] : -1;
+        sr[i] = ok && j < R ? ridx[(size_t)tt * R + j] : -1;
+      }
     }
   };
   int sw[OPL], sr[OPL];

@@ -44,7 +44,7 @@ constexpr int kC = 64;                   // tokens per chunk
 constexpr int kMaxList = 32;             // W, R <= 32 on this path
 constexpr int kBuckets = 4096;           // LDS hash: at most 2048 distinct slots, at most half full
 constexpr uint32_t kFree = 0xFFFFFFFFu;
-constexpr int kFilterWords = 2048;       // 64K-bit filter of the chunk's written slots
+constexpr int kFilterWords = 512;        // 16K-bit filter of the chunk's written slots
 constexpr int kKMax = kC * (kC - 1) / 2;  // distinct (t, tau < t) pairs
 constexpr int kQMax = kC * (kC + 1) / 2;  // distinct (t, tau <= t) pairs
 constexpr int kXcd = 8;                  // workgroups are dealt round-robin to this many L2 domains
@@ -99,19 +99,17 @@ struct ChunkArgs {
 };
 
 __device__ __forceinline__ uint32_t chunk_hash(uint32_t s) { return (s * 2654435761u) >> 20; }  // 12 bits
-__device__ __forceinline__ uint32_t filter_bit(uint32_t s) { return (s * 0x9E3779B1u) >> 16; }  // 16 bits
+__device__ __forceinline__ uint32_t filter_bit(uint32_t s) { return (s * 0x9E3779B1u) >> 18; }  // 14 bits
 
 template <int LIST>
 __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
   constexpr int NOC = kC * LIST;
   constexpr int NO = NOC / 256;  // occurrences per thread, write and read each
   constexpr int SH = LIST == 8 ? 3 : LIST == 16 ? 4 : 5;
-  __shared__ int sn[NOC];          // slot of each write occurrence [t][LIST], -1 for none
-  __shared__ float sa[NOC];        // its weight
-  __shared__ short snx[NOC];       // next occurrence of the same slot, -1 at the end
-  __shared__ short sbk[NOC];       // its hash bucket
+  // 48 KB of LDS: three workgroups per CU
+  __shared__ short snx[NOC];       // next write occurrence [t][LIST] of the same slot, -1 at the end
   __shared__ uint32_t keys[kBuckets];
-  __shared__ int head[kBuckets];
+  __shared__ uint32_t head2[kBuckets / 2];  // first occurrence of each bucket's slot, 16 bits each (0xFFFF: none)
   // couplings: K[t][tau] at [t][tau] (tau < t), Q[t][tau] at [tau][t] (tau <= t)
   __shared__ float KQ[kC][kC + 1];
   __shared__ unsigned long long kmask[kC], qmask[kC];
@@ -137,10 +135,8 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
     rs[k] = okr ? A.ridx[(ut0 + t) * R + j] : -1;
     ra[k] = okr ? A.rgt[(ut0 + t) * R + j] : 0.f;
   }
-  for (int i = tid; i < kBuckets; i += 256) {
-    keys[i] = kFree;
-    head[i] = -1;
-  }
+  for (int i = tid; i < kBuckets; i += 256) keys[i] = kFree;
+  for (int i = tid; i < kBuckets / 2; i += 256) head2[i] = 0xFFFFFFFFu;
   for (int i = tid; i < kFilterWords; i += 256) filt[i] = 0u;
   for (int i = tid; i < kC * (kC + 1); i += 256) (&KQ[0][0])[i] = 0.f;
   if (tid < kC) {
@@ -151,13 +147,30 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
   }
   if (tid == 0) wlcnt = 0;
 #pragma unroll
-  for (int k = 0; k < NO; ++k) {
-    const int i = tid + 256 * k;
+  for (int k = 0; k < NO; ++k)
     if (ws[k] < 0 || ws[k] >= N) ws[k] = -1;
-    sn[i] = ws[k];
-    sa[i] = wa[k];
-  }
   __syncthreads();
+  // list heads: 16-bit entries, exchanged by compare-and-swap on their 32-bit word
+  auto head_at = [&](int b) -> int {
+    const int v = (int)((head2[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu);
+    return v == 0xFFFF ? -1 : v;
+  };
+  auto head_xchg = [&](int b, int v) -> int {
+    uint32_t* w = &head2[b >> 1];
+    const int sh = (b & 1) * 16;
+    uint32_t old = *w;
+    while (true) {
+      const uint32_t nw = (old & ~(0xFFFFu << sh)) | ((uint32_t)v << sh);
+      const uint32_t prev = atomicCAS(w, old, nw);
+      if (prev == old) break;
+      old = prev;
+    }
+    const int pv = (int)((old >> sh) & 0xFFFFu);
+    return pv == 0xFFFF ? -1 : pv;
+  };
+  // the weight of write occurrence q (t LIST + j): from the input, for the rare slots with
+  // several writers in the chunk
+  auto wgt_of = [&](int q) -> float { return A.wgt[(ut0 + (q >> SH)) * W + (q & (LIST - 1))]; };
   auto find = [&](uint32_t s) -> int {  // bucket of a slot written in the chunk, or -1
     uint32_t b = chunk_hash(s);
     while (true) {
@@ -190,12 +203,11 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
       bk[k] = insert((uint32_t)ws[k]);  // the home bucket holds another slot
   int nx[NO];
 #pragma unroll
-  for (int k = 0; k < NO; ++k) nx[k] = ws[k] >= 0 ? atomicExch(&head[bk[k]], tid + 256 * k) : -1;
+  for (int k = 0; k < NO; ++k) nx[k] = ws[k] >= 0 ? head_xchg(bk[k], tid + 256 * k) : -1;
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
     const int i = tid + 256 * k;
     snx[i] = (short)nx[k];
-    sbk[i] = (short)bk[k];
     if (ws[k] >= 0) {
       const uint32_t fb = filter_bit((uint32_t)ws[k]);
       atomicOr(&filt[fb >> 5], 1u << (fb & 31));
@@ -207,7 +219,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
   float st[NO];
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
-    hd[k] = ws[k] >= 0 ? head[bk[k]] : -1;
+    hd[k] = ws[k] >= 0 ? head_at(bk[k]) : -1;
     st[k] = sal[(tid + 256 * k) >> SH];
   }
 #pragma unroll
@@ -225,17 +237,17 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
       const float a = wa[k];
       float before = 1.f, after = 1.f, all = 1.f;
       int others = 0;
-      for (int q = head[b]; q >= 0; q = snx[q]) {
+      for (int q = head_at(b); q >= 0; q = snx[q]) {
         const int tk = q >> SH;
         all *= sal[tk];
         if (tk < t) {
           before *= sal[tk];
           float between = 1.f;  // dec(n; tk, t)
-          for (int l = head[b]; l >= 0; l = snx[l]) {
+          for (int l = head_at(b); l >= 0; l = snx[l]) {
             const int tl = l >> SH;
             if (tl > tk && tl < t) between *= sal[tl];
           }
-          atomicAdd(&KQ[t][tk], sal[t] * a * between * sa[q]);
+          atomicAdd(&KQ[t][tk], sal[t] * a * between * wgt_of(q));
           atomicOr(&kmask[t], 1ull << tk);
           ++others;
         } else if (tk > t) {
@@ -249,14 +261,14 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
         gev = all;
         const int start = others ? atomicAdd(&wlcnt, others) : 0;
         int e = start;
-        for (int q = head[b]; q >= 0; q = snx[q]) {
+        for (int q = head_at(b); q >= 0; q = snx[q]) {
           const int tk = q >> SH;
           if (tk >= t) continue;  // the same writers that were counted
           float aft = 1.f;        // dec(n; tk, end)
-          for (int l = head[b]; l >= 0; l = snx[l])
+          for (int l = head_at(b); l >= 0; l = snx[l])
             if ((l >> SH) > tk) aft *= sal[l >> SH];
           la[kLa0 + 2 * e] = (uint32_t)tk;
-          la[kLa0 + 2 * e + 1] = __float_as_uint(sa[q] * aft);
+          la[kLa0 + 2 * e + 1] = __float_as_uint(wgt_of(q) * aft);
           ++e;
         }
         wbv = start << 8 | others;
@@ -286,16 +298,16 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(ChunkArgs A) {
       const int b = find((uint32_t)s);
       float upto = 1.f;
       if (b >= 0) {
-        for (int q = head[b]; q >= 0; q = snx[q]) {
+        for (int q = head_at(b); q >= 0; q = snx[q]) {
           const int tk = q >> SH;
           if (tk > t) continue;
           upto *= sal[tk];
           float between = 1.f;  // dec(m; tk, t + 1)
-          for (int l = head[b]; l >= 0; l = snx[l]) {
+          for (int l = head_at(b); l >= 0; l = snx[l]) {
             const int tl = l >> SH;
             if (tl > tk && tl <= t) between *= sal[tl];
           }
-          atomicAdd(&KQ[tk][t], w * between * sa[q]);
+          atomicAdd(&KQ[tk][t], w * between * wgt_of(q));
           atomicOr(&qmask[t], 1ull << tk);
         }
       }

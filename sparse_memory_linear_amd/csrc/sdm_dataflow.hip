@@ -47,6 +47,7 @@ namespace {
 
 constexpr int kDepBlk = 64;        // tokens per deps workgroup
 constexpr int kMaxHashBits = 15;   // deps hash table: at most 32768 entries, at most half full
+constexpr int kDepFilterWords = 2048;  // 64K-bit filter of the slots in the deps hash table
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 constexpr int kMaxWin = 127;
 // packed slot word: [31] coded | [30:24] distance | [23:18] writer position | [17:0] slot,
@@ -80,10 +81,12 @@ struct DepArgs {
 };
 
 __device__ __forceinline__ uint32_t dep_hash(uint32_t slot, int bits) { return (slot * 2654435761u) >> (32 - bits); }
+__device__ __forceinline__ uint32_t dep_filter_bit(uint32_t slot) { return (slot * 0x9E3779B1u) >> 16; }  // 16 bits
 
 // hash entry = slot << 14 | window offset << 6 | writer position
 __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
-  extern __shared__ uint32_t table[];  // 2^bits entries
+  extern __shared__ uint32_t table[];  // 2^bits entries, then the filter
+  uint32_t* filt = table + (1 << A.bits);  // kDepFilterWords: a slot whose bit is clear is not in the table
   const int bits = A.bits;
   const uint32_t hmask = (1u << bits) - 1;
   const int u = blockIdx.y;
@@ -92,46 +95,76 @@ __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
   const int whi = t0 + kDepBlk < A.T ? t0 + kDepBlk : A.T;
   const int W = A.W, R = A.R, per = W + R;
   for (int i = threadIdx.x; i < (1 << bits); i += 256) table[i] = kEmpty;
+  for (int i = threadIdx.x; i < kDepFilterWords; i += 256) filt[i] = 0u;
   __syncthreads();
   const int32_t* wi = A.widx + (size_t)u * A.T * W;
   const int32_t* ri = A.ridx + (size_t)u * A.T * R;
-  for (int e = threadIdx.x; e < (whi - wlo) * W; e += 256) {
-    const int k = e / W, j = e - k * W;
-    const int32_t slot = wi[(size_t)(wlo + k) * W + j];
-    if (slot < 0 || slot >= A.N) continue;
-    const uint32_t ent = ((uint32_t)slot << 14) | ((uint32_t)k << 6) | (uint32_t)j;
-    uint32_t h = dep_hash((uint32_t)slot, bits);
-    while (atomicCAS(&table[h], kEmpty, ent) != kEmpty) h = (h + 1) & hmask;
+  // eight entries per thread at a time: their slot loads are in flight together
+  constexpr int kB = 8;
+  const int nins = (whi - wlo) * W;
+  for (int e0 = threadIdx.x; e0 < nins; e0 += 256 * kB) {
+    int32_t sl[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int e = e0 + 256 * b, k = e / W, j = e - k * W;
+      sl[b] = e < nins ? wi[(size_t)(wlo + k) * W + j] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int e = e0 + 256 * b, k = e / W, j = e - k * W;
+      const int32_t slot = sl[b];
+      if (slot < 0 || slot >= A.N) continue;
+      const uint32_t ent = ((uint32_t)slot << 14) | ((uint32_t)k << 6) | (uint32_t)j;
+      uint32_t h = dep_hash((uint32_t)slot, bits);
+      while (atomicCAS(&table[h], kEmpty, ent) != kEmpty) h = (h + 1) & hmask;
+      const uint32_t fb = dep_filter_bit((uint32_t)slot);
+      atomicOr(&filt[fb >> 5], 1u << (fb & 31));
+    }
   }
   __syncthreads();
   uint32_t* out = A.pk + ((size_t)u * A.T + t0) * per;
-  for (int e = threadIdx.x; e < (whi - t0) * per; e += 256) {
-    const int kk = e / per, p = e - kk * per;
-    const int t = t0 + kk, kt = t - wlo;
-    const bool rd = p >= W;
-    const int32_t slot = rd ? ri[(size_t)t * R + (p - W)] : wi[(size_t)t * W + p];
-    uint32_t word = kInvalid;
-    if (slot >= 0 && slot < A.N) {
-      int best = -1, bestj = 0;
-      uint32_t h = dep_hash((uint32_t)slot, bits);
-      while (true) {
-        const uint32_t ent = table[h];
-        if (ent == kEmpty) break;
-        if ((ent >> 14) == (uint32_t)slot) {
-          const int k = (ent >> 6) & 255;
-          const int d = kt - k;
-          // latest writer: an earlier token, or this token itself for a read slot
-          if ((rd ? d >= 0 : d >= 1) && d <= A.win && k > best) {
-            best = k;
-            bestj = ent & 63;
+  const int nlook = (whi - t0) * per;
+  for (int e0 = threadIdx.x; e0 < nlook; e0 += 256 * kB) {
+    int32_t sl[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int e = e0 + 256 * b, kk = e / per, p = e - kk * per, t = t0 + kk;
+      sl[b] = e < nlook ? (p >= W ? ri[(size_t)t * R + (p - W)] : wi[(size_t)t * W + p]) : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int e = e0 + 256 * b;
+      if (e >= nlook) continue;
+      const int kk = e / per, p = e - kk * per;
+      const int t = t0 + kk, kt = t - wlo;
+      const bool rd = p >= W;
+      const int32_t slot = sl[b];
+      uint32_t word = kInvalid;
+      if (slot >= 0 && slot < A.N) {
+        int best = -1, bestj = 0;
+        const uint32_t fb = dep_filter_bit((uint32_t)slot);
+        if ((filt[fb >> 5] >> (fb & 31)) & 1u) {
+          uint32_t h = dep_hash((uint32_t)slot, bits);
+          while (true) {
+            const uint32_t ent = table[h];
+            if (ent == kEmpty) break;
+            if ((ent >> 14) == (uint32_t)slot) {
+              const int k = (ent >> 6) & 255;
+              const int d = kt - k;
+              // latest writer: an earlier token, or this token itself for a read slot
+              if ((rd ? d >= 0 : d >= 1) && d <= A.win && k > best) {
+                best = k;
+                bestj = ent & 63;
+              }
+            }
+            h = (h + 1) & hmask;
           }
         }
-        h = (h + 1) & hmask;
+        word = (uint32_t)slot;
+        if (best >= 0) word |= kCoded | ((uint32_t)(kt - best) << 24) | ((uint32_t)bestj << 18);
       }
-      word = (uint32_t)slot;
-      if (best >= 0) word |= kCoded | ((uint32_t)(kt - best) << 24) | ((uint32_t)bestj << 18);
+      out[e] = word;
     }
-    out[e] = word;
   }
 }
 
@@ -959,7 +992,7 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   // at most half full: writers of one block and its window
   D.bits = 10;
   while (D.bits < kMaxHashBits && (1 << D.bits) < 2 * (kDepBlk + c.win) * S.W) ++D.bits;
-  hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), (size_t)4 << D.bits, stream, D);
+  hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), ((size_t)4 << D.bits) + kDepFilterWords * 4, stream, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float* fac = nullptr;

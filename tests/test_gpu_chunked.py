@@ -25,6 +25,11 @@ CASES = {
     # consecutive chunks rewrite the same rows: the rows a chunk gathers early are mostly stale
     "crowded_N1024_bf16": SI.Shape("crowded_N1024_bf16", 1, 2, 300, 1024, 64, 128, 32, 32, 32, "bf16", "bf16", 10),
     "crowded_N1024_f32": SI.Shape("crowded_N1024_f32", 1, 3, 200, 1024, 64, 64, 32, 32, 32, "f32", "f32", 11),
+    # edges: one token; a few tokens with lists that are not a multiple of four (the narrow
+    # slot loads, two occurrences per lane); float32 inputs with a bf16 table
+    "edge_T1": W_["small"].replace(B=1, H=2, T=1),
+    "edge_T5_W3_R5": W_["small"].replace(B=2, H=1, T=5, W=3, R=5),
+    "in_f32_table_bf16_T130": W_["layer_1p4b"].replace(B=1, H=2, T=130, in_dtype="f32"),
 }
 
 

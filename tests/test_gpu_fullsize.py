@@ -10,7 +10,10 @@ checked where the oracle can follow it:
 * the chunkwise two-phase recurrence likewise: sampled units' outputs over a prefix against
   the oracle's chunkwise form, untouched rows still M0;
 * decode: one step over all B x H tables, sampled units checked against the oracle after
-  the oracle's own prefill (other tables hold M0 only; units are independent).
+  the oracle's own prefill (other tables hold M0 only; units are independent);
+* the backward: with the output gradient nonzero only on a window of leading tokens, every
+  gradient of a sampled unit against the oracle's backward over that window, exact zeros
+  past it, and M0 restored bit for bit by the walk back over the whole sequence.
 """
 import numpy as np
 import pytest
@@ -289,3 +292,89 @@ def test_fullsize_decay_variant(sdm):
         touched[gw[b, h].ravel()] = True
         lam_h = lama[b, h].cpu().numpy()
         assert np.all(lam_h[~touched] == 0.0) and np.all(lam_h[touched] < 0.0)
+
+
+@pytest.mark.parametrize("name", list(PLAN))
+def test_fullsize_backward(sdm, name):
+    """The forward with its log and the recurrence backward at full size, launched as
+    ``bench.py --backward`` launches them (addressing of keys and queries, one
+    sdm_recurrent_log call, one sdm_recurrent_backward call over all units and tokens). The
+    output gradient go is nonzero only on a window [0, P) of every unit: the loss then depends
+    only on those tokens, so the oracle's forward, log and backward over the window give every
+    gradient of a sampled unit (dv, dalpha, dbeta, both weight gradients and dM0), while past
+    the window every token gradient is exactly zero. The walk back over all T tokens must
+    restore M0 bit for bit in every unit. P is cut at the first token where the device's slot
+    lists differ from the oracle's (a tie), so that both sides differentiate the same slots."""
+    import torch
+    sh = W_[name]
+    units, _, _ = PLAN[name]
+    P = min(1024, sh.T)
+    log(f"[full] backward {name}: generating inputs")
+    inp = SI.make_inputs(sh)
+    dev = upload(inp, sh)
+    S = lib_shape(sh)
+    M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    sdm.init_from_M0(S, dev["M0"], M)
+    M0_dev = M.clone()
+    shp_w, shp_r = (sh.B, sh.H, sh.T, sh.W), (sh.B, sh.H, sh.T, sh.R)
+    wi = torch.empty(shp_w, dtype=torch.int32, device="cuda")
+    wg = torch.empty(shp_w, dtype=torch.float32, device="cuda")
+    ri = torch.empty(shp_r, dtype=torch.int32, device="cuda")
+    rg = torch.empty(shp_r, dtype=torch.float32, device="cuda")
+    sdm.address(S, dev["k"], dev["subkeys"], sh.W, wi, wg)
+    sdm.address(S, dev["q"], dev["subkeys"], sh.R, ri, rg)
+    torch.cuda.synchronize()
+    ref = {}
+    for (b, h) in units:
+        Up = unit_inputs(inp, sh, b, h, T=P)
+        owi, oww, _ = O.address(Up["k"], Up["C1"], Up["C2"], sh.kappa, sh.W)
+        ori, orw, _ = O.address(Up["q"], Up["C1"], Up["C2"], sh.kappa, sh.R)
+        gw, gr = wi[b, h, :P].cpu().numpy(), ri[b, h, :P].cpu().numpy()
+        _, _, fw = compare_indices(gw, owi, Up["k"], Up["C1"], Up["C2"], sh.N)
+        _, _, fr = compare_indices(gr, ori, Up["q"], Up["C1"], Up["C2"], sh.N)
+        assert not fw and not fr
+        diff = np.nonzero((gw != owi).any(1) | (gr != ori).any(1))[0]
+        if len(diff):
+            P = min(P, int(diff[0]))
+        ref[(b, h)] = (Up, owi, oww, ori, orw)
+    assert P >= 256, f"{name}: slot lists differ from the oracle's at token {P}"
+    rng = np.random.default_rng(29)
+    go_h = np.zeros((sh.B, sh.H, sh.T, sh.d_v), np.float32)
+    go_h[:, :, :P] = rng.standard_normal((sh.B, sh.H, P, sh.d_v)).astype(np.float32)
+    go = to_dev(go_h, "f32")
+    del go_h
+    o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+    xlog = empty_mem((sh.B, sh.H, sh.T, sh.W, sh.d_v), sh.mem_dtype)
+    ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    log(f"[full] backward {name}: log and backward B={sh.B} H={sh.H} T={sh.T}, go window {P}")
+    sdm.recurrent_log(S, wi, wg, ri, rg, dev["v"], dev["alpha"], dev["beta"], M, o, xlog, ws)
+    G = torch.zeros((sh.B, sh.H, sh.N, sh.d_v), dtype=torch.float32, device="cuda")
+    dv = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
+    dal = torch.empty((sh.B, sh.H, sh.T), dtype=torch.float32, device="cuda")
+    dbe = torch.empty_like(dal)
+    dwg = torch.empty(shp_w, dtype=torch.float32, device="cuda")
+    drg = torch.empty(shp_r, dtype=torch.float32, device="cuda")
+    bws = torch.empty(sdm.backward_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    sdm.recurrent_backward(S, wi, wg, ri, rg, dev["v"], dev["alpha"], dev["beta"], M, xlog, go, G, dv, dal, dbe,
+                           dwg, drg, bws)
+    torch.cuda.synchronize()
+    assert sdm.workspace_error(bws) == 0, "a workgroup of the backward gave up waiting"
+    assert torch.equal(M, M0_dev), "the undo over the whole sequence did not restore M0 bit for bit"
+    for nm, t in (("dv", dv), ("dalpha", dal), ("dbeta", dbe), ("dwgt", dwg), ("drgt", drg)):
+        nz = int(torch.count_nonzero(t[:, :, P:]))
+        assert nz == 0, f"{nm}: {nz} nonzero entries past the go window"
+    tol = tolerance(sh)
+    for (b, h), (Up, owi, oww, ori, orw) in ref.items():
+        wwp, rwp = oww[:P].astype(np.float32).astype(np.float64), orw[:P].astype(np.float32).astype(np.float64)
+        v, al, be = Up["v"][:P], Up["alpha"][:P], Up["beta"][:P]
+        _, MT = O.recurrence(Up["M0"], owi[:P], wwp, ori[:P], rwp, v, al, be, sh.mem_dtype)
+        xl = O.recurrence_log(Up["M0"], owi[:P], wwp, v, al, be, sh.mem_dtype)
+        g = O.recurrence_backward(MT, xl, owi[:P], wwp, ori[:P], rwp, v, al, be, go[b, h, :P].cpu().numpy()
+                                  .astype(np.float64))
+        out = {"dv": dv[b, h, :P], "dalpha": dal[b, h, :P], "dbeta": dbe[b, h, :P], "dwgt": dwg[b, h, :P],
+               "drgt": drg[b, h, :P], "dM0": G[b, h]}
+        errs = {k: rel_err(t.cpu().numpy(), g[k]) for k, t in out.items()}
+        log(f"[full] backward {name} unit ({b},{h}): " + " ".join(f"{k} {e:.1e}" for k, e in errs.items()) +
+            f" (tol {tol})")
+        for k, e in errs.items():
+            assert e < tol, k

@@ -278,7 +278,9 @@ sdm_status sdm_decay_state_init(const sdm_shape* shape, double* lam, double* lru
 
 /* Workspace bytes of sdm_forward_decay / sdm_recurrent_decay: sdm_workspace_bytes plus the
  * per-token cumulative log-decay [B,H,T+1] float64, one factor per token-slot [B,H,T,W+R]
- * float32 and the latest writer of each slot [B,H,N] int32. 0 if the shape is invalid. */
+ * float32, the latest writer of each slot [B,H,N] int32 and, when few units leave compute
+ * units idle, up to three more such int32 tables (one per extra token segment of the pass
+ * that finds each access's latest writer). 0 if the shape is invalid. */
 size_t sdm_workspace_bytes_decay(const sdm_shape* shape);
 
 /* sdm_recurrent with whole-table decay: for each unit, tokens in order,

@@ -203,6 +203,7 @@ WsLayout workspace_layout(const sdm_shape& S, bool decay) {
   L.ltok = o;
   L.fac = o;
   L.lastw = o;
+  L.segl = o;
   if (dataflow_supported(S, decay)) {
     o = align_up(o + dataflow_deps_bytes(S));
     L.sched = o;
@@ -214,6 +215,8 @@ WsLayout workspace_layout(const sdm_shape& S, bool decay) {
       o = align_up(o + tensor_bytes(S, (int64_t)S.W + S.R, 4));
       L.lastw = o;
       o = align_up(o + (size_t)S.B * S.H * (size_t)S.N * 4);
+      L.segl = o;
+      o = align_up(o + (size_t)(decay_segments(S) - 1) * S.B * S.H * (size_t)S.N * 4);
     }
   }
   L.total = o;

@@ -1002,7 +1002,7 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
     fac = (float*)(w + L.fac);
     e = launch_log_decay_scan(S, alpha, Ltok, dk->lrun, stream);
     if (e != hipSuccess) return e;
-    e = launch_decay_pass(S, pk, Ltok, dk->lam, fac, (int*)(w + L.lastw), c.win, stream);
+    e = launch_decay_pass(S, pk, Ltok, dk->lam, fac, (int*)(w + L.lastw), (int*)(w + L.segl), c.win, stream);
     if (e != hipSuccess) return e;
   }
   PipeArgs A;

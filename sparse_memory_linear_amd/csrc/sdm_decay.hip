@@ -17,8 +17,12 @@
 // for the other accesses decay_order_kernel walks the tokens of a unit in chunks of at
 // most `win` tokens, keeping per slot range (in LDS) the latest writer so far: an access
 // with no writer inside the window sees no write since its chunk began, so the record as
-// of the chunk start is its latest writer. decay_factor_kernel then forms every factor in
-// parallel, and decay_lam_kernel moves lam forward for the slots the call wrote.
+// of the chunk start is its latest writer. When a unit's slot ranges alone would leave
+// most compute units idle, its tokens are cut into segments walked in parallel:
+// decay_seglast_kernel first records each segment's latest writer of every slot, and a
+// segment's walk starts from the latest of those records over the segments before it.
+// decay_factor_kernel then forms every factor in parallel, and decay_lam_kernel moves lam
+// forward for the slots the call wrote.
 
 #include <algorithm>
 
@@ -78,26 +82,74 @@ struct PassArgs {
   double* lam;         // [U][N] in/out
   float* fac;          // [U][T][E] out (first holds each outside-window access's latest writer)
   int* lastw;          // [U][N] latest writer of each slot in this call, -1 = none
+  int* segl;           // [U][nseg - 1][N] latest writer of each slot within each segment but the last
   int U, T, W, E, P, span, chunk;
+  int nseg, seglen;    // token segments per unit (seglen a multiple of chunk)
   long long N;
 };
 
-// Order pass: one workgroup per (unit, range of `span` slots), tokens in chunks of at most
-// `win`. An access with no writer inside the window sees no write since its chunk began,
-// so the record of the latest writer as of the chunk start (LDS) is its latest writer; it
-// is left, as an int, in the access's factor word. Then the chunk's writes update the
-// record. The next chunk's slot words are loaded while a chunk is processed; the loop
-// touches nothing but LDS and registers otherwise. All ranges of a unit run on one XCD.
+// Latest writer of every slot of one range within one token segment (all but a unit's last
+// segment): the largest token of the segment that writes the slot, -1 if none does.
+__global__ void __launch_bounds__(kPassThreads) decay_seglast_kernel(PassArgs A) {
+  extern __shared__ int last_tok[];  // [span]
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int per_unit = A.P * (A.nseg - 1);
+  const int u = xcd + 8 * (k / per_unit), p = k % per_unit % A.P, seg = k % per_unit / A.P, tid = threadIdx.x;
+  if (u >= A.U) return;
+  const int E = A.E, W = A.W, span = A.span;
+  const long long n0 = (long long)p * span;
+  for (int i = tid; i < span; i += kPassThreads) last_tok[i] = -1;
+  __syncthreads();
+  const int t_lo = min(A.T, seg * A.seglen), t_hi = min(A.T, t_lo + A.seglen);
+  const uint32_t* pk = A.pk + ((size_t)u * A.T + t_lo) * E;
+  const int nw = (t_hi - t_lo) * E;
+  for (int q0 = 0; q0 < nw; q0 += kPerThread * kPassThreads) {
+    uint32_t w[kPerThread];
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+      const int q = q0 + tid + r * kPassThreads;
+      w[r] = q < nw ? pk[q] : kInvalid;
+    }
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+      const int q = q0 + tid + r * kPassThreads;
+      if ((w[r] & (kCoded | kInvalid)) == kInvalid || q % E >= W) continue;
+      const long long n = w[r] & kSlotMask;
+      if (n >= n0 && n < n0 + span) atomicMax(&last_tok[n - n0], t_lo + q / E);
+    }
+  }
+  __syncthreads();
+  int* out = A.segl + ((size_t)u * (A.nseg - 1) + seg) * A.N;
+  for (int i = tid; i < span; i += kPassThreads)
+    if (n0 + i < A.N) out[n0 + i] = last_tok[i];
+}
+
+// Order pass: one workgroup per (unit, range of `span` slots, token segment), tokens in
+// chunks of at most `win`. The record starts as the latest writer over the earlier
+// segments. An access with no writer inside the window sees no write since its chunk
+// began, so the record of the latest writer as of the chunk start (LDS) is its latest
+// writer; it is left, as an int, in the access's factor word. Then the chunk's writes
+// update the record. The next chunk's slot words are loaded while a chunk is processed;
+// the loop touches nothing but LDS and registers otherwise. All workgroups of a unit run
+// on one XCD.
 __global__ void __launch_bounds__(kPassThreads) decay_order_kernel(PassArgs A) {
   extern __shared__ int last_tok[];  // [span]
   const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
-  const int u = xcd + 8 * (k / A.P), p = k % A.P, tid = threadIdx.x;
+  const int per_unit = A.P * A.nseg;
+  const int u = xcd + 8 * (k / per_unit), p = k % per_unit % A.P, seg = k % per_unit / A.P, tid = threadIdx.x;
   if (u >= A.U) return;
-  const int T = A.T, W = A.W, E = A.E, span = A.span, C = A.chunk;
+  const int W = A.W, E = A.E, span = A.span, C = A.chunk;
+  const int t_lo = min(A.T, seg * A.seglen), T = min(A.T, t_lo + A.seglen);  // this segment: [t_lo, T)
   const long long n0 = (long long)p * span;
-  for (int i = tid; i < span; i += kPassThreads) last_tok[i] = -1;
-  const uint32_t* pk = A.pk + (size_t)u * T * E;
-  int* lt_out = (int*)(A.fac + (size_t)u * T * E);
+  const int* prev = A.segl + (size_t)u * (A.nseg - 1) * A.N + n0;
+  for (int i = tid; i < span; i += kPassThreads) {
+    int lt = -1;
+    for (int sg = 0; sg < seg; ++sg)
+      if (n0 + i < A.N) lt = max(lt, prev[(size_t)sg * A.N + i]);
+    last_tok[i] = lt;
+  }
+  const uint32_t* pk = A.pk + (size_t)u * A.T * E;
+  int* lt_out = (int*)(A.fac + (size_t)u * A.T * E);
   const int per = C * E;  // accesses per chunk, at most kPerThread * kPassThreads
   uint32_t cur[kPerThread], nxt[kPerThread];
   auto load = [&](int c0, uint32_t (&w)[kPerThread]) {
@@ -108,9 +160,9 @@ __global__ void __launch_bounds__(kPassThreads) decay_order_kernel(PassArgs A) {
       w[r] = (q < per && i < (long long)T * E) ? pk[i] : kInvalid;
     }
   };
-  load(0, cur);
+  load(t_lo, cur);
   __syncthreads();
-  for (int c0 = 0; c0 < T; c0 += C) {
+  for (int c0 = t_lo; c0 < T; c0 += C) {
     load(c0 + C, nxt);
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
@@ -133,6 +185,7 @@ __global__ void __launch_bounds__(kPassThreads) decay_order_kernel(PassArgs A) {
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) cur[r] = nxt[r];
   }
+  if (seg != A.nseg - 1) return;  // the last segment's record is the call's latest writer
   int* lastw = A.lastw + (size_t)u * A.N;
   for (int i = tid; i < span; i += kPassThreads)
     if (n0 + i < A.N) lastw[n0 + i] = last_tok[i];
@@ -196,8 +249,18 @@ hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double*
 
 int decay_pass_ranges(const sdm_shape& S) { return (int)((S.N + kPassSlotsMax - 1) / kPassSlotsMax); }
 
+// Token segments per unit for the order pass: enough (at most 4) for the workgroups to cover
+// the 256 compute units, each segment at least 2048 tokens long (shorter walks do not repay
+// the extra pass).
+int decay_segments(const sdm_shape& S) {
+  const long long wgs = (long long)S.B * S.H * decay_pass_ranges(S);
+  int nseg = wgs >= 256 ? 1 : (int)std::min<long long>(4, 256 / wgs);
+  while (nseg > 1 && S.T < 2048LL * nseg) --nseg;
+  return nseg;
+}
+
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,
-                             int* lastw, int win, hipStream_t stream) {
+                             int* lastw, int* segl, int win, hipStream_t stream) {
   PassArgs A;
   A.pk = pk;
   A.L = L;
@@ -214,9 +277,21 @@ hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const doubl
   // the longest chunk inside the window whose accesses fit the threads' registers
   A.chunk = std::min(win, kPerThread * kPassThreads / A.E);
   if (A.chunk < 1) return hipErrorInvalidValue;
+  A.segl = segl;
+  A.nseg = decay_segments(S);
+  A.seglen = (S.T + A.nseg - 1) / A.nseg;
+  A.seglen = (A.seglen + A.chunk - 1) / A.chunk * A.chunk;
   const int groups = (A.U + 7) / 8;
-  hipLaunchKernelGGL(decay_order_kernel, dim3(8 * groups * A.P), dim3(kPassThreads), (size_t)A.span * 4, stream, A);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (A.nseg > 1) {
+    hipLaunchKernelGGL(decay_seglast_kernel, dim3(8 * groups * A.P * (A.nseg - 1)), dim3(kPassThreads),
+                       (size_t)A.span * 4, stream, A);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(decay_order_kernel, dim3(8 * groups * A.P * A.nseg), dim3(kPassThreads), (size_t)A.span * 4,
+                     stream, A);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long acc = (long long)A.U * A.T * A.E;
   hipLaunchKernelGGL(decay_factor_kernel, dim3((unsigned)((acc + 255) / 256)), dim3(256), 0, stream, A);

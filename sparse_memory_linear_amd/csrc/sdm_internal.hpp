@@ -25,6 +25,7 @@ struct WsLayout {
   size_t sched;                 // scheduler counters and done flags
   size_t ltok, fac, lastw;      // whole-table decay: log-decay per token [U][T+1], factors [U][T][E],
                                 // latest writer per slot [U][N]
+  size_t segl;                  // whole-table decay: latest writer per token segment [U][nseg-1][N]
   size_t total;
 };
 WsLayout workspace_layout(const sdm_shape& S, bool decay = false);
@@ -72,8 +73,9 @@ hipError_t launch_backward(const sdm_shape& S, const int32_t* widx, const float*
                            float* dwgt, float* drgt, void* ws, hipStream_t stream);
 
 hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun, hipStream_t stream);
+int decay_segments(const sdm_shape& S);  // token segments of the decay order pass
 hipError_t launch_decay_pass(const sdm_shape& S, const uint32_t* pk, const double* L, double* lam, float* fac,
-                             int* lastw, int win, hipStream_t stream);
+                             int* lastw, int* segl, int win, hipStream_t stream);
 hipError_t launch_gates(const sdm_shape& S, const float* a, const float* b, const float* A_log, const float* dt_bias,
                         float* alpha, float* beta, hipStream_t stream);
 hipError_t launch_output_gate(const sdm_shape& S, const float* o, const void* z, const float* w, float eps,

@@ -22,6 +22,12 @@ CASES = {
     "small_T160": W_["small"].replace(B=1, H=2, T=160),
     # the 8B-scale shape (bf16 table, s = 512, repeated keys), ragged token count
     "layer_8b_T100": W_["layer_8b_long"].replace(B=1, H=2, T=100),
+    # few units and long enough sequences for the order pass to cut each unit's tokens into
+    # parallel segments (4 and 2 segments, the last one ragged): N = 4096 keeps the oracle's
+    # dense decay of every row cheap
+    "segments4_T8300": W_["small"].replace(B=1, H=2, T=8300, N=4096, d_k=64, d_v=32),
+    "segments2_T4200_bf16": W_["layer_8b_long"].replace(B=1, H=2, T=4200, N=4096, d_k=64, d_v=32, kappa=16,
+                                                         W=16, R=16),
 }
 
 

@@ -286,12 +286,19 @@ def test_fullsize_decay_variant(sdm):
                    SI.widen(from_dev(Ma, sh.mem_dtype), sh.mem_dtype)) < 1e-2
     # slots no token wrote keep lam = 0 (their value is still M0 times the whole decay);
     # written ones hold the (negative) log-decay after their last writer
+    # (the order pass runs this shape in four parallel token segments: each written slot's
+    # lam must be the cumulative log-decay through its latest writer over the whole call)
     gw = wo.cpu().numpy()
     for b, h in ((0, 0), (0, 7)):
         touched = np.zeros(sh.N, bool)
         touched[gw[b, h].ravel()] = True
         lam_h = lama[b, h].cpu().numpy()
         assert np.all(lam_h[~touched] == 0.0) and np.all(lam_h[touched] < 0.0)
+        last = np.full(sh.N, -1, np.int64)
+        np.maximum.at(last, gw[b, h].ravel(), np.repeat(np.arange(sh.T), sh.W))
+        Lc = np.cumsum(np.maximum(np.log(inp["alpha"][b, h].astype(np.float64)), -1000.0))
+        assert np.allclose(lam_h[touched], Lc[last[touched]], rtol=1e-9, atol=1e-9), \
+            "lam of a written slot is not the log-decay through its latest writer"
 
 
 @pytest.mark.parametrize("name", list(PLAN))

@@ -79,15 +79,18 @@ def backward_bytes_per_token_head(sh: SI.Shape) -> int:
 RECURRENCE_SOURCES = ("sdm_dataflow.hip", "sdm_device.hpp")
 CHUNKED_SOURCES = ("sdm_chunked.hip", "sdm_device.hpp")
 BACKWARD_SOURCES = ("sdm_backward.hip", "sdm_device.hpp")
+DECAY_SOURCES = ("sdm_decay.hip", "sdm_dataflow.hip", "sdm_device.hpp")
 
 
 def kernel_source_hash(kind: str = "recurrence") -> str:
     """Hash of the sources of the recurrence kernels (dependency pass and pipeline), with
     kind="chunked" of the chunkwise kernels (preparation and apply), with kind="backward" of
-    the recurrence backward (preparation and walk)."""
+    the recurrence backward (preparation and walk), with kind="decay" of the whole-table
+    decay recurrence (decay passes, dependency pass and pipeline)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc")
-    srcs = {"chunked": CHUNKED_SOURCES, "backward": BACKWARD_SOURCES}.get(kind, RECURRENCE_SOURCES)
+    srcs = {"chunked": CHUNKED_SOURCES, "backward": BACKWARD_SOURCES, "decay": DECAY_SOURCES}.get(kind,
+                                                                                                 RECURRENCE_SOURCES)
     for f in srcs:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
@@ -95,8 +98,8 @@ def kernel_source_hash(kind: str = "recurrence") -> str:
 
 
 def traffic_from_profile(workload: str, kind: str = "recurrence"):
-    """HBM bytes per launch of the measured kernel (kind "recurrence", "chunked" or
-    "backward") from the committed counter summary, if it was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of the measured kernel (kind "recurrence", "chunked", "backward"
+    or "decay") from the committed counter summary, if it was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
     if not os.path.exists(p):
         return None
@@ -292,9 +295,8 @@ def main():
     if args.backward:
         assert S.workspace_error(bws) == 0, "a workgroup of the backward gave up waiting"
 
-    traffic = (None if args.decay else
-               traffic_from_profile(sh.name, "chunked" if args.chunked else "backward" if args.backward else
-                                    "recurrence"))
+    traffic = traffic_from_profile(sh.name, "chunked" if args.chunked else "backward" if args.backward else
+                                   "decay" if args.decay else "recurrence")
     out = {
         "metric": (METRIC_BACKWARD if args.backward else METRIC),
         "value": value,

@@ -33,7 +33,7 @@ namespace sdm {
 
 namespace {
 
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;
 constexpr int kPassThreads = 1024;
 constexpr int kPerThread = 8;                  // accesses per thread and chunk (chunk * (W + R) <= 8192)
 constexpr int kPassSlotsMax = 32768;           // slots of one workgroup's LDS record (128 KB)
@@ -46,34 +46,73 @@ __device__ __forceinline__ double log_gate(float a) { return fmax(log((double)a)
 __device__ __forceinline__ float decay_factor(double to, double from) { return expf((float)(to - from)); }
 
 // L[u][0] = lrun[u]; L[u][t + 1] = L[u][t] + log alpha[u][t]; then lrun[u] = L[u][T].
-__global__ void __launch_bounds__(kScanThreads) log_decay_scan_kernel(const float* alpha, double* L, double* lrun,
-                                                                      int T) {
+// Three steps, so that a long sequence is scanned by many workgroups: each block of
+// kScanBlock tokens sums its log gates into L at its end boundary e_b = min((b+1)*kScanBlock,
+// T); one thread per unit turns those sums into running totals (from lrun) in place; each
+// block then scans its own tokens from the total at its start and writes every entry but its
+// end boundary, which already holds the running total.
+constexpr int kScanPer = 8;                         // tokens per thread
+constexpr int kScanBlock = kScanThreads * kScanPer;  // tokens per block
+
+__device__ __forceinline__ double block_sum_f64(double v, double* part) {
+  const int tid = threadIdx.x;
+  part[tid] = v;
+  __syncthreads();
+  for (int off = kScanThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
+    __syncthreads();
+  }
+  return part[0];
+}
+
+__global__ void __launch_bounds__(kScanThreads) log_decay_sums_kernel(const float* alpha, double* L, int T) {
   __shared__ double part[kScanThreads];
-  const int u = blockIdx.x, tid = threadIdx.x;
+  const int u = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
   const float* a = alpha + (size_t)u * T;
-  double* Lu = L + (size_t)u * (T + 1);
-  const int per = (T + kScanThreads - 1) / kScanThreads;
-  const int lo = tid * per, hi = min(T, lo + per);
+  const int lo = b * kScanBlock + tid * kScanPer, hi = min(T, lo + kScanPer);
   double s = 0.0;
   for (int t = lo; t < hi; ++t) s += log_gate(a[t]);
+  const double tot = block_sum_f64(s, part);
+  if (tid == 0) L[(size_t)u * (T + 1) + min((b + 1) * kScanBlock, T)] = tot;
+}
+
+__global__ void log_decay_totals_kernel(double* L, double* lrun, int T, int U) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= U) return;
+  double* Lu = L + (size_t)u * (T + 1);
+  double run = lrun[u];
+  Lu[0] = run;
+  for (int e = kScanBlock; e - kScanBlock < T; e += kScanBlock) {
+    const int eb = min(e, T);
+    run += Lu[eb];
+    Lu[eb] = run;
+  }
+  lrun[u] = run;
+}
+
+__global__ void __launch_bounds__(kScanThreads) log_decay_scan_kernel(const float* alpha, double* L, int T) {
+  __shared__ double part[kScanThreads];
+  const int u = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
+  const float* a = alpha + (size_t)u * T;
+  double* Lu = L + (size_t)u * (T + 1);
+  const int lo = b * kScanBlock + tid * kScanPer, hi = min(T, lo + kScanPer);
+  const int eb = min((b + 1) * kScanBlock, T);
+  double s = 0.0;
+  for (int t = lo; t < hi; ++t) s += log_gate(a[t]);
+  // inclusive scan of the per-thread sums (Hillis-Steele over LDS)
   part[tid] = s;
   __syncthreads();
-  // inclusive scan of the per-thread sums (Hillis-Steele over LDS)
   for (int off = 1; off < kScanThreads; off <<= 1) {
     const double add = tid >= off ? part[tid - off] : 0.0;
     __syncthreads();
     part[tid] += add;
     __syncthreads();
   }
-  const double base = lrun[u];
-  double run = base + (tid > 0 ? part[tid - 1] : 0.0);
-  if (tid == 0) Lu[0] = base;
+  double run = Lu[b * kScanBlock] + (tid > 0 ? part[tid - 1] : 0.0);
   for (int t = lo; t < hi; ++t) {
     run += log_gate(a[t]);
-    Lu[t + 1] = run;
+    if (t + 1 != eb) Lu[t + 1] = run;
   }
-  __syncthreads();
-  if (tid == 0) lrun[u] = base + part[kScanThreads - 1];
 }
 
 struct PassArgs {
@@ -243,8 +282,19 @@ __global__ void __launch_bounds__(256) materialize_kernel(const MemT* M, const d
 
 hipError_t launch_log_decay_scan(const sdm_shape& S, const float* alpha, double* L, double* lrun,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(log_decay_scan_kernel, dim3(S.B * S.H), dim3(kScanThreads), 0, stream, alpha, L, lrun, S.T);
-  return hipGetLastError();
+  const int U = S.B * S.H, nb = (S.T + kScanBlock - 1) / kScanBlock;
+  hipError_t e;
+  if (nb > 0) {
+    hipLaunchKernelGGL(log_decay_sums_kernel, dim3(nb, U), dim3(kScanThreads), 0, stream, alpha, L, S.T);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(log_decay_totals_kernel, dim3((U + 63) / 64), dim3(64), 0, stream, L, lrun, S.T, U);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (nb > 0) {
+    hipLaunchKernelGGL(log_decay_scan_kernel, dim3(nb, U), dim3(kScanThreads), 0, stream, alpha, L, S.T);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int decay_pass_ranges(const sdm_shape& S) { return (int)((S.N + kPassSlotsMax - 1) / kPassSlotsMax); }

@@ -53,10 +53,14 @@ typedef enum {
 
 typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
 
-/* Problem shape. Limits checked by every call:
- *   B, H >= 1; T >= 1 (T may be 0 only where stated); N = s*s a perfect square with
- *   4 <= N <= 2^24; d_k even, 2 <= d_k <= 256; 1 <= d_v <= 512 with d_v*sizeof(mem) a
- *   multiple of 16 bytes; 1 <= kappa <= min(s, 64); 1 <= W, R <= min(kappa*kappa, 64). */
+/* Problem shape. Limits checked by every call (SDM_ERR_INVALID_ARG for a malformed shape,
+ * SDM_ERR_UNSUPPORTED for a valid one past what the kernels implement):
+ *   B, H >= 1; T >= 1 (T may be 0 only where stated); B*T <= 2^30 - 1; B*H <= 65535*64;
+ *   N = s*s a perfect square with 4 <= N <= 262144 (s <= 512); d_k even, 2 <= d_k <= 256;
+ *   d_v >= 1 with a table row of d_v*sizeof(mem) bytes a multiple of 16 and at most 1024
+ *   (d_v <= 256 for a float32 table, <= 512 for bf16); 1 <= kappa <= min(s, 64);
+ *   1 <= W, R <= min(kappa*kappa, 64). Some entry points narrow these further (stated at
+ *   each). */
 typedef struct {
   int32_t B, H, T;      /* batch, heads, tokens in this call                            */
   int64_t N;            /* slots per head (perfect square; s = sqrt(N) sub-keys/half)   */
@@ -97,7 +101,9 @@ sdm_status sdm_init_from_M0(const sdm_shape* shape, const void* M0, void* M, voi
  *   score   [B, H, T, n_sel] float32 out, may be NULL: the selected scores
  * Per half the kappa best sub-keys are kept, the kappa*kappa sums are ranked, and the
  * first n_sel are returned. Every ranking orders by float32 score descending, then by
- * index ascending. Scores are float32 sums of exact products (bf16) or float32 products. */
+ * index ascending. Scores are float32 sums of exact products (bf16) or float32 products;
+ * where two slots' exact scores agree to within float32 rounding, the order between them
+ * can differ from an exact-arithmetic ranking (the two are then an equally good choice). */
 sdm_status sdm_address(const sdm_shape* shape, const void* x, const void* subkeys, int32_t n_sel,
                        int32_t* idx, float* weight, float* score, void* stream);
 

@@ -43,12 +43,12 @@ import numpy as np
 __all__ = [
     "round_bf16",
     "round_mem",
-    "decision_f32",
     "half_scores",
     "top_order",
     "product_key_select",
     "softmax",
     "address",
+    "slot_weights",
     "recurrence",
     "forward_unit",
     "forward",
@@ -89,12 +89,6 @@ def round_mem(x: np.ndarray, mem_dtype: str) -> np.ndarray:
     raise ValueError(mem_dtype)
 
 
-def decision_f32(x: np.ndarray) -> np.ndarray:
-    """Scores on which slot selection is decided: float32, the precision the device takes
-    the same integer decision in (READING R18). Weights still use the float64 scores."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
-
-
 # ----------------------------------------------------------------------------- addressing
 def half_scores(x: np.ndarray, C1: np.ndarray, C2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Product-key scores of the two halves of x (PL §2 "Product Key Memory"; Atlas
@@ -125,23 +119,23 @@ def product_key_select(x: np.ndarray, C1: np.ndarray, C2: np.ndarray, kappa: int
        sigma1[i] + sigma2[j];
     4. keep the first n_sel candidates by (score desc, slot asc).
 
-    Returns (slots [.., n_sel] int64, exact scores [.., n_sel] float64) in rank order.
-    Decisions (steps 2 and 4) compare float32-rounded scores (READING R18)."""
+    Returns (slots [.., n_sel] int64, scores [.., n_sel] float64) in rank order. Every
+    decision compares the float64 scores (READING R18: the plain reading, exact arithmetic
+    up to float64 rounding; a device deciding in a narrower precision can order two slots
+    differently only where their scores agree to within that precision, which the parity
+    comparison counts as a tie, READING R17)."""
     x2 = np.atleast_2d(np.asarray(x, dtype=np.float64))
     s = C1.shape[0]
     s1, s2 = half_scores(x2, C1, C2)
-    d1, d2 = decision_f32(s1), decision_f32(s2)
-    sub = np.broadcast_to(np.arange(s), d1.shape)
-    I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)   # [T, kappa]
-    I2 = np.take_along_axis(sub, top_order(d2, sub, kappa), axis=-1)
+    sub = np.broadcast_to(np.arange(s), s1.shape)
+    I1 = np.take_along_axis(sub, top_order(s1, sub, kappa), axis=-1)   # [T, kappa]
+    I2 = np.take_along_axis(sub, top_order(s2, sub, kappa), axis=-1)
     T = x2.shape[0]
     slots = (I1[:, :, None] * s + I2[:, None, :]).reshape(T, kappa * kappa)
-    exact = (np.take_along_axis(s1, I1, -1)[:, :, None] + np.take_along_axis(s2, I2, -1)[:, None, :]).reshape(T, -1)
-    dec = decision_f32(np.take_along_axis(d1, I1, -1)[:, :, None] + np.take_along_axis(d2, I2, -1)[:, None, :])
-    dec = dec.reshape(T, -1)
-    pick = top_order(dec, slots, n_sel)
+    cand = (np.take_along_axis(s1, I1, -1)[:, :, None] + np.take_along_axis(s2, I2, -1)[:, None, :]).reshape(T, -1)
+    pick = top_order(cand, slots, n_sel)
     sel = np.take_along_axis(slots, pick, -1)
-    sc = np.take_along_axis(exact, pick, -1)
+    sc = np.take_along_axis(cand, pick, -1)
     if np.ndim(x) == 1:
         return sel[0], sc[0]
     return sel, sc
@@ -168,6 +162,21 @@ def address(x, C1, C2, kappa: int, n_sel: int, block: int = 4096):
     idx = np.concatenate(outs_i, 0) if outs_i else np.zeros((0, n_sel), np.int64)
     sc = np.concatenate(outs_s, 0) if outs_s else np.zeros((0, n_sel))
     return idx, softmax(sc) if sc.size else sc, sc
+
+
+def slot_weights(x, C1, C2, slots):
+    """Weights and scores of given slot lists: slot n = i*s + j of row t scores
+    x_t[:h].C1[i] + x_t[h:].C2[j] (READING R5), and the weights are the softmax over the
+    listed slots' scores (PL §4 "SDM Configuration"; READING R6). x [T, d_k], slots [T, n].
+    This is the last step of ``address`` applied to slot lists chosen elsewhere (where a
+    tie let another ranking pick a different but equally scored slot). Returns
+    (weights [T, n], scores [T, n]) in float64."""
+    x2 = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    sl = np.atleast_2d(np.asarray(slots, dtype=np.int64))
+    s = C1.shape[0]
+    s1, s2 = half_scores(x2, C1, C2)
+    sc = np.take_along_axis(s1, sl // s, -1) + np.take_along_axis(s2, sl % s, -1)
+    return softmax(sc), sc
 
 
 # ----------------------------------------------------------------------------- recurrence

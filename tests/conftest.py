@@ -12,3 +12,17 @@ if HERE not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    config.addinivalue_line("markers", "oracle_pool: runs the oracle in a pool of worker processes")
+
+
+def pytest_collection_modifyitems(session, config, items):
+    # the oracle pool is forked now, before any test touches the GPU: its workers never hold
+    # GPU state and only run the numpy oracle
+    if any(item.get_closest_marker("oracle_pool") for item in items):
+        import parity
+        parity.start_pool()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    import parity
+    parity.stop_pool()

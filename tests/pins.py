@@ -43,17 +43,17 @@ def _rand_unit(rng, T, d_k, d_v, s, quantised=False):
 
 
 def brute_force_top(x, C1, C2, n_sel):
-    """Score every slot n = i*s + j as sigma1[i] + sigma2[j] (both halves rounded to float32,
-    summed in float32 -- the decision precision) and take the first n_sel by (score desc,
-    slot asc). Written independently of the oracle: explicit loops over all N slots."""
+    """Score every slot n = i*s + j as sigma1[i] + sigma2[j] (each half a correctly rounded
+    float64 dot product, the two halves added in float64) and take the first n_sel by
+    (score desc, slot asc). Written independently of the oracle: explicit loops over all N
+    slots."""
     s, h = C1.shape
-    sig1 = [np.float32(sum(float(x[c]) * float(C1[i, c]) for c in range(h))) for i in range(s)]
-    sig2 = [np.float32(sum(float(x[h + c]) * float(C2[j, c]) for c in range(h))) for j in range(s)]
+    sig1 = [math.fsum(float(x[c]) * float(C1[i, c]) for c in range(h)) for i in range(s)]
+    sig2 = [math.fsum(float(x[h + c]) * float(C2[j, c]) for c in range(h)) for j in range(s)]
     cands = []
     for i in range(s):
         for j in range(s):
-            sc = np.float32(sig1[i] + sig2[j])   # float32 + float32 -> float32 (IEEE)
-            cands.append((-float(sc), i * s + j))
+            cands.append((-(sig1[i] + sig2[j]), i * s + j))
     cands.sort()
     return [n for _, n in cands[:n_sel]]
 
@@ -553,6 +553,75 @@ def pin_chunkwise_equals_sequential(O):
             assert np.allclose(M1, M2, rtol=1e-10, atol=1e-10), (trial, C)
 
 
+def pin_chunkwise_bf16_rounding_point(O):
+    """Where the chunkwise form rounds a bf16 table (READING R26; PL App. A.1: Phase 2 writes
+    the state back once per chunk). Worked by hand on one slot, d_v = 1, W = R = 1 with
+    weight 1, two tokens that both write and then read slot 0; every value is a short
+    dyadic fraction, so float64 holds each one exactly and the only rounding is to bf16
+    (8 significant bits, nearest-even):
+
+      M0 = 97/64; token 0: alpha 1, beta 3/4, v 1; token 1: alpha 3/4, beta 1/4, v 1.
+      delta_0 = 3/4 (1 - 97/64) = -99/256, new row y_0 = 97/64 - 99/256 = 289/256.
+      Token by token: 289/256 is the midpoint of 288/256 and 290/256, so it rounds to the
+        even 9/8; o_0 = 9/8. Token 1: delta_1 = 1/4 (1 - 3/4 * 9/8) = 5/128,
+        y_1 = 27/32 + 5/128 = 113/128 (exact in bf16); o_1 = final row = 113/128.
+      One chunk of two tokens: token 1 sees the unrounded 289/256, so
+        delta_1 = 1/4 (1 - 867/1024) = 157/4096 and o_0 = 289/256,
+        o_1 = 867/1024 + 157/4096 = 3625/4096; the write-back rounds once:
+        3625/4096 = 226.5625/256 -> 227/256.
+      Rounding the chunk-start row after its decay but before adding the deltas would give
+        round(3/4 * 97/64) = round(291/256) = 292/256 (the even neighbour), then
+        292/256 - 297/1024 + 157/4096 = 3641/4096 -> 228/256, not 227/256.
+      With chunk length 1 every chunk writes its rows back at once: the table equals the
+        token-by-token table (113/128), and o_0 is the unrounded 289/256 (a token reading a
+        row it writes sees it before the write-back rounds it).
+    """
+    M0 = np.array([[97 / 64], [0.0]])
+    widx = [np.array([0]), np.array([0])]
+    one = [np.array([1.0]), np.array([1.0])]
+    v = np.array([[1.0], [1.0]])
+    alpha = np.array([1.0, 0.75])
+    beta = np.array([0.75, 0.25])
+    o, M = O.recurrence(M0, widx, one, widx, one, v, alpha, beta, "bf16")
+    assert o[0, 0] == 9 / 8 and o[1, 0] == 113 / 128 and M[0, 0] == 113 / 128, (o, M)
+    o, M = O.chunkwise_recurrence(M0, widx, one, widx, one, v, alpha, beta, 2, "bf16")
+    assert o[0, 0] == 289 / 256 and o[1, 0] == 3625 / 4096 and M[0, 0] == 227 / 256, (o, M)
+    o, M = O.chunkwise_recurrence(M0, widx, one, widx, one, v, alpha, beta, 1, "bf16")
+    assert o[0, 0] == 289 / 256 and o[1, 0] == 113 / 128 and M[0, 0] == 113 / 128, (o, M)
+    assert M[1, 0] == 0.0
+
+
+def pin_chunkwise_chunk1_bf16_is_token_rule(O):
+    """Chunk length 1 with a bf16 table is the token-by-token bf16 rule (READING R26 rounds
+    at each chunk's write-back, and a chunk of one token writes back at its own write, where
+    READING R10 rounds): the final table bit for bit, and every output up to float64
+    summation order, on tables where rows are rewritten often and no token reads a slot it
+    writes itself (that case is worked by hand in ``pin_chunkwise_bf16_rounding_point``)."""
+    rng = np.random.default_rng(53)
+    for trial in range(10):
+        N, d_v = int(rng.integers(8, 14)), 4
+        T = int(rng.integers(3, 40))
+        W, R = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        widx, ridx = [], []
+        for _ in range(T):
+            perm = rng.permutation(N)
+            widx.append(perm[:W])
+            ridx.append(perm[W:W + R])
+        wgt, rgt = rng.random((T, W)) + 0.05, rng.random((T, R)) + 0.05
+        v = rng.standard_normal((T, d_v))
+        alpha = rng.uniform(0.2, 0.99, T)
+        beta = rng.uniform(0.05, 1.0, T)
+        M0 = O.round_bf16(rng.standard_normal((N, d_v)))
+        o1, M1 = O.recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, "bf16")
+        o2, M2 = O.chunkwise_recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, 1, "bf16")
+        assert np.array_equal(M1, M2), trial
+        assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12), trial
+        # longer chunks differ from the token rule by the rounding they skip, no more
+        o3, M3 = O.chunkwise_recurrence(M0, widx, wgt, ridx, rgt, v, alpha, beta, 8, "bf16")
+        scale = np.max(np.abs(M1))
+        assert np.max(np.abs(M3 - M1)) <= 0.05 * scale, trial
+
+
 ALL_PINS = [
     pin_round_bf16,
     pin_pk_equals_brute_force,
@@ -577,4 +646,6 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_address_backward_finite_differences,
     pin_chunkwise_equals_sequential,
+    pin_chunkwise_bf16_rounding_point,
+    pin_chunkwise_chunk1_bf16_is_token_rule,
 ]

@@ -142,14 +142,18 @@ def test_forward_decay_parity_and_state_carry(sdm, name):
     for b in range(sh.B):
         for h in range(sh.H):
             U = unit_inputs(inp, sh, b, h)
-            r = O.forward_unit(U["q"], U["k"], U["v"], U["alpha"], U["beta"], U["C1"], U["C2"], U["M0"], sh.kappa,
-                               sh.W, sh.R, sh.mem_dtype, decay="table")
-            _, cw, fw = compare_indices(gw[b, h], r["widx"], U["k"], U["C1"], U["C2"], sh.N)
-            _, cr, fr = compare_indices(gr[b, h], r["ridx"], U["q"], U["C1"], U["C2"], sh.N)
+            oi_w, _, _ = O.address(U["k"], U["C1"], U["C2"], sh.kappa, sh.W)
+            oi_r, _, _ = O.address(U["q"], U["C1"], U["C2"], sh.kappa, sh.R)
+            _, _, fw = compare_indices(gw[b, h], oi_w, U["k"], U["C1"], U["C2"], sh.N)
+            _, _, fr = compare_indices(gr[b, h], oi_r, U["q"], U["C1"], U["C2"], sh.N)
             assert not fw and not fr
-            first = min(cw + cr) if (cw or cr) else sh.T
-            eo = rel_err(go[b, h][:first], r["o"][:first]) if first else 0.0
-            em = rel_err(gM[b, h], r["M"]) if first == sh.T else 0.0
+            # the oracle on the device's slot lists (its own wherever no tie occurred)
+            ww, _ = O.slot_weights(U["k"], U["C1"], U["C2"], gw[b, h])
+            rw, _ = O.slot_weights(U["q"], U["C1"], U["C2"], gr[b, h])
+            ro_, rM_ = O.recurrence(U["M0"], gw[b, h], ww, gr[b, h], rw, U["v"], U["alpha"], U["beta"], sh.mem_dtype,
+                                    decay="table")
+            eo = rel_err(go[b, h], ro_)
+            em = rel_err(gM[b, h], rM_)
             log(f"[decay forward] {name} unit ({b},{h}): o {eo:.2e} table {em:.2e} (tol {tol})")
             assert eo < tol and em < tol
     # two calls on the carried state
@@ -208,14 +212,17 @@ def test_decode_decay_parity(sdm):
             C1, C2 = sk[0], sk[1]
             M0 = SI.widen(params["M0"][h], sh.mem_dtype)
             U = {k: SI.widen(pre[b][k][0, h], sh.in_dtype) for k in ("q", "k", "v")}
-            r = O.forward_unit(U["q"], U["k"], U["v"], pre[b]["alpha"][0, h].astype(np.float64),
-                               pre[b]["beta"][0, h].astype(np.float64), C1, C2, M0, sh.kappa, sh.W, sh.R,
-                               sh.mem_dtype, decay="table")
-            _, cw, fw = compare_indices(gw[b, h], r["widx"], U["k"], C1, C2, sh.N)
-            _, cr, fr = compare_indices(gr[b, h], r["ridx"], U["q"], C1, C2, sh.N)
+            oi_w, _, _ = O.address(U["k"], C1, C2, sh.kappa, sh.W)
+            oi_r, _, _ = O.address(U["q"], C1, C2, sh.kappa, sh.R)
+            _, _, fw = compare_indices(gw[b, h], oi_w, U["k"], C1, C2, sh.N)
+            _, _, fr = compare_indices(gr[b, h], oi_r, U["q"], C1, C2, sh.N)
             assert not fw and not fr
-            if cw or cr:
-                continue  # a set-changing tie in the prefill: this unit's tables differ legitimately
+            # the oracle's prefill on the device's slot lists (its own wherever no tie occurred)
+            ww, _ = O.slot_weights(U["k"], C1, C2, gw[b, h])
+            rw, _ = O.slot_weights(U["q"], C1, C2, gr[b, h])
+            _, Mpre = O.recurrence(M0, gw[b, h], ww, gr[b, h], rw, U["v"], pre[b]["alpha"][0, h].astype(np.float64),
+                                   pre[b]["beta"][0, h].astype(np.float64), sh.mem_dtype, decay="table")
+            r = {"M": Mpre}
             od, Md, _ = O.decode_step_unit(r["M"], SI.widen(params["q"][b, h, 0], sh.in_dtype),
                                            SI.widen(params["k"][b, h, 0], sh.in_dtype),
                                            SI.widen(params["v"][b, h, 0], sh.in_dtype), float(params["alpha"][b, h, 0]),

@@ -1,26 +1,31 @@
 """The HIP path at full workload sizes, in the launch configuration the benchmark times,
-checked where the oracle can follow it:
+checked against the oracle (one unit per task in a pool of worker processes):
 
-* slot indices of tokens sampled over the whole sequence (addressing is per token) are
-  compared position by position, ties counted;
-* outputs over a long prefix of sampled units are compared with the oracle run on that
-  prefix (o_t depends only on tokens up to t), up to the first tie that changes a slot set;
-* table rows that no token writes stay bit-identical to M0, in every checked unit;
-* the whole sequence in two calls on the carried table equals one call, bit for bit;
-* the chunkwise two-phase recurrence likewise: sampled units' outputs over a prefix against
-  the oracle's chunkwise form, untouched rows still M0;
-* decode: one step over all B x H tables, sampled units checked against the oracle after
-  the oracle's own prefill (other tables hold M0 only; units are independent);
+* forward, every workload but decode: every unit over the whole sequence -- slot lists
+  position by position with ties counted, then o at every token and the whole final table
+  against the oracle run on the device's slot lists with the oracle's own float64 weights
+  (a tie that picked an equally scored slot does not cascade), rows no token writes
+  bit-identical to M0; the same sequence in two calls equals one call bit for bit;
+* the chunkwise two-phase recurrence: the same procedure for every unit against the
+  oracle's chunkwise form, and against the token-by-token rule within the tolerance;
+* decode: one step over all 64 x 16 tables, every unit checked, after a prefill of four
+  sequences that is itself checked in full;
 * the backward: with the output gradient nonzero only on a window of leading tokens, every
   gradient of a sampled unit against the oracle's backward over that window, exact zeros
   past it, and M0 restored bit for bit by the walk back over the whole sequence.
+
+Per-workload records (units and token-heads compared, tie counts, worst errors) are
+written to gpurun_out/parity_fullsize.json.
 """
+import time
+
 import numpy as np
 import pytest
 
 import oracle.sdm_oracle as O
 import sdm_inputs as SI
-from parity import compare_indices, empty_mem, from_dev, lib_shape, log, rel_err, to_dev, tolerance
+from parity import (SharedDir, compare_indices, empty_mem, from_dev, lib_shape, log, pool, pool_size, rel_err,
+                    summarise, to_dev, tolerance, unit_parity, write_record)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,11 +80,42 @@ def forward(sdm, sh, dev, S, M, T_lo=0, T_hi=None):
     return o, wo, ro
 
 
-@pytest.mark.parametrize("name", list(PLAN))
+def run_pool(tasks, label):
+    """Runs unit_parity over the tasks in the oracle pool, logging each finished unit."""
+    results = []
+    t0 = time.time()
+    for r in pool().imap_unordered(unit_parity, tasks, chunksize=1):
+        results.append(r)
+        if len(results) % max(1, len(tasks) // 8) == 0 or len(results) == len(tasks):
+            log(f"[full] {label}: {len(results)}/{len(tasks)} units checked ({time.time() - t0:.0f} s)")
+    return sorted(results, key=lambda r: (r["b"], r["h"]))
+
+
+def check_results(name, sh, results, tol, extra=None):
+    fails = [(r["b"], r["h"], r["fails"]) for r in results if r["fails"]]
+    assert not fails, f"{name}: slot lists differ from the oracle's beyond ties: {fails[:3]}"
+    rec = summarise(name, sh, results, tol, extra)
+    write_record(rec)
+    log(f"[full] {name}: {rec['units_compared']} units, {rec['token_heads_compared']} token-heads, "
+        f"tie positions {rec['tie_positions']} ({rec['set_changing_tie_tokens']} tokens with a changed slot set, "
+        f"{rec['units_with_ties']} units re-run on the device's slots); rel err o {rec['max_rel_err_o']:.2e}, "
+        f"table {rec['max_rel_err_table']:.2e} (tol {tol})")
+    assert rec["untouched_rows_bit_identical"], f"{name}: a row no token wrote differs from the start table"
+    assert rec["max_rel_err_o"] < tol and rec["max_rel_err_table"] < tol
+    return rec
+
+
+@pytest.mark.oracle_pool
+@pytest.mark.parametrize("name", ["tiny_fp32"] + list(PLAN))
 def test_fullsize_forward(sdm, name):
+    """Every unit over the whole sequence, in the launch the benchmark times (one
+    sdm_forward call over all units): slot lists position by position (ties counted), then
+    o at every token and the whole final table against the oracle run on the device's slot
+    lists (the oracle's own lists wherever no tie occurred), rows no token writes bit-equal
+    to M0. The per-workload record (tie counts, worst errors) goes to
+    gpurun_out/parity_fullsize.json."""
     import torch
     sh = W_[name]
-    units, prefix, nsamp = PLAN[name]
     log(f"[full] {name}: generating inputs")
     inp = SI.make_inputs(sh)
     dev = upload(inp, sh)
@@ -89,38 +125,18 @@ def test_fullsize_forward(sdm, name):
     log(f"[full] {name}: forward B={sh.B} H={sh.H} T={sh.T}")
     o, wo, ro = forward(sdm, sh, dev, S, M)
     tol = tolerance(sh)
-    rng = np.random.default_rng(7)
-    ties = 0
-    for (b, h) in units:
-        U = unit_inputs(inp, sh, b, h)
-        gw, gr = wo[b, h].cpu().numpy(), ro[b, h].cpu().numpy()
-        # indices of tokens sampled over the whole sequence (always including the last)
-        ts = np.unique(np.concatenate([rng.choice(sh.T, nsamp, replace=False), [sh.T - 1]]))
-        for which, g, n_sel in (("k", gw, sh.W), ("q", gr, sh.R)):
-            oi, _, _ = O.address(U[which][ts], U["C1"], U["C2"], sh.kappa, n_sel)
-            t_, _, fails = compare_indices(g[ts], oi, U[which][ts], U["C1"], U["C2"], sh.N)
-            assert not fails, f"{name} unit ({b},{h}) {which}: {fails[:3]}"
-            ties += t_
-        # outputs over the prefix, up to the first slot-set change caused by a tie
-        P = min(prefix, sh.T)
-        Up = unit_inputs(inp, sh, b, h, T=P)
-        r = O.forward_unit(Up["q"], Up["k"], Up["v"], Up["alpha"], Up["beta"], Up["C1"], Up["C2"], Up["M0"],
-                           sh.kappa, sh.W, sh.R, sh.mem_dtype)
-        tw, cw, fw = compare_indices(gw[:P], r["widx"], Up["k"], Up["C1"], Up["C2"], sh.N)
-        tr, cr, fr = compare_indices(gr[:P], r["ridx"], Up["q"], Up["C1"], Up["C2"], sh.N)
-        assert not fw and not fr
-        first = min(cw + cr) if (cw or cr) else P
-        assert first >= P // 2, f"{name} unit ({b},{h}): slot sets diverge at token {first}"
-        eo = rel_err(o[b, h, :first].cpu().numpy(), r["o"][:first])
-        log(f"[full] {name} unit ({b},{h}): o over {first} tokens rel err {eo:.2e} (tol {tol}); "
-            f"tie positions {tw + tr}")
-        assert eo < tol
-        # rows no token wrote are still M0
-        Mh = SI.widen(from_dev(M[b, h], sh.mem_dtype), sh.mem_dtype)
-        touched = np.zeros(sh.N, bool)
-        touched[gw.ravel()] = True
-        assert np.array_equal(Mh[~touched], U["M0"][~touched])
-    log(f"[full] {name}: sampled tie positions {ties}")
+    need = M.numel() * M.element_size() + o.numel() * 4
+    with SharedDir(need) as sd:
+        for n in ("q", "k", "v", "alpha", "beta", "subkeys", "M0"):
+            sd.save(n, inp[n])
+        sd.save("o", o.cpu().numpy())
+        sd.save("M", from_dev(M, sh.mem_dtype))
+        sd.save("widx", wo.cpu().numpy())
+        sd.save("ridx", ro.cpu().numpy())
+        tasks = [dict(dir=sd.path, shape=sh, b=b, h=h) for b in range(sh.B) for h in range(sh.H)]
+        log(f"[full] {name}: oracle over {len(tasks)} units in {pool_size()} workers")
+        results = run_pool(tasks, name)
+    check_results(name, sh, results, tol)
     # the same sequence in two calls on the carried table: bit for bit
     M2 = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
     sdm.init_from_M0(S, dev["M0"], M2)
@@ -131,17 +147,17 @@ def test_fullsize_forward(sdm, name):
     assert torch.equal(M2, M), "carried table differs"
 
 
+@pytest.mark.oracle_pool
 @pytest.mark.parametrize("name", list(PLAN))
 def test_fullsize_chunked(sdm, name):
     """The chunkwise two-phase recurrence at full size, launched as ``bench.py --chunked``
     launches it (addressing of keys and queries, then one sdm_recurrent_chunked call over all
-    units): in sampled units the device's slots are checked against the oracle's addressing
-    of a prefix, and the outputs up to the first slot-set change caused by a tie against the
-    oracle's chunkwise form on the oracle's own slots (o_t depends only on tokens up to t);
-    rows no token writes stay M0."""
+    units): every unit over the whole sequence by the full-size parity procedure against the
+    oracle's chunkwise form at chunk length 64 (READING R26 fixes where it rounds a bf16
+    table), and its outputs and table also against the token-by-token rule within the
+    tolerance."""
     import torch
     sh = W_[name]
-    units, prefix, _ = PLAN[name]
     log(f"[full] chunked {name}: generating inputs")
     inp = SI.make_inputs(sh)
     dev = upload(inp, sh)
@@ -160,36 +176,44 @@ def test_fullsize_chunked(sdm, name):
     sdm.recurrent_chunked(S, wi, wg, ri, rg, dev["v"], dev["alpha"], dev["beta"], M, o, ws)
     torch.cuda.synchronize()
     tol = tolerance(sh)
-    for (b, h) in units:
-        P = min(prefix, sh.T)
-        Up = unit_inputs(inp, sh, b, h, T=P)
-        owi, oww, _ = O.address(Up["k"], Up["C1"], Up["C2"], sh.kappa, sh.W)
-        ori, orw, _ = O.address(Up["q"], Up["C1"], Up["C2"], sh.kappa, sh.R)
-        gw, gr = wi[b, h, :P].cpu().numpy(), ri[b, h, :P].cpu().numpy()
-        tw, cw, fw = compare_indices(gw, owi, Up["k"], Up["C1"], Up["C2"], sh.N)
-        tr, cr, fr = compare_indices(gr, ori, Up["q"], Up["C1"], Up["C2"], sh.N)
-        assert not fw and not fr
-        first = min(cw + cr) if (cw or cr) else P
-        assert first >= P // 2, f"{name} unit ({b},{h}): slot sets diverge at token {first}"
-        oc, _ = O.chunkwise_recurrence(Up["M0"], owi, oww, ori, orw, Up["v"], Up["alpha"], Up["beta"], 64,
-                                       sh.mem_dtype)
-        eo = rel_err(o[b, h, :first].cpu().numpy(), oc[:first])
-        log(f"[full] chunked {name} unit ({b},{h}): o over {first} tokens rel err {eo:.2e} (tol {tol}); "
-            f"tie positions {tw + tr}")
-        assert eo < tol
-        Mh = SI.widen(from_dev(M[b, h], sh.mem_dtype), sh.mem_dtype)
-        touched = np.zeros(sh.N, bool)
-        touched[wi[b, h].cpu().numpy().ravel()] = True
-        assert np.array_equal(Mh[~touched], Up["M0"][~touched])
+    with SharedDir(M.numel() * M.element_size() + o.numel() * 4) as sd:
+        for n in ("q", "k", "v", "alpha", "beta", "subkeys", "M0"):
+            sd.save(n, inp[n])
+        sd.save("o", o.cpu().numpy())
+        sd.save("M", from_dev(M, sh.mem_dtype))
+        sd.save("widx", wi.cpu().numpy())
+        sd.save("ridx", ri.cpu().numpy())
+        tasks = [dict(dir=sd.path, shape=sh, b=b, h=h, chunk=64, token_rule=True) for b in range(sh.B)
+                 for h in range(sh.H)]
+        log(f"[full] chunked {name}: oracle over {len(tasks)} units in {pool_size()} workers")
+        results = run_pool(tasks, f"chunked {name}")
+    tok_o = max(r["err_o_token_rule"] for r in results)
+    tok_m = max(r["err_M_token_rule"] for r in results)
+    check_results(f"{name}_chunked", sh, results, tol,
+                  {"form": "chunkwise, chunk 64", "max_rel_err_o_vs_token_rule": tok_o,
+                   "max_rel_err_table_vs_token_rule": tok_m})
+    log(f"[full] chunked {name}: against the token-by-token rule: o {tok_o:.2e}, table {tok_m:.2e}")
+    assert tok_o < tol and tok_m < tol
 
 
+@pytest.mark.oracle_pool
 def test_fullsize_decode(sdm):
-    """One decode step over the full 64 x 16 tables (launch of the benchmark); sequences 0 and
-    37 are prefilled with their 4096 prior tokens, the others hold M0."""
+    """One decode step over all 64 x 16 tables of the decode workload (the launch the
+    benchmark times). Sequences 0, 21, 42 and 63 are first prefilled with their 4096 prior
+    tokens (one sdm_forward call each); the others hold M0. Checked against the oracle:
+
+    * the prefill of those 4 sequences (64 units): slot lists, every output and the whole
+      table after the prefill, by the full-size parity procedure;
+    * the decode step in every one of the 1024 units: the device's slot lists of the decode
+      token (sdm_address, the selection the fused step uses) against the oracle's, then the
+      oracle's decode step on the rows those lists name, taken from a copy of the table made
+      just before the step: o and every written row; every row the step changed is one of
+      the token's write slots (so the rest of each table is untouched)."""
     import torch
     sh = W_["decode"]
     P = sh.prefill
-    log(f"[full] decode: B={sh.B} H={sh.H} N={sh.N}, prefill {P} on sampled sequences")
+    PRE = (0, 21, 42, 63)
+    log(f"[full] decode: B={sh.B} H={sh.H} N={sh.N}, prefill {P} tokens on sequences {PRE}")
     params = SI.make_inputs(sh)
     dev = upload(params, sh)
     S1 = lib_shape(sh, T=1)
@@ -197,38 +221,106 @@ def test_fullsize_decode(sdm):
     sdm.init_from_M0(S1, dev["M0"], M)
     Sp = lib_shape(sh, B=1, T=P)
     ws = torch.empty(sdm.workspace_bytes(Sp), dtype=torch.uint8, device="cuda")
-    o_pre = torch.empty((1, sh.H, P, sh.d_v), dtype=torch.float32, device="cuda")
-    pre = {}
-    for b in (0, 37):
-        pre[b] = SI.make_prefill(sh, b)
+    pre = {b: SI.make_prefill(sh, b) for b in PRE}
+    o_pre = torch.empty((len(PRE), sh.H, P, sh.d_v), dtype=torch.float32, device="cuda")
+    w_pre = torch.empty((len(PRE), sh.H, P, sh.W), dtype=torch.int32, device="cuda")
+    r_pre = torch.empty((len(PRE), sh.H, P, sh.R), dtype=torch.int32, device="cuda")
+    for i, b in enumerate(PRE):
         t = {n: to_dev(pre[b][n], sh.in_dtype if n in ("q", "k", "v") else "f32")
              for n in ("q", "k", "v", "alpha", "beta")}
-        sdm.forward(Sp, t["q"], t["k"], t["v"], t["alpha"], t["beta"], dev["subkeys"], M[b:b + 1], o_pre, ws)
+        sdm.forward(Sp, t["q"], t["k"], t["v"], t["alpha"], t["beta"], dev["subkeys"], M[b:b + 1], o_pre[i:i + 1],
+                    ws, w_pre[i:i + 1], r_pre[i:i + 1])
+    torch.cuda.synchronize()
+    assert sdm.workspace_error(ws) == 0
+    snap = M.clone()
     o = torch.empty((sh.B, sh.H, 1, sh.d_v), dtype=torch.float32, device="cuda")
+    log("[full] decode: one step over all units")
     sdm.decode_step(S1, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], M, o)
+    wi = torch.empty((sh.B, sh.H, 1, sh.W), dtype=torch.int32, device="cuda")
+    wg = torch.empty((sh.B, sh.H, 1, sh.W), dtype=torch.float32, device="cuda")
+    ri = torch.empty((sh.B, sh.H, 1, sh.R), dtype=torch.int32, device="cuda")
+    rg = torch.empty((sh.B, sh.H, 1, sh.R), dtype=torch.float32, device="cuda")
+    sdm.address(S1, dev["k"], dev["subkeys"], sh.W, wi, wg)
+    sdm.address(S1, dev["q"], dev["subkeys"], sh.R, ri, rg)
     torch.cuda.synchronize()
     tol = tolerance(sh)
-    for b, h in ((0, 0), (37, 15), (5, 3)):
-        sk = SI.widen(params["subkeys"][h], sh.in_dtype)
-        M0h = SI.widen(params["M0"][h], sh.mem_dtype)
-        if b in pre:
-            pb = pre[b]
-            r = O.forward_unit(SI.widen(pb["q"][0, h], sh.in_dtype), SI.widen(pb["k"][0, h], sh.in_dtype),
-                               SI.widen(pb["v"][0, h], sh.in_dtype), pb["alpha"][0, h].astype(np.float64),
-                               pb["beta"][0, h].astype(np.float64), sk[0], sk[1], M0h, sh.kappa, sh.W, sh.R,
-                               sh.mem_dtype)
-            Mstart = r["M"]
-        else:
-            Mstart = M0h
-        o_ref, M_ref, _ = O.decode_step_unit(Mstart, SI.widen(params["q"][b, h, 0], sh.in_dtype),
-                               SI.widen(params["k"][b, h, 0], sh.in_dtype), SI.widen(params["v"][b, h, 0], sh.in_dtype),
-                               float(params["alpha"][b, h, 0]), float(params["beta"][b, h, 0]), sk[0], sk[1],
-                               sh.kappa, sh.W, sh.R, sh.mem_dtype)
-        eo = rel_err(o[b, h, 0].cpu().numpy(), o_ref)
-        Mh = SI.widen(from_dev(M[b, h], sh.mem_dtype), sh.mem_dtype)
-        em = rel_err(Mh, M_ref)
-        log(f"[full] decode unit ({b},{h}): o rel err {eo:.2e}, table rel err {em:.2e} (tol {tol})")
-        assert eo < tol and em < tol
+    # 1. the prefill of the four sequences, every unit in full
+    with SharedDir(len(PRE) * sh.H * sh.N * sh.d_v * 2) as sd:
+        for n in ("q", "k", "v", "alpha", "beta"):
+            sd.save(n, np.concatenate([pre[b][n] for b in PRE], 0))
+        sd.save("subkeys", params["subkeys"])
+        sd.save("M0", params["M0"])
+        sd.save("o", o_pre.cpu().numpy())
+        sd.save("M", from_dev(snap[list(PRE)], sh.mem_dtype))
+        sd.save("widx", w_pre.cpu().numpy())
+        sd.save("ridx", r_pre.cpu().numpy())
+        tasks = [dict(dir=sd.path, shape=sh.replace(B=len(PRE), T=P), b=i, h=h) for i in range(len(PRE))
+                 for h in range(sh.H)]
+        log(f"[full] decode: oracle prefill over {len(tasks)} units in {pool_size()} workers")
+        res_pre = run_pool(tasks, "decode prefill")
+    fails = [(r["b"], r["h"], r["fails"]) for r in res_pre if r["fails"]]
+    assert not fails, fails[:3]
+    # 2. the decode step in every unit, on the rows its slot lists name
+    gw = wi[:, :, 0].cpu().numpy().astype(np.int64)
+    gr = ri[:, :, 0].cpu().numpy().astype(np.int64)
+    slots = torch.from_numpy(np.concatenate([gw, gr], -1)).cuda()            # [B, H, W + R]
+    idx = slots[..., None].expand(-1, -1, -1, sh.d_v)
+    before = SI.widen(from_dev(torch.gather(snap, 2, idx).contiguous(), sh.mem_dtype), sh.mem_dtype)
+    after = SI.widen(from_dev(torch.gather(M, 2, idx).contiguous(), sh.mem_dtype), sh.mem_dtype)
+    changed_ok = True
+    for b in range(sh.B):
+        ch = (M[b] != snap[b]).any(-1)                                         # [H, N]
+        for h in range(sh.H):
+            rows = torch.nonzero(ch[h]).flatten().cpu().numpy()
+            changed_ok &= bool(np.isin(rows, gw[b, h]).all())
+    assert changed_ok, "the decode step changed a row outside the token's write slots"
+    go = o[:, :, 0].cpu().numpy()
+    ties = set_changes = differs = 0
+    worst_o = worst_m = 0.0
+    for b in range(sh.B):
+        for h in range(sh.H):
+            sk = SI.widen(params["subkeys"][h], sh.in_dtype)
+            C1, C2 = sk[0], sk[1]
+            q1 = SI.widen(params["q"][b, h], sh.in_dtype)
+            k1 = SI.widen(params["k"][b, h], sh.in_dtype)
+            v1 = SI.widen(params["v"][b, h], sh.in_dtype)
+            oi_w, _, _ = O.address(k1, C1, C2, sh.kappa, sh.W)
+            oi_r, _, _ = O.address(q1, C1, C2, sh.kappa, sh.R)
+            tw, cw, fw = compare_indices(gw[b, h][None], oi_w, k1, C1, C2, sh.N)
+            tr, cr, fr = compare_indices(gr[b, h][None], oi_r, q1, C1, C2, sh.N)
+            assert not fw and not fr, (b, h, fw + fr)
+            ties += tw + tr
+            set_changes += bool(cw or cr)
+            differs += bool((gw[b, h] != oi_w[0]).any() or (gr[b, h] != oi_r[0]).any())
+            # the rule touches only the listed rows: run it on a table of just those rows
+            lst = np.concatenate([gw[b, h], gr[b, h]])
+            uniq, first = np.unique(lst, return_index=True)
+            sub = before[b, h][first]
+            loc = {int(n): i for i, n in enumerate(uniq)}
+            lw = np.array([[loc[int(n)] for n in gw[b, h]]])
+            lr = np.array([[loc[int(n)] for n in gr[b, h]]])
+            ww, _ = O.slot_weights(k1, C1, C2, gw[b, h][None])
+            rw, _ = O.slot_weights(q1, C1, C2, gr[b, h][None])
+            o_ref, sub_ref = O.recurrence(sub, lw, ww, lr, rw, v1, np.array([float(params["alpha"][b, h, 0])]),
+                                          np.array([float(params["beta"][b, h, 0])]), sh.mem_dtype)
+            worst_o = max(worst_o, rel_err(go[b, h], o_ref[0]))
+            worst_m = max(worst_m, rel_err(after[b, h][first], sub_ref))
+    rec = summarise("decode", sh, res_pre, tol, {
+        "prefill_sequences_checked": list(PRE),
+        "decode_units_compared": sh.B * sh.H,
+        "decode_tie_positions": ties,
+        "decode_units_with_set_changing_ties": set_changes,
+        "decode_units_with_ties": differs,
+        "decode_max_rel_err_o": worst_o,
+        "decode_max_rel_err_written_rows": worst_m,
+    })
+    write_record(rec)
+    log(f"[full] decode: prefill of {len(PRE)} sequences: rel err o {rec['max_rel_err_o']:.2e}, table "
+        f"{rec['max_rel_err_table']:.2e}, tie positions {rec['tie_positions']}; decode step over {sh.B * sh.H} "
+        f"units: rel err o {worst_o:.2e}, written rows {worst_m:.2e}, tie positions {ties} (tol {tol})")
+    assert rec["untouched_rows_bit_identical"]
+    assert rec["max_rel_err_o"] < tol and rec["max_rel_err_table"] < tol
+    assert worst_o < tol and worst_m < tol
 
 
 def test_fullsize_decay_variant(sdm):

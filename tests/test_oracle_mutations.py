@@ -86,7 +86,16 @@ MUTANTS = {
     # chunkwise form: the written-back row forgets the decay of its chunk-start value
     "chunk_no_start_decay": ("row = dec(slot, -1, L) * M[slot]", "row = M[slot]"),
     # per-half top-k keeps too few sub-keys
-    "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(d1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(d1, sub, max(1, kappa - 1)), axis=-1)"),
+    "kappa_off_by_one": ("I1 = np.take_along_axis(sub, top_order(s1, sub, kappa), axis=-1)", "I1 = np.take_along_axis(sub, top_order(s1, sub, max(1, kappa - 1)), axis=-1)"),
+    # chunkwise form, bf16 table: the chunk-start row rounded after its decay, before the
+    # deltas are added
+    "chunk_round_start_early": ("row = dec(slot, -1, L) * M[slot]", "row = round_mem(dec(slot, -1, L) * M[slot], mem_dtype)"),
+    # chunkwise form: the written-back row is not rounded to the table dtype
+    "chunk_no_writeback_rounding": ("            M[slot] = round_mem(row, mem_dtype)\n", "            M[slot] = row\n"),
+    # chunkwise form: the chunk-start row's decay taken up to the last writer only
+    "chunk_start_decay_short": ("row = dec(slot, -1, L) * M[slot]", "row = dec(slot, -1, L - 1) * M[slot]"),
+    # selection by the first half's scores alone
+    "select_first_half_only": ("pick = top_order(cand, slots, n_sel)", "pick = top_order(np.repeat(np.take_along_axis(s1, I1, -1), kappa, axis=-1), slots, n_sel)"),
 }
 
 

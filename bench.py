@@ -80,6 +80,7 @@ RECURRENCE_SOURCES = ("sdm_dataflow.hip", "sdm_device.hpp")
 CHUNKED_SOURCES = ("sdm_chunked.hip", "sdm_device.hpp")
 BACKWARD_SOURCES = ("sdm_backward.hip", "sdm_device.hpp")
 DECAY_SOURCES = ("sdm_decay.hip", "sdm_dataflow.hip", "sdm_device.hpp")
+DECODE_SOURCES = ("sdm_decode.hip", "sdm_select.hpp", "sdm_device.hpp")
 
 
 def kernel_source_hash(kind: str = "recurrence") -> str:
@@ -89,8 +90,8 @@ def kernel_source_hash(kind: str = "recurrence") -> str:
     decay recurrence (decay passes, dependency pass and pipeline)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_memory_linear_amd", "csrc")
-    srcs = {"chunked": CHUNKED_SOURCES, "backward": BACKWARD_SOURCES, "decay": DECAY_SOURCES}.get(kind,
-                                                                                                 RECURRENCE_SOURCES)
+    srcs = {"chunked": CHUNKED_SOURCES, "backward": BACKWARD_SOURCES, "decay": DECAY_SOURCES,
+            "decode": DECODE_SOURCES}.get(kind, RECURRENCE_SOURCES)
     for f in srcs:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
@@ -325,62 +326,121 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _prefill_tokens(args):
+    """Worker: the prefill tokens of one decode sequence."""
+    name, b = args
+    return b, SI.make_prefill(SI.WORKLOADS[name], b)
+
+
+def _oracle_decode(args):
+    """Worker: the oracle's decode step on one head's table, over nsteps bank tokens of
+    sequence b; returns the wall time."""
+    import oracle.sdm_oracle as O
+    name, b, h, nsteps = args
+    sh = SI.WORKLOADS[name]
+    p, bank = _oracle_decode.params, _oracle_decode.bank
+    sk = SI.widen(p["subkeys"][h], sh.in_dtype)
+    M = SI.widen(p["M0"][h], sh.mem_dtype)
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        _, M, _ = O.decode_step_unit(M, SI.widen(bank["q"][i, b, h, 0], sh.in_dtype),
+                                     SI.widen(bank["k"][i, b, h, 0], sh.in_dtype),
+                                     SI.widen(bank["v"][i, b, h, 0], sh.in_dtype), float(bank["alpha"][i, b, h, 0]),
+                                     float(bank["beta"][i, b, h, 0]), sk[0], sk[1], sh.kappa, sh.W, sh.R,
+                                     sh.mem_dtype)
+    return time.perf_counter() - t0
+
+
 def bench_decode(args, sh):
-    """Decode workload: latency of one fused decode step over B sequences (tables pre-filled
-    by a prefill through the forward), tokens/s = B / step time."""
+    """Decode workload: each step is one fused decode step over all B sequences (tables
+    pre-filled by a 4096-token prefill through the forward), fed the next token of a bank
+    of distinct tokens, so every step addresses fresh rows. Latency = median of the
+    event-timed steps; tokens/s = B / that latency."""
+    import multiprocessing as mp
+
+    n = max(args.steps, 100)
+    log(f"[bench] decode: token bank of {n + args.warmup} steps x {sh.B} sequences")
+    params = SI.make_inputs(sh)
+    bank = SI.make_decode_bank(sh, n + args.warmup)
+    P = max(1, min(16, len(os.sched_getaffinity(0))))
+    cpu = None
+    # before the GPU is touched: prefill tokens and the oracle baseline in forked workers
+    _oracle_decode.params, _oracle_decode.bank = params, bank
+    with mp.get_context("fork").Pool(P) as pool:
+        log(f"[bench] decode: prefill tokens of {sh.B} sequences in {P} workers")
+        pre = dict(pool.map(_prefill_tokens, [(sh.name, b) for b in range(sh.B)]))
+        if not args.no_cpu_baseline:
+            dt = _oracle_decode((sh.name, 0, 0, 2)) / 2
+            steps = int(max(2, min(n, 15.0 / max(dt, 1e-6))))
+            units = [(b % sh.B, b % sh.H) for b in range(P)]
+            t0 = time.perf_counter()
+            pool.map(_oracle_decode, [(sh.name, b, h, steps) for (b, h) in units])
+            wall = time.perf_counter() - t0
+            cpu = {"value": P * steps / wall / sh.H, "unit": "tokens/s", "cores": P, "kind": "oracle",
+                   "sample": f"{P} (sequence, head) tables x {steps} consecutive bank tokens, float64 numpy oracle "
+                             f"decode step (addressing + write + read) from M0, one process per table; tokens/s = "
+                             f"table-steps/s / H"}
+            log(f"[bench] oracle decode {cpu['value']:.1f} tokens/s on {P} cores")
+
     import torch
     import sparse_memory_linear_amd as S
-
-    log(f"[bench] decode: building {sh.B}x{sh.H} tables")
-    rng_inp = SI.make_inputs(sh)
 
     def dev(a, dt):
         if dt == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
-    subkeys = dev(rng_inp["subkeys"], sh.in_dtype)
-    M0 = dev(rng_inp["M0"], sh.mem_dtype)
+    log(f"[bench] decode: building {sh.B}x{sh.H} tables")
+    subkeys = dev(params["subkeys"], sh.in_dtype)
+    M0 = dev(params["M0"], sh.mem_dtype)
     mdt = torch.bfloat16 if sh.mem_dtype == "bf16" else torch.float32
     M = torch.empty((sh.B, sh.H, sh.N, sh.d_v), dtype=mdt, device="cuda")
     s1 = S.make_shape(sh.B, sh.H, 1, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
     S.init_from_M0(s1, M0, M)
-    P = sh.prefill
-    sp = S.make_shape(1, sh.H, P, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
+    Tp = sh.prefill
+    sp = S.make_shape(1, sh.H, Tp, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
     ws = torch.empty(S.workspace_bytes(sp), dtype=torch.uint8, device="cuda")
-    o_pre = torch.empty((1, sh.H, P, sh.d_v), dtype=torch.float32, device="cuda")
+    o_pre = torch.empty((1, sh.H, Tp, sh.d_v), dtype=torch.float32, device="cuda")
     for b in range(sh.B):
-        pre = SI.make_prefill(sh, b)
-        t = {n: dev(pre[n], sh.in_dtype if n in ("q", "k", "v") else "f32") for n in ("q", "k", "v", "alpha", "beta")}
+        t = {k: dev(pre[b][k], sh.in_dtype if k in ("q", "k", "v") else "f32") for k in ("q", "k", "v", "alpha",
+                                                                                       "beta")}
         S.forward(sp, t["q"], t["k"], t["v"], t["alpha"], t["beta"], subkeys, M[b:b + 1], o_pre, ws)
+    del pre
+    bq, bk, bv = (dev(bank[k], sh.in_dtype) for k in ("q", "k", "v"))
+    ba, bb = dev(bank["alpha"], "f32"), dev(bank["beta"], "f32")
     torch.cuda.synchronize()
-    q, k, v = (dev(rng_inp[n], sh.in_dtype) for n in ("q", "k", "v"))
-    alpha, beta = dev(rng_inp["alpha"], "f32"), dev(rng_inp["beta"], "f32")
     o = torch.empty((sh.B, sh.H, 1, sh.d_v), dtype=torch.float32, device="cuda")
-    for _ in range(args.warmup):
-        S.decode_step(s1, q, k, v, alpha, beta, subkeys, M, o)
+    for i in range(args.warmup):
+        S.decode_step(s1, bq[i], bk[i], bv[i], ba[i], bb[i], subkeys, M, o)
     torch.cuda.synchronize()
-    n = max(args.steps, 100)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(n):
-        S.decode_step(s1, q, k, v, alpha, beta, subkeys, M, o)
-    e1.record()
+    for j in range(n):
+        i = args.warmup + j
+        ev[j][0].record()
+        S.decode_step(s1, bq[i], bk[i], bv[i], ba[i], bb[i], subkeys, M, o)
+        ev[j][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / n
-    per_th = recurrence_bytes_per_token_head(sh) + 2 * sh.d_k * 2
+    lat = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = lat[n // 2]
+    per_th = recurrence_bytes_per_token_head(sh) + 2 * sh.d_k * (2 if sh.in_dtype == "bf16" else 4)
     launch_bytes = per_th * sh.B * sh.H
     achieved = launch_bytes / (ms / 1e3) / 1e9
+    log(f"[bench] decode: median step {ms * 1e3:.1f} us (min {lat[0] * 1e3:.1f}, max {lat[-1] * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s algorithmic")
     out = {
-        "metric": METRIC, "value": sh.B / (wall / n), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "metric": METRIC, "value": sh.B / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / n, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": 1, "N": sh.N, "prefill": P},
+        "vs_baseline": None, "dtype": sh.mem_dtype, "data": "synthetic",
+        "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": 1, "N": sh.N, "d_k": sh.d_k, "d_v": sh.d_v,
+                   "kappa": sh.kappa, "W": sh.W, "R": sh.R, "in_dtype": sh.in_dtype, "mem_dtype": sh.mem_dtype,
+                   "arith": "fp32", "prefill": Tp, "token_bank": n + args.warmup,
+                   "latency_ms_median": ms, "latency_ms_min": lat[0], "latency_ms_max": lat[-1]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "decode", "ms_per_launch": ms},
-        "cpu_baseline": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(sh.name, "decode"),
+                     "kernel": "decode", "ms_per_launch": ms, "bytes_per_launch": launch_bytes},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

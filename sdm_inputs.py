@@ -183,6 +183,15 @@ def make_prefill(shape: Shape, b: int, T: Optional[int] = None) -> Dict[str, np.
     return draw_tokens(shape, rng, 1, shape.prefill if T is None else T)
 
 
+def make_decode_bank(shape: Shape, n: int) -> Dict[str, np.ndarray]:
+    """n successive decode tokens for every sequence of a decode workload (own generator,
+    seeded with (workload seed, 2**20); the same distributions as every other token),
+    shaped [n, B, H, 1, .] so that step i's tokens form one contiguous [B, H, 1, .] block."""
+    rng = np.random.default_rng([shape.seed, 1 << 20])
+    tk = draw_tokens(shape, rng, shape.B, n)
+    return {k: np.ascontiguousarray(np.moveaxis(v, 2, 0)[:, :, :, None]) for k, v in tk.items()}
+
+
 def adversarial(shape: Shape, kind: str, seed: int = 99) -> Dict[str, np.ndarray]:
     """Address-reuse stress inputs (same distributions, structured keys):
 

@@ -68,7 +68,7 @@ def forward(sdm, sh, dev, S, M, T_lo=0, T_hi=None):
     import torch
     T_hi = sh.T if T_hi is None else T_hi
     Sp = lib_shape(sh, T=T_hi - T_lo)
-    sl = lambda t: t[:, :, T_lo:T_hi].contiguous()
+    sl = lambda t: t[:, :, T_lo:T_hi].clone()  # a fresh (aligned) buffer even where the slice is contiguous
     o = torch.empty((sh.B, sh.H, T_hi - T_lo, sh.d_v), dtype=torch.float32, device="cuda")
     wo = torch.empty((sh.B, sh.H, T_hi - T_lo, sh.W), dtype=torch.int32, device="cuda")
     ro = torch.empty((sh.B, sh.H, T_hi - T_lo, sh.R), dtype=torch.int32, device="cuda")

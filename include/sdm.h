@@ -137,6 +137,27 @@ sdm_status sdm_forward(const sdm_shape* shape, const void* q, const void* k, con
                        const float* beta, const void* subkeys, void* M, float* o, int32_t* widx_out,
                        int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Largest workspace sdm_forward_static can use: its library-owned device array (bytes). */
+#define SDM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* sdm_forward without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops and harnesses that forbid allocation. The
+ * slot lists, weights, dependency words and error word that sdm_forward keeps in `ws` live
+ * in a library-owned device array of SDM_STATIC_SCRATCH_BYTES, one per GPU, whose address
+ * is looked up the first time the call runs on that GPU and which stays until the process
+ * ends. Arguments, layouts and results are those of sdm_forward (bit for bit).
+ * Errors: those of sdm_forward; SDM_ERR_WORKSPACE, with nothing enqueued, when
+ * sdm_workspace_bytes(shape) exceeds SDM_STATIC_SCRATCH_BYTES; SDM_ERR_HIP if the array's
+ * address cannot be obtained. The call allocates nothing.
+ * Every call on one GPU shares that GPU's array and leaves the last call's contents there:
+ * calls that overlap in time on one GPU (other streams, other host threads) race and give
+ * undefined results; calls ordered on one stream are safe. The recurrence's error word is
+ * not exposed to the caller (the forward's own addressing never produces a slot outside
+ * [0, N)). */
+sdm_status sdm_forward_static(const sdm_shape* shape, const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const void* subkeys, void* M, float* o, int32_t* widx_out,
+                              int32_t* ridx_out, void* stream);
+
 /* One decode step: T must be 1. Same result as sdm_forward with T = 1, fused into one
  * launch; needs no workspace.
  *   q, k [B,H,1,d_k]; v [B,H,1,d_v]; alpha, beta [B,H,1]; M in/out; o [B,H,1,d_v] f32. */

@@ -17,7 +17,7 @@ from typing import Optional
 __all__ = [
     "SDM_F32", "SDM_BF16", "SdmError", "SdmLibraryMissing", "Shape", "lib", "lib_path",
     "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
-    "forward", "decode_step", "workspace_error", "status_string", "abi_version",
+    "forward", "forward_static", "STATIC_SCRATCH_BYTES", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
     "materialize", "gates", "output_gate", "head_mix", "recurrent_log", "recurrent_backward",
     "backward_workspace_bytes", "address_backward", "workspace_bytes_chunked", "recurrent_chunked",
@@ -25,6 +25,7 @@ __all__ = [
 
 SDM_F32 = 0
 SDM_BF16 = 1
+STATIC_SCRATCH_BYTES = 64 << 20  # SDM_STATIC_SCRATCH_BYTES of the header
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsdm.so")
@@ -65,6 +66,7 @@ _SIGS = {
     "sdm_address": (ctypes.c_int, [_SP, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "sdm_recurrent": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sdm_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "sdm_forward_static": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sdm_decode_step": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sdm_workspace_error": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P]),
     "sdm_decay_state_init": (ctypes.c_int, [_SP, _P, _P, _P]),
@@ -171,6 +173,12 @@ def forward(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, ws, widx_out=None
     _check(lib().sdm_forward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                              _ptr(subkeys), _ptr(M), _ptr(o), _ptr(widx_out), _ptr(ridx_out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "sdm_forward")
+
+
+def forward_static(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, widx_out=None, ridx_out=None, stream=None):
+    _check(lib().sdm_forward_static(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(subkeys), _ptr(M), _ptr(o), _ptr(widx_out), _ptr(ridx_out),
+                                    _stream(stream)), "sdm_forward_static")
 
 
 def decode_step(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, stream=None):

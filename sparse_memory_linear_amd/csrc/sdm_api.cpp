@@ -6,6 +6,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/sdm.h"
 #include "sdm_internal.hpp"
 
@@ -120,9 +123,37 @@ sdm_status recurrent_impl(const sdm_shape* S, const int32_t* widx, const float* 
       launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, decay ? &dk : nullptr, hs, xlog));
 }
 
+// Workspace of sdm_forward_static: one array per GPU (each device holds its own copy of a
+// __device__ variable), never passed to a kernel by name; its device address is looked up
+// once per device and kept.
+__device__ __align__(256) unsigned char scratch[SDM_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, or null on a HIP error.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+// use_static: the workspace is the library's scratch array (ws and ws_bytes are ignored);
+// it is looked up only after every argument check has passed.
 sdm_status forward_impl(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
                         const float* beta, const void* subkeys, void* M, double* lam, double* lrun, float* o,
-                        int32_t* widx_out, int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t* widx_out, int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream,
+                        bool use_static = false) {
   sdm_status st = check_shape(S, true);
   if (st != SDM_OK) return st;
   if (!q || !k || !v || !alpha || !beta || !subkeys || !M || !o) return SDM_ERR_INVALID_ARG;
@@ -133,8 +164,14 @@ sdm_status forward_impl(const sdm_shape* S, const void* q, const void* k, const 
   const bool decay = lam != nullptr;
   if (decay && !dataflow_supported(*S, true)) return SDM_ERR_UNSUPPORTED;
   const WsLayout L = workspace_layout(*S, decay);
-  if (!ws || ws_bytes < L.total) return SDM_ERR_WORKSPACE;
-  if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
+  if (use_static) {
+    if (L.total > SDM_STATIC_SCRATCH_BYTES) return SDM_ERR_WORKSPACE;
+    ws = nullptr;  // not known yet: it overlaps no caller buffer
+    ws_bytes = 0;
+  } else {
+    if (!ws || ws_bytes < L.total) return SDM_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SDM_ERR_INVALID_ARG;
+  }
   const size_t mb = (size_t)S->B * S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
   const size_t ob = tensor_bytes(*S, S->d_v, 4);
   const size_t xb = tensor_bytes(*S, S->d_k, dtype_size(S->in_dtype));
@@ -149,6 +186,11 @@ sdm_status forward_impl(const sdm_shape* S, const void* q, const void* k, const 
   st = check_decay(S, lam, lrun, M, mb, o, ob, ws, ws_bytes);
   if (st != SDM_OK) return st;
   if (S->T == 0) return SDM_OK;
+  if (use_static) {
+    ws = static_scratch();
+    if (!ws) return SDM_ERR_HIP;
+    ws_bytes = SDM_STATIC_SCRATCH_BYTES;
+  }
   hipStream_t hs = (hipStream_t)stream;
   char* w = (char*)ws;
   int32_t* widx = widx_out ? widx_out : (int32_t*)(w + L.widx);
@@ -288,6 +330,13 @@ sdm_status sdm_forward(const sdm_shape* S, const void* q, const void* k, const v
                        int32_t* ridx_out, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(S, q, k, v, alpha, beta, subkeys, M, nullptr, nullptr, o, widx_out, ridx_out, ws, ws_bytes,
                       stream);
+}
+
+sdm_status sdm_forward_static(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const void* subkeys, void* M, float* o, int32_t* widx_out,
+                              int32_t* ridx_out, void* stream) {
+  return forward_impl(S, q, k, v, alpha, beta, subkeys, M, nullptr, nullptr, o, widx_out, ridx_out, nullptr, 0,
+                      stream, true);
 }
 
 sdm_status sdm_decode_step(const sdm_shape* S, const void* q, const void* k, const void* v, const float* alpha,

@@ -285,3 +285,27 @@ def test_chunked_validates(sdm, no_gpu):
     assert L.sdm_recurrent_chunked(sp, *args, None) == -1
     assert L.sdm_recurrent_chunked(ctypes.byref(base(W=40, kappa=16)), *ok, None) == -2   # unsupported
 
+
+
+def test_forward_static_validates(sdm, no_gpu):
+    """The allocation-free forward checks its arguments and its workspace limit on the host
+    before any HIP call."""
+    import sdm_inputs as SI
+    from parity import lib_shape
+    L = sdm.lib()
+    big = lib_shape(SI.WORKLOADS["layer_8b_long"])
+    p = [0x100000 * (i + 1) for i in range(10)]  # q, k, v, alpha, beta, subkeys, M, o, widx_out, ridx_out
+    assert sdm.workspace_bytes(big) > sdm.STATIC_SCRATCH_BYTES
+    assert L.sdm_forward_static(ctypes.byref(big), *p, None) == -3           # workspace past the array
+    small = lib_shape(SI.WORKLOADS["small"].replace(B=1, H=2, T=64))
+    q = list(p)
+    q[0] = None
+    assert L.sdm_forward_static(ctypes.byref(small), *q, None) == -1         # null q
+    q = list(p)
+    q[1] += 4
+    assert L.sdm_forward_static(ctypes.byref(small), *q, None) == -1         # misaligned k
+    q = list(p)
+    q[7] = q[6]
+    assert L.sdm_forward_static(ctypes.byref(small), *q, None) == -1         # o overlaps M
+    bad = lib_shape(SI.WORKLOADS["small"].replace(N=1000))
+    assert L.sdm_forward_static(ctypes.byref(bad), *p, None) == -1           # N not a square

@@ -8,7 +8,7 @@
 // kappa sub-keys of each half form kappa^2 candidate slots, of which the best n_sel are
 // kept and weighted by a softmax over their scores.
 //
-// One workgroup (4 waves) handles 32 tokens of one head. Scores of one half for the 32
+// One workgroup (8 waves) handles 32 tokens of one head. Scores of one half for the 32
 // tokens are kept in LDS (never written to HBM); wave-level selection follows.
 
 #include "sdm_device.hpp"
@@ -22,9 +22,9 @@ namespace {
 constexpr int kTok = 32;      // tokens per workgroup
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxK8 = 8;     // MFMA scoring for half widths up to 64 (8 steps of 8)
+constexpr int kMaxK16 = 8;    // MFMA scoring for half widths up to 128 (8 steps of 16)
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 struct AddrArgs {
@@ -58,33 +58,35 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
   const int stride = score_stride(s);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const bool use_mfma = BF16 && (s % 32 == 0) && (h % 8 == 0) && h <= 8 * kMaxK8;
+  const bool use_mfma = BF16 && (s % 32 == 0) && (h % 16 == 0) && h <= 16 * kMaxK16;
   if (use_mfma) {
+    // v_mfma_f32_32x32x16_bf16: lane l carries k = 8 (l / 32) .. +7 of row (or column) l % 32
+    // of both operands; bf16 products are exact and summed in float32
     const uint16_t* X = (const uint16_t*)A.x;
     const uint16_t* C = (const uint16_t*)A.subkeys + ((size_t)head * 2 + half) * (size_t)s * h;
     int r = r0 + (lane & 31);
     if (r >= BT) r = BT - 1;  // rows past the end: valid address, result discarded
     const int b = r / A.T, t = r % A.T;
     const uint16_t* xrow = X + (((size_t)b * A.H + head) * A.T + t) * d_k + (size_t)half * h;
-    const int kq = (lane >> 5) * 4;
-    const int nk = h / 8;
+    const int kq = (lane >> 5) * 8;
+    const int nk = h / 16;
     // this lane's token fragments for every k step, loaded once for all sub-key tiles
-    uint2 xf[kMaxK8];
+    uint4 xf[kMaxK16];
 #pragma unroll
-    for (int k = 0; k < kMaxK8; ++k)
-      if (k < nk) xf[k] = *(const uint2*)(xrow + 8 * k + kq);
+    for (int k = 0; k < kMaxK16; ++k)
+      if (k < nk) xf[k] = *(const uint4*)(xrow + 16 * k + kq);
     for (int st = wave; st < s / 32; st += kWaves) {
       const uint16_t* crow = C + (size_t)(st * 32 + (lane & 31)) * h;
-      uint2 cf[kMaxK8];
+      uint4 cf[kMaxK16];
 #pragma unroll
-      for (int k = 0; k < kMaxK8; ++k)
-        if (k < nk) cf[k] = *(const uint2*)(crow + 8 * k + kq);
+      for (int k = 0; k < kMaxK16; ++k)
+        if (k < nk) cf[k] = *(const uint4*)(crow + 16 * k + kq);
       float16_t acc = {};
 #pragma unroll
-      for (int k = 0; k < kMaxK8; ++k)
+      for (int k = 0; k < kMaxK16; ++k)
         if (k < nk)
-          acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4_t, cf[k]),
-                                                         __builtin_bit_cast(short4_t, xf[k]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cf[k]),
+                                                        __builtin_bit_cast(bf16x8_t, xf[k]), acc, 0, 0, 0);
       // D[row = sub-key][col = token]; lane holds col = lane%32,
       // rows 8*(i/4) + 4*(lane/32) + i%4.
       const int col = lane & 31;

@@ -14,7 +14,7 @@ namespace sdm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxK8 = 8;  // MFMA scoring for half widths up to 64
+constexpr int kMaxK16 = 8;  // MFMA scoring for half widths up to 128 (8 steps of 16)
 
 struct DecArgs {
   const void* q;
@@ -108,31 +108,32 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecArgs A) {
   const int d_k = 2 * hh;
 
   // 1. scores of (k half 0, k half 1, q half 0, q half 1) against their sub-keys
-  if (BF16 && (s % 32 == 0) && (hh % 8 == 0) && hh <= 8 * kMaxK8) {
-    // MFMA: a 32-sub-key tile of one half is the A operand; the B operand's columns 0 and 1
-    // are that half of k and of q (the other columns are zero), so one pass scores both.
-    typedef short short4_t __attribute__((ext_vector_type(4)));
+  if (BF16 && (s % 32 == 0) && (hh % 16 == 0) && hh <= 16 * kMaxK16) {
+    // MFMA (v_mfma_f32_32x32x16_bf16): a 32-sub-key tile of one half is the A operand; the B
+    // operand's columns 0 and 1 are that half of k and of q (the other columns are zero), so
+    // one pass scores both. Lane l carries k = 8 (l / 32) .. +7 of both operands.
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     typedef float float16_t __attribute__((ext_vector_type(16)));
-    const int col = lane & 31, kq = (lane >> 5) * 4, nk = hh / 8;
+    const int col = lane & 31, kq = (lane >> 5) * 8, nk = hh / 16;
     for (int half = 0; half < 2; ++half) {
       const uint16_t* xv = (const uint16_t*)(col == 0 ? A.k : A.q) + (size_t)u * d_k + (size_t)half * hh;
-      uint2 xf[kMaxK8];
+      uint4 xf[kMaxK16];
 #pragma unroll
-      for (int kk = 0; kk < kMaxK8; ++kk)
-        if (kk < nk) xf[kk] = col < 2 ? *(const uint2*)(xv + 8 * kk + kq) : make_uint2(0u, 0u);
+      for (int kk = 0; kk < kMaxK16; ++kk)
+        if (kk < nk) xf[kk] = col < 2 ? *(const uint4*)(xv + 16 * kk + kq) : make_uint4(0u, 0u, 0u, 0u);
       const uint16_t* C = (const uint16_t*)A.subkeys + ((size_t)head * 2 + half) * (size_t)s * hh;
       for (int st = wave; st < s / 32; st += kThreads / 64) {
         const uint16_t* crow = C + (size_t)(st * 32 + col) * hh;
-        uint2 cf[kMaxK8];
+        uint4 cf[kMaxK16];
 #pragma unroll
-        for (int kk = 0; kk < kMaxK8; ++kk)
-          if (kk < nk) cf[kk] = *(const uint2*)(crow + 8 * kk + kq);
+        for (int kk = 0; kk < kMaxK16; ++kk)
+          if (kk < nk) cf[kk] = *(const uint4*)(crow + 16 * kk + kq);
         float16_t acc = {};
 #pragma unroll
-        for (int kk = 0; kk < kMaxK8; ++kk)
+        for (int kk = 0; kk < kMaxK16; ++kk)
           if (kk < nk)
-            acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(short4_t, cf[kk]),
-                                                           __builtin_bit_cast(short4_t, xf[kk]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cf[kk]),
+                                                          __builtin_bit_cast(bf16x8_t, xf[kk]), acc, 0, 0, 0);
         // D[row = sub-key][col]; lane holds col = lane % 32, rows 8*(i/4) + 4*(lane/32) + i%4
         if (col < 2) {
 #pragma unroll

@@ -26,8 +26,11 @@ training step.
 With --chunked the recurrence runs in its chunkwise two-phase form (64-token chunks: the
 preparation kernel over every chunk in parallel, then the apply kernel over the chunks in
 order); ``roofline`` describes that call, priced with the recurrence's algorithmic bytes.
+Without a mode flag the recurrence runs in the form sdm_forward takes for the shape
+(sdm_forward_uses_chunkwise: the chunkwise form for a float32 table with at least 32 units,
+else the pipeline); --pipeline forces the pipelined recurrence.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay | --backward | --chunked]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay | --backward | --chunked | --pipeline]
 """
 from __future__ import annotations
 
@@ -168,9 +171,10 @@ def main():
     ap.add_argument("--decay", action="store_true", help="whole-table decay variant")
     ap.add_argument("--backward", action="store_true", help="training step: forward with log and backward")
     ap.add_argument("--chunked", action="store_true", help="forward with the chunkwise two-phase recurrence")
+    ap.add_argument("--pipeline", action="store_true", help="forward with the pipelined recurrence")
     args = ap.parse_args()
-    if args.decay + args.backward + args.chunked > 1:
-        print("--decay, --backward and --chunked are separate modes", file=sys.stderr)
+    if args.decay + args.backward + args.chunked + args.pipeline > 1:
+        print("--decay, --backward, --chunked and --pipeline are separate modes", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -183,7 +187,7 @@ def main():
     sh = SI.WORKLOADS[args.workload]
     if sh.T == 1:
         return bench_decode(args, sh)
-    if args.decay or args.backward or args.chunked:
+    if args.decay or args.backward or args.chunked or args.pipeline:
         args.no_cpu_baseline = True  # the oracle baseline times the default forward
     log(f"[bench] generating {sh.name} inputs")
     t0 = time.time()
@@ -219,6 +223,10 @@ def main():
     ridx = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.int32, device="cuda")
     rgt = torch.empty((sh.B, sh.H, sh.T, sh.R), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    # the recurrence form sdm_forward takes for this shape, unless a mode flag fixes it
+    if not (args.decay or args.backward or args.pipeline) and S.forward_uses_chunkwise(shape):
+        args.chunked = True
+        log("[bench] sdm_forward runs the chunkwise form for this shape")
     if args.chunked:
         cws = torch.empty(S.workspace_bytes_chunked(shape), dtype=torch.uint8, device="cuda")
     if args.backward:

@@ -125,7 +125,9 @@ sdm_status sdm_recurrent(const sdm_shape* shape, const int32_t* widx, const floa
                          void* ws, size_t ws_bytes, void* stream);
 
 /* One SDM layer forward over a [B, H, T] token block: addressing of k (W write slots) and
- * q (R read slots) followed by the recurrence above, continuing from the table in M (call
+ * q (R read slots) followed by the recurrence above (for a float32 table with at least 32
+ * units, by its chunkwise two-phase form, which agrees with it up to float32 summation order;
+ * see sdm_forward_uses_chunkwise), continuing from the table in M (call
  * sdm_init_from_M0 first for a fresh sequence; calling again with the carried M continues
  * the sequence).
  *   q, k [B,H,T,d_k] in_dtype; v [B,H,T,d_v] in_dtype; alpha, beta [B,H,T] f32
@@ -157,6 +159,16 @@ sdm_status sdm_forward(const sdm_shape* shape, const void* q, const void* k, con
 sdm_status sdm_forward_static(const sdm_shape* shape, const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, const void* subkeys, void* M, float* o, int32_t* widx_out,
                               int32_t* ridx_out, void* stream);
+
+/* Which form of the recurrence sdm_forward (and sdm_forward_static) runs for this shape:
+ * 0 = the pipelined token-by-token recurrence (the result of sdm_recurrent), 1 = the
+ * chunkwise two-phase form of sdm_recurrent_chunked, -1 = invalid shape. The chunkwise form
+ * is taken for a float32 table with at least 32 units (B*H), where it agrees with the token
+ * rule up to float32 summation order and was measured faster. That order can differ from run
+ * to run (its first phase accumulates couplings with LDS float atomics), so with the
+ * chunkwise form results and the state carried across calls agree up to float32 summation
+ * order rather than bit for bit; the pipeline is deterministic. */
+int sdm_forward_uses_chunkwise(const sdm_shape* shape);
 
 /* One decode step: T must be 1. Same result as sdm_forward with T = 1, fused into one
  * launch; needs no workspace.

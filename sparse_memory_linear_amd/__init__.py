@@ -17,7 +17,7 @@ from typing import Optional
 __all__ = [
     "SDM_F32", "SDM_BF16", "SdmError", "SdmLibraryMissing", "Shape", "lib", "lib_path",
     "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
-    "forward", "forward_static", "STATIC_SCRATCH_BYTES", "decode_step", "workspace_error", "status_string", "abi_version",
+    "forward", "forward_static", "STATIC_SCRATCH_BYTES", "forward_uses_chunkwise", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
     "materialize", "gates", "output_gate", "head_mix", "recurrent_log", "recurrent_backward",
     "backward_workspace_bytes", "address_backward", "workspace_bytes_chunked", "recurrent_chunked",
@@ -67,6 +67,7 @@ _SIGS = {
     "sdm_recurrent": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sdm_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sdm_forward_static": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "sdm_forward_uses_chunkwise": (ctypes.c_int, [_SP]),
     "sdm_decode_step": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sdm_workspace_error": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P]),
     "sdm_decay_state_init": (ctypes.c_int, [_SP, _P, _P, _P]),
@@ -173,6 +174,14 @@ def forward(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, ws, widx_out=None
     _check(lib().sdm_forward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                              _ptr(subkeys), _ptr(M), _ptr(o), _ptr(widx_out), _ptr(ridx_out), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "sdm_forward")
+
+
+def forward_uses_chunkwise(shape: Shape) -> bool:
+    """True where sdm_forward runs the chunkwise form of the recurrence for this shape."""
+    r = lib().sdm_forward_uses_chunkwise(ctypes.byref(shape))
+    if r < 0:
+        raise SdmError(-1, "sdm_forward_uses_chunkwise")
+    return bool(r)
 
 
 def forward_static(shape: Shape, q, k, v, alpha, beta, subkeys, M, o, widx_out=None, ridx_out=None, stream=None):

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -22,6 +23,16 @@ constexpr size_t kAlign = 256;
 constexpr size_t kMaxLds = 160 * 1024;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// sdm_forward runs the recurrence in its chunkwise two-phase form instead of the pipeline
+// where the two agree up to float32 summation order and the chunkwise form was measured
+// faster: a float32 table (the chunkwise form rounds rows to the table dtype only at each
+// chunk's write-back, which for float32 changes nothing but the order of the float32 sums)
+// and at least 32 units (their chunk workgroups fill the chip; with one unit the pipeline is
+// faster). Not for the whole-table decay variant, which runs on the pipeline only.
+bool forward_uses_chunkwise(const sdm_shape& S, bool decay) {
+  return !decay && S.mem_dtype == SDM_F32 && (int64_t)S.B * S.H >= 32 && chunked_supported(S);
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -203,6 +214,8 @@ sdm_status forward_impl(const sdm_shape* S, const void* q, const void* k, const 
   if (e != hipSuccess) return SDM_ERR_HIP;
   e = launch_zero(w + L.err, 1, hs);
   if (e != hipSuccess) return SDM_ERR_HIP;
+  if (forward_uses_chunkwise(*S, decay))
+    return hip_status(launch_chunked(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, w + L.chunk, hs));
   DecayState dk{lam, lrun};
   return hip_status(launch_recurrent(*S, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, L, decay ? &dk : nullptr, hs));
 }
@@ -261,6 +274,10 @@ WsLayout workspace_layout(const sdm_shape& S, bool decay) {
       o = align_up(o + (size_t)(decay_segments(S) - 1) * S.B * S.H * (size_t)S.N * 4);
     }
   }
+  // the chunkwise form's per-chunk lists, where sdm_forward takes it (same region as the
+  // pipeline's dependency words: a call uses one or the other)
+  L.chunk = L.deps;
+  if (forward_uses_chunkwise(S, decay)) o = std::max(o, align_up(L.chunk + chunked_workspace_bytes(S)));
   L.total = o;
   return L;
 }
@@ -284,6 +301,11 @@ const char* sdm_status_string(int status) {
 }
 
 int sdm_abi_version(void) { return SDM_ABI_VERSION; }
+
+int sdm_forward_uses_chunkwise(const sdm_shape* shape) {
+  if (check_shape(shape, true) != SDM_OK) return -1;
+  return forward_uses_chunkwise(*shape, false) ? 1 : 0;
+}
 
 sdm_status sdm_check_shape(const sdm_shape* shape) { return check_shape(shape, true); }
 

@@ -26,6 +26,7 @@ struct WsLayout {
   size_t ltok, fac, lastw;      // whole-table decay: log-decay per token [U][T+1], factors [U][T][E],
                                 // latest writer per slot [U][N]
   size_t segl;                  // whole-table decay: latest writer per token segment [U][nseg-1][N]
+  size_t chunk;                 // chunkwise form's per-chunk lists (sdm_forward on float32 tables)
   size_t total;
 };
 WsLayout workspace_layout(const sdm_shape& S, bool decay = false);

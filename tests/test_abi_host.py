@@ -309,3 +309,22 @@ def test_forward_static_validates(sdm, no_gpu):
     assert L.sdm_forward_static(ctypes.byref(small), *q, None) == -1         # o overlaps M
     bad = lib_shape(SI.WORKLOADS["small"].replace(N=1000))
     assert L.sdm_forward_static(ctypes.byref(bad), *p, None) == -1           # N not a square
+
+
+def test_forward_form_query(sdm):
+    """Which recurrence form sdm_forward takes: the chunkwise form for a float32 table with at
+    least 32 units, the pipeline otherwise; -1 for an invalid shape (host only)."""
+    import sdm_inputs as SI
+    from parity import lib_shape
+    L = sdm.lib()
+    W_ = SI.WORKLOADS
+    assert sdm.forward_uses_chunkwise(lib_shape(W_["small"]))                       # 32 units, f32 table
+    assert not sdm.forward_uses_chunkwise(lib_shape(W_["small"].replace(B=2)))      # 16 units
+    assert not sdm.forward_uses_chunkwise(lib_shape(W_["tiny_fp32"]))               # one unit
+    assert not sdm.forward_uses_chunkwise(lib_shape(W_["layer_1p4b"]))              # bf16 table
+    assert not sdm.forward_uses_chunkwise(lib_shape(W_["layer_8b_long"]))
+    bad = lib_shape(W_["small"].replace(N=1000))
+    assert L.sdm_forward_uses_chunkwise(ctypes.byref(bad)) == -1
+    # the forward's workspace covers the chunkwise lists where it takes that form
+    s = lib_shape(W_["small"])
+    assert sdm.workspace_bytes(s) >= sdm.workspace_bytes_chunked(s)

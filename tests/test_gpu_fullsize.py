@@ -137,14 +137,22 @@ def test_fullsize_forward(sdm, name):
         log(f"[full] {name}: oracle over {len(tasks)} units in {pool_size()} workers")
         results = run_pool(tasks, name)
     check_results(name, sh, results, tol)
-    # the same sequence in two calls on the carried table: bit for bit
+    # the same sequence in two calls on the carried table: bit for bit on the pipeline; where
+    # the forward runs the chunkwise form (float32 tables, many units) the float32 sums of
+    # its first phase can be ordered differently from run to run, so up to that order
     M2 = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
     sdm.init_from_M0(S, dev["M0"], M2)
     T1 = sh.T // 2 + 3
     o1, _, _ = forward(sdm, sh, dev, S, M2, 0, T1)
     o2, _, _ = forward(sdm, sh, dev, S, M2, T1, sh.T)
-    assert torch.equal(torch.cat([o1, o2], 2), o), "split call differs from the single call"
-    assert torch.equal(M2, M), "carried table differs"
+    if sdm.forward_uses_chunkwise(S):
+        e_o = rel_err(torch.cat([o1, o2], 2).cpu().numpy(), o.cpu().numpy())
+        e_m = rel_err(M2.float().cpu().numpy(), M.float().cpu().numpy())
+        log(f"[full] {name}: split call against one call (chunkwise form): o {e_o:.1e}, table {e_m:.1e}")
+        assert e_o < 1e-5 and e_m < 1e-5, "split call differs from the single call beyond float32 summation order"
+    else:
+        assert torch.equal(torch.cat([o1, o2], 2), o), "split call differs from the single call"
+        assert torch.equal(M2, M), "carried table differs"
 
 
 @pytest.mark.oracle_pool

@@ -277,3 +277,47 @@ def write_record(rec: dict, fname: str = "parity_fullsize.json") -> None:
     data[rec["workload"]] = rec
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
+
+
+def unit_backward_parity(task) -> dict:
+    """Full-size parity of the recurrence backward for one unit (runs in a pool worker): the
+    device's slot lists are checked against the oracle's addressing (ties counted), then the
+    oracle's forward, log of pre-update rows and reverse walk run on the device's slot lists
+    and float32 weights (the inputs the device's backward took), and every gradient is
+    compared: dv, dalpha, dbeta, the write and read weight gradients and the table's
+    gradient at the start (dM0)."""
+    import time
+    import oracle.sdm_oracle as O
+    t0 = time.perf_counter()
+    d, sh, b, h = task["dir"], task["shape"], task["b"], task["h"]
+    ind, md = sh.in_dtype, sh.mem_dtype
+    L = lambda n: _load(d, n)
+    q = SI.widen(np.asarray(L("q")[b, h]), ind)
+    k = SI.widen(np.asarray(L("k")[b, h]), ind)
+    v = SI.widen(np.asarray(L("v")[b, h]), ind)
+    alpha = np.asarray(L("alpha")[b, h], dtype=np.float64)
+    beta = np.asarray(L("beta")[b, h], dtype=np.float64)
+    sk = SI.widen(np.asarray(L("subkeys")[h]), ind)
+    M0 = SI.widen(np.asarray(L("M0")[h]), md)
+    gw = np.asarray(L("widx")[b, h]).astype(np.int64)
+    gr = np.asarray(L("ridx")[b, h]).astype(np.int64)
+    ww = np.asarray(L("wgt")[b, h], dtype=np.float64)
+    rw = np.asarray(L("rgt")[b, h], dtype=np.float64)
+    go = np.asarray(L("go")[b, h], dtype=np.float64)
+    out = {"b": b, "h": h, "tokens": int(len(gw))}
+    oi_w, _, _ = O.address(k, sk[0], sk[1], sh.kappa, sh.W)
+    oi_r, _, _ = O.address(q, sk[0], sk[1], sh.kappa, sh.R)
+    tw, cw, fw = compare_indices(gw, oi_w, k, sk[0], sk[1], sh.N)
+    tr, cr, fr = compare_indices(gr, oi_r, q, sk[0], sk[1], sh.N)
+    out.update(ties=tw + tr, set_changes=len(set(cw) | set(cr)), differs=bool(tw + tr), fails=(fw + fr)[:5])
+    if fw or fr:
+        return out
+    _, MT = O.recurrence(M0, gw, ww, gr, rw, v, alpha, beta, md)
+    xlog = O.recurrence_log(M0, gw, ww, v, alpha, beta, md)
+    g = O.recurrence_backward(MT, xlog, gw, ww, gr, rw, v, alpha, beta, go)
+    del xlog, MT
+    dev = {"dv": L("dv")[b, h], "dalpha": L("dalpha")[b, h], "dbeta": L("dbeta")[b, h], "dwgt": L("dwgt")[b, h],
+           "drgt": L("drgt")[b, h], "dM0": L("G")[b, h]}
+    out["errs"] = {n: rel_err(np.asarray(a, dtype=np.float64), g[n]) for n, a in dev.items()}
+    out["oracle_s"] = time.perf_counter() - t0
+    return out

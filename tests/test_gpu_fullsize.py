@@ -25,7 +25,7 @@ import pytest
 import oracle.sdm_oracle as O
 import sdm_inputs as SI
 from parity import (SharedDir, compare_indices, empty_mem, from_dev, lib_shape, log, pool, pool_size, rel_err,
-                    summarise, to_dev, tolerance, unit_parity, write_record)
+                    summarise, to_dev, tolerance, unit_backward_parity, unit_parity, write_record)
 
 pytestmark = pytest.mark.gpu
 
@@ -401,21 +401,18 @@ def test_fullsize_decay_variant(sdm):
             "lam of a written slot is not the log-decay through its latest writer"
 
 
+@pytest.mark.oracle_pool
 @pytest.mark.parametrize("name", list(PLAN))
 def test_fullsize_backward(sdm, name):
     """The forward with its log and the recurrence backward at full size, launched as
     ``bench.py --backward`` launches them (addressing of keys and queries, one
-    sdm_recurrent_log call, one sdm_recurrent_backward call over all units and tokens). The
-    output gradient go is nonzero only on a window [0, P) of every unit: the loss then depends
-    only on those tokens, so the oracle's forward, log and backward over the window give every
-    gradient of a sampled unit (dv, dalpha, dbeta, both weight gradients and dM0), while past
-    the window every token gradient is exactly zero. The walk back over all T tokens must
-    restore M0 bit for bit in every unit. P is cut at the first token where the device's slot
-    lists differ from the oracle's (a tie), so that both sides differentiate the same slots."""
+    sdm_recurrent_log call, one sdm_recurrent_backward call over all units and tokens), with
+    an output gradient over every token: in every unit, the device's slot lists against the
+    oracle's addressing (ties counted), then every gradient (dv, dalpha, dbeta, the weight
+    gradients and dM0) against the oracle's forward, log and reverse walk on the device's
+    slots and weights; the walk back over all T tokens must restore M0 bit for bit."""
     import torch
     sh = W_[name]
-    units, _, _ = PLAN[name]
-    P = min(1024, sh.T)
     log(f"[full] backward {name}: generating inputs")
     inp = SI.make_inputs(sh)
     dev = upload(inp, sh)
@@ -430,30 +427,11 @@ def test_fullsize_backward(sdm, name):
     rg = torch.empty(shp_r, dtype=torch.float32, device="cuda")
     sdm.address(S, dev["k"], dev["subkeys"], sh.W, wi, wg)
     sdm.address(S, dev["q"], dev["subkeys"], sh.R, ri, rg)
-    torch.cuda.synchronize()
-    ref = {}
-    for (b, h) in units:
-        Up = unit_inputs(inp, sh, b, h, T=P)
-        owi, oww, _ = O.address(Up["k"], Up["C1"], Up["C2"], sh.kappa, sh.W)
-        ori, orw, _ = O.address(Up["q"], Up["C1"], Up["C2"], sh.kappa, sh.R)
-        gw, gr = wi[b, h, :P].cpu().numpy(), ri[b, h, :P].cpu().numpy()
-        _, _, fw = compare_indices(gw, owi, Up["k"], Up["C1"], Up["C2"], sh.N)
-        _, _, fr = compare_indices(gr, ori, Up["q"], Up["C1"], Up["C2"], sh.N)
-        assert not fw and not fr
-        diff = np.nonzero((gw != owi).any(1) | (gr != ori).any(1))[0]
-        if len(diff):
-            P = min(P, int(diff[0]))
-        ref[(b, h)] = (Up, owi, oww, ori, orw)
-    assert P >= 256, f"{name}: slot lists differ from the oracle's at token {P}"
-    rng = np.random.default_rng(29)
-    go_h = np.zeros((sh.B, sh.H, sh.T, sh.d_v), np.float32)
-    go_h[:, :, :P] = rng.standard_normal((sh.B, sh.H, P, sh.d_v)).astype(np.float32)
-    go = to_dev(go_h, "f32")
-    del go_h
+    go = torch.randn((sh.B, sh.H, sh.T, sh.d_v), device="cuda", generator=torch.Generator("cuda").manual_seed(29))
     o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
     xlog = empty_mem((sh.B, sh.H, sh.T, sh.W, sh.d_v), sh.mem_dtype)
     ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
-    log(f"[full] backward {name}: log and backward B={sh.B} H={sh.H} T={sh.T}, go window {P}")
+    log(f"[full] backward {name}: log and backward B={sh.B} H={sh.H} T={sh.T}")
     sdm.recurrent_log(S, wi, wg, ri, rg, dev["v"], dev["alpha"], dev["beta"], M, o, xlog, ws)
     G = torch.zeros((sh.B, sh.H, sh.N, sh.d_v), dtype=torch.float32, device="cuda")
     dv = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
@@ -465,23 +443,41 @@ def test_fullsize_backward(sdm, name):
     sdm.recurrent_backward(S, wi, wg, ri, rg, dev["v"], dev["alpha"], dev["beta"], M, xlog, go, G, dv, dal, dbe,
                            dwg, drg, bws)
     torch.cuda.synchronize()
+    del xlog
     assert sdm.workspace_error(bws) == 0, "a workgroup of the backward gave up waiting"
     assert torch.equal(M, M0_dev), "the undo over the whole sequence did not restore M0 bit for bit"
-    for nm, t in (("dv", dv), ("dalpha", dal), ("dbeta", dbe), ("dwgt", dwg), ("drgt", drg)):
-        nz = int(torch.count_nonzero(t[:, :, P:]))
-        assert nz == 0, f"{nm}: {nz} nonzero entries past the go window"
+    del M, M0_dev
     tol = tolerance(sh)
-    for (b, h), (Up, owi, oww, ori, orw) in ref.items():
-        wwp, rwp = oww[:P].astype(np.float32).astype(np.float64), orw[:P].astype(np.float32).astype(np.float64)
-        v, al, be = Up["v"][:P], Up["alpha"][:P], Up["beta"][:P]
-        _, MT = O.recurrence(Up["M0"], owi[:P], wwp, ori[:P], rwp, v, al, be, sh.mem_dtype)
-        xl = O.recurrence_log(Up["M0"], owi[:P], wwp, v, al, be, sh.mem_dtype)
-        g = O.recurrence_backward(MT, xl, owi[:P], wwp, ori[:P], rwp, v, al, be, go[b, h, :P].cpu().numpy()
-                                  .astype(np.float64))
-        out = {"dv": dv[b, h, :P], "dalpha": dal[b, h, :P], "dbeta": dbe[b, h, :P], "dwgt": dwg[b, h, :P],
-               "drgt": drg[b, h, :P], "dM0": G[b, h]}
-        errs = {k: rel_err(t.cpu().numpy(), g[k]) for k, t in out.items()}
-        log(f"[full] backward {name} unit ({b},{h}): " + " ".join(f"{k} {e:.1e}" for k, e in errs.items()) +
-            f" (tol {tol})")
-        for k, e in errs.items():
-            assert e < tol, k
+    need = G.numel() * 4 + 2 * go.numel() * 4
+    with SharedDir(need) as sd:
+        for n in ("q", "k", "v", "alpha", "beta", "subkeys", "M0"):
+            sd.save(n, inp[n])
+        for n, t in (("widx", wi), ("wgt", wg), ("ridx", ri), ("rgt", rg), ("go", go), ("dv", dv), ("dalpha", dal),
+                     ("dbeta", dbe), ("dwgt", dwg), ("drgt", drg), ("G", G)):
+            sd.save(n, t.cpu().numpy())
+        del G
+        tasks = [dict(dir=sd.path, shape=sh, b=b, h=h) for b in range(sh.B) for h in range(sh.H)]
+        log(f"[full] backward {name}: oracle over {len(tasks)} units in {pool_size()} workers")
+        results = []
+        t0 = time.time()
+        for r in pool().imap_unordered(unit_backward_parity, tasks, chunksize=1):
+            results.append(r)
+            if len(results) % max(1, len(tasks) // 8) == 0 or len(results) == len(tasks):
+                log(f"[full] backward {name}: {len(results)}/{len(tasks)} units checked ({time.time() - t0:.0f} s)")
+    fails = [(r["b"], r["h"], r["fails"]) for r in results if r["fails"]]
+    assert not fails, f"{name}: slot lists differ from the oracle's beyond ties: {fails[:3]}"
+    worst = {}
+    for r in results:
+        for n, e in r["errs"].items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    rec = {"workload": f"{name}_backward", "units_compared": len(results),
+           "token_heads_compared": int(sum(r["tokens"] for r in results)),
+           "tie_positions": int(sum(r["ties"] for r in results)),
+           "max_rel_err": worst, "tolerance": tol, "m0_restored_bit_for_bit": True,
+           "oracle_workers": pool_size(),
+           "form": "recurrence backward on the device's slots and float32 weights, output gradient on every token"}
+    write_record(rec)
+    log(f"[full] backward {name}: {len(results)} units, every token: " +
+        " ".join(f"{n} {e:.1e}" for n, e in worst.items()) + f" (tol {tol}); tie positions {rec['tie_positions']}")
+    for n, e in worst.items():
+        assert e < tol, n

@@ -297,6 +297,18 @@ sdm_status sdm_output_gate(const sdm_shape* shape, const float* o, const void* z
  *   rows), y [M, N] f32 out. K a multiple of 32; bf16 products, float32 sums (MFMA). */
 sdm_status sdm_head_mix(const void* x, const void* Wo, float* y, int64_t M, int32_t K, int32_t N, void* stream);
 
+/* The two calls above in one pass, without the bf16 x in memory (PL §3 "Sparse retrieval":
+ * RMS-normalised, elementwise gated, projected into the layer output):
+ *   y[b*T + t, n] = sum_h sum_c x[b,t,h,c] Wo[n, h*d_v + c]
+ * with x[b,t,h,:] = bf16(o[b,h,t,:] / sqrt(mean(o[b,h,t,:]^2) + eps) * w * silu(z[b,t,h,:])),
+ * bit for bit the x that sdm_output_gate stores (both sum the squares in the same order). o [B,H,T,d_v] f32; z [B,T,H,d_v] in_dtype; w [d_v] f32; Wo [d_model, H*d_v] bf16;
+ * y [B*T, d_model] f32 out, which may not overlap the inputs. d_v one of 32, 64, 128, 256
+ * and H*d_v <= 2552 (x of 32 tokens stays in one workgroup's LDS), B*T <= 2^27, else
+ * SDM_ERR_UNSUPPORTED; 1 <= d_model <= 2^22; 0 <= eps <= 1; every pointer 16-byte aligned.
+ * bf16 products, float32 sums (MFMA). */
+sdm_status sdm_output_project(const sdm_shape* shape, const float* o, const void* z, const float* w, float eps,
+                              const void* Wo, int32_t d_model, float* y, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Whole-table decay variant. The calls above decay only the W written rows by alpha_t. If
  * alpha_t instead decays every row of the table, as the dense state of Gated DeltaNet

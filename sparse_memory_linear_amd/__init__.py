@@ -19,7 +19,7 @@ __all__ = [
     "make_shape", "check_shape", "workspace_bytes", "init_from_M0", "address", "recurrent",
     "forward", "forward_static", "STATIC_SCRATCH_BYTES", "forward_uses_chunkwise", "decode_step", "workspace_error", "status_string", "abi_version",
     "decay_state_init", "workspace_bytes_decay", "recurrent_decay", "forward_decay", "decode_step_decay",
-    "materialize", "gates", "output_gate", "head_mix", "recurrent_log", "recurrent_backward",
+    "materialize", "gates", "output_gate", "head_mix", "output_project", "recurrent_log", "recurrent_backward",
     "backward_workspace_bytes", "address_backward", "workspace_bytes_chunked", "recurrent_chunked",
 ]
 
@@ -79,6 +79,7 @@ _SIGS = {
     "sdm_gates": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
     "sdm_output_gate": (ctypes.c_int, [_SP, _P, _P, _P, ctypes.c_float, _P, _P]),
     "sdm_head_mix": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P]),
+    "sdm_output_project": (ctypes.c_int, [_SP, _P, _P, _P, ctypes.c_float, _P, ctypes.c_int32, _P, _P]),
     "sdm_recurrent_log": (ctypes.c_int, [_SP] + [_P] * 11 + [ctypes.c_size_t, _P]),
     "sdm_backward_workspace_bytes": (ctypes.c_size_t, [_SP]),
     "sdm_workspace_bytes_chunked": (ctypes.c_size_t, [_SP]),
@@ -253,6 +254,11 @@ def head_mix(x, Wo, y, M: int, K: int, N: int, stream=None):
 
 
 # ----------------------------------------------------------------------------- backward
+def output_project(shape: Shape, o, z, w, eps: float, Wo, d_model: int, y, stream=None):
+    _check(lib().sdm_output_project(ctypes.byref(shape), _ptr(o), _ptr(z), _ptr(w), float(eps), _ptr(Wo),
+                                    int(d_model), _ptr(y), _stream(stream)), "sdm_output_project")
+
+
 def recurrent_log(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, xlog, ws, stream=None):
     _check(lib().sdm_recurrent_log(ctypes.byref(shape), _ptr(widx), _ptr(wgt), _ptr(ridx), _ptr(rgt), _ptr(v),
                                    _ptr(alpha), _ptr(beta), _ptr(M), _ptr(o), _ptr(xlog), _ptr(ws),

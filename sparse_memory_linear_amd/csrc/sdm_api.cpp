@@ -549,6 +549,8 @@ sdm_status sdm_output_gate(const sdm_shape* S, const float* o, const void* z, co
   if (!o || !z || !w || !x || !aligned16(o) || !aligned16(z) || !aligned16(w) || !aligned16(x))
     return SDM_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || eps > 1.f) return SDM_ERR_INVALID_ARG;
+  // grid: one thread per 8 values (at most 2^32 threads)
+  if ((int64_t)S->B * S->H * S->T * S->d_v > ((int64_t)1 << 34)) return SDM_ERR_UNSUPPORTED;
   const size_t ob = tensor_bytes(*S, S->d_v, 4), zb = tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype));
   const size_t xb = tensor_bytes(*S, S->d_v, 2);
   if (overlaps(x, xb, o, ob) || overlaps(x, xb, z, zb) || overlaps(x, xb, w, (size_t)S->d_v * 4))
@@ -559,12 +561,35 @@ sdm_status sdm_output_gate(const sdm_shape* S, const float* o, const void* z, co
 
 sdm_status sdm_head_mix(const void* x, const void* Wo, float* y, int64_t M, int32_t K, int32_t N, void* stream) {
   if (M < 0 || K < 32 || K % 32 != 0 || N < 1) return SDM_ERR_INVALID_ARG;
-  if (M > ((int64_t)1 << 40) || K > (1 << 20) || N > (1 << 22)) return SDM_ERR_UNSUPPORTED;
+  // grid: ceil(M/128) workgroups of 256 threads along x stay below 2^32 threads
+  if (M > ((int64_t)1 << 30) || K > (1 << 20) || N > (1 << 22)) return SDM_ERR_UNSUPPORTED;
   if (!x || !Wo || !y || !aligned16(x) || !aligned16(Wo) || !aligned16(y)) return SDM_ERR_INVALID_ARG;
   const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K * 2, yb = (size_t)M * N * 4;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, Wo, wb)) return SDM_ERR_INVALID_ARG;
   if (M == 0) return SDM_OK;
   return hip_status(launch_head_mix((const uint16_t*)x, (const uint16_t*)Wo, y, (long long)M, K, N, (hipStream_t)stream));
+}
+
+sdm_status sdm_output_project(const sdm_shape* S, const float* o, const void* z, const float* w, float eps,
+                              const void* Wo, int32_t d_model, float* y, void* stream) {
+  sdm_status st = check_shape(S, true);
+  if (st != SDM_OK) return st;
+  if (!o || !z || !w || !Wo || !y || !aligned16(o) || !aligned16(z) || !aligned16(w) || !aligned16(Wo) ||
+      !aligned16(y))
+    return SDM_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || eps > 1.f || d_model < 1) return SDM_ERR_INVALID_ARG;
+  if (!output_project_supported(S->d_v, S->H) || d_model > (1 << 22)) return SDM_ERR_UNSUPPORTED;
+  // row bases of o and z are 32-bit token-head counts
+  if ((int64_t)S->B * S->H * S->T > (int64_t)INT32_MAX - S->H * (int64_t)S->T) return SDM_ERR_UNSUPPORTED;
+  if ((int64_t)S->B * S->T > ((int64_t)1 << 27)) return SDM_ERR_UNSUPPORTED;  // grid of 32-token workgroups
+  const size_t ob = tensor_bytes(*S, S->d_v, 4), zb = tensor_bytes(*S, S->d_v, dtype_size(S->in_dtype));
+  const size_t wob = (size_t)d_model * S->H * S->d_v * 2, yb = (size_t)S->B * S->T * d_model * 4;
+  if (overlaps(y, yb, o, ob) || overlaps(y, yb, z, zb) || overlaps(y, yb, w, (size_t)S->d_v * 4) ||
+      overlaps(y, yb, Wo, wob))
+    return SDM_ERR_INVALID_ARG;
+  if (S->T == 0) return SDM_OK;
+  return hip_status(
+      launch_output_project(*S, o, z, w, eps, (const uint16_t*)Wo, d_model, y, (hipStream_t)stream));
 }
 
 sdm_status sdm_workspace_error(const void* ws, size_t ws_bytes, int64_t* host_count, void* stream) {

@@ -54,6 +54,52 @@ __global__ void __launch_bounds__(256) output_gate_kernel(const float* o, const 
   }
 }
 
+// Same output for d_v in {32, 64, 128, 256}: DV / 8 lanes per token-head, 8 values each
+// (two 16-byte loads of o, one or two of z, one 16-byte store of x), 64 / (DV / 8)
+// token-heads per wave; the sum of squares is a reduction over the token-head's lanes.
+template <bool ZBF16, int DV>
+__global__ void __launch_bounds__(256) output_gate_vec_kernel(const float* o, const void* z, const float* w,
+                                                              float eps, uint16_t* x, int H, int T, long long units) {
+  constexpr int L = DV / 8;
+  const long long th = ((long long)blockIdx.x * 256 + threadIdx.x) / L;  // (b, h, t)
+  const int cp = (threadIdx.x % L) * 8;
+  const bool live = th < units;  // every lane takes part in the reduction
+  const long long thc = live ? th : units - 1;
+  const int t = (int)(thc % T);
+  const long long bh = thc / T;
+  const int h = (int)(bh % H);
+  const long long b = bh / H;
+  const float* orow = o + thc * DV + cp;
+  const float4 o0 = *(const float4*)orow, o1 = *(const float4*)(orow + 4);
+  const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+  const long long zo = ((b * T + t) * H + h) * DV + cp;  // row of x and z
+  float zv[8];
+  if (ZBF16) {
+    const uint4 zq = *(const uint4*)((const uint16_t*)z + zo);
+    const uint32_t zw[4] = {zq.x, zq.y, zq.z, zq.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) zv[c] = (c & 1) ? bf16hi(zw[c >> 1]) : bf16lo(zw[c >> 1]);
+  } else {
+    const float4 z0 = *(const float4*)((const float*)z + zo), z1 = *(const float4*)((const float*)z + zo + 4);
+    zv[0] = z0.x; zv[1] = z0.y; zv[2] = z0.z; zv[3] = z0.w;
+    zv[4] = z1.x; zv[5] = z1.y; zv[6] = z1.z; zv[7] = z1.w;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) ss = fmaf(ov[c], ov[c], ss);
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) ss += shfl_xor_f32(ss, m);
+  const float r = rsqrtf(ss / (float)DV + eps);
+  uint32_t xw[4];
+#pragma unroll
+  for (int c = 0; c < 8; c += 2) {
+    const float y0 = ov[c] * r * w[cp + c] * (zv[c] / (1.f + expf(-zv[c])));
+    const float y1 = ov[c + 1] * r * w[cp + c + 1] * (zv[c + 1] / (1.f + expf(-zv[c + 1])));
+    xw[c >> 1] = pack_bf16x2(y0, y1);
+  }
+  if (live) *(uint4*)(x + zo) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+}
+
 // ------------------------------------------------------------------ head mixing
 // y[M, N] = x[M, K] . Wo[N, K]^T, bf16 operands, float32 accumulation on MFMA
 // (v_mfma_f32_32x32x16_bf16). Workgroup tile 128 x 128 (four waves, 64 x 64 each); K in
@@ -130,7 +176,228 @@ __global__ void __launch_bounds__(256) head_mix_kernel(const uint16_t* X, const 
     }
 }
 
+// ------------------------------------------------------------------ gate fused into mixing
+// y[m, n] = sum_h sum_c x[m, h, c] Wo[n, h d_v + c] with x = the bf16 output of the
+// normalisation and gate above, never written to memory. One workgroup (8 waves) owns RM
+// rows (tokens) and every column of y:
+//   1. x for its rows and all K = H d_v columns goes into LDS: each head's row piece of d_v
+//      values is loaded by DV / 8 lanes (8 values each), whose sum of squares is a reduction
+//      over those lanes; o is read once, in float32, straight from the recurrence's output.
+//   2. each wave takes groups of 64 output columns in turn and multiplies the resident x by
+//      those 64 rows of Wo: x fragments come from LDS, Wo fragments straight from memory into
+//      registers (no wave shares them, so staging them through LDS would buy nothing), loaded
+//      four K steps ahead of the MFMAs. No barrier in this part.
+// The gate of every token-head is thus evaluated once, whatever d_model is.
+constexpr int kProjThreads = 512;
+constexpr int kProjAhead = 4;  // K steps of 16 whose Wo fragments are in flight
+
+struct OutProjArgs {
+  const float* o;     // [B,H,T,DV] f32
+  const void* z;      // [B,T,H,DV] bf16 or f32
+  const float* w;     // [DV]
+  const uint16_t* Wo; // [N, H*DV] bf16
+  float* y;           // [B*T, N] f32
+  float eps;
+  int H, T, N;
+  long long M;        // B*T
+};
+
+size_t output_project_lds(int rm, int K) { return (size_t)rm * (K + 8) * 2; }
+
+template <bool ZBF16, int DV, int RM>
+__global__ void __launch_bounds__(kProjThreads) output_project_kernel(OutProjArgs A) {
+  extern __shared__ __align__(16) uint16_t As[];  // [RM][K + 8]
+  constexpr int L = DV / 8;                       // lanes per row piece, 8 columns each
+  constexpr int RP = kProjThreads / L;            // row pieces per pass
+  constexpr int NP = (RM + RP - 1) / RP;          // passes per head
+  const int H = A.H, T = A.T, K = A.H * DV, PA = K + 8;
+  const long long m0 = (long long)blockIdx.x * RM;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // ---- 1. gated x of the RM rows into LDS
+  {
+    const int cp = (tid % L) * 8, rr = tid / L;
+    int ob[NP], zb[NP];  // o row base b*H*T + t, z row base (b*T + t)*H; -1 past M or past RM
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int row = rr + RP * i;
+      const long long m = m0 + row;
+      if (row < RM && m < A.M) {
+        const int b = (int)(m / T), t = (int)(m % T);
+        ob[i] = b * H * T + t;
+        zb[i] = (b * T + t) * H;
+      } else {
+        ob[i] = -1;
+        zb[i] = 0;
+      }
+    }
+    float wv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) wv[c] = A.w[cp + c];
+    float4 oa[NP][2];
+    uint4 za[NP][ZBF16 ? 1 : 2];
+    auto load = [&](int h) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        if (ob[i] >= 0) {
+          const float* orow = A.o + (size_t)(ob[i] + h * T) * DV + cp;
+          oa[i][0] = *(const float4*)orow;
+          oa[i][1] = *(const float4*)(orow + 4);
+          const size_t zo = (size_t)(zb[i] + h) * DV + cp;
+          if (ZBF16) {
+            za[i][0] = *(const uint4*)((const uint16_t*)A.z + zo);
+          } else {
+            za[i][0] = *(const uint4*)((const float*)A.z + zo);
+            za[i][ZBF16 ? 0 : 1] = *(const uint4*)((const float*)A.z + zo + 4);  // (index 1 when float32)
+          }
+        } else {
+          oa[i][0] = oa[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    };
+    load(0);
+    for (int h = 0; h < H; ++h) {
+      float ov[NP][8];
+      uint32_t zw[NP][ZBF16 ? 4 : 8];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        ov[i][0] = oa[i][0].x; ov[i][1] = oa[i][0].y; ov[i][2] = oa[i][0].z; ov[i][3] = oa[i][0].w;
+        ov[i][4] = oa[i][1].x; ov[i][5] = oa[i][1].y; ov[i][6] = oa[i][1].z; ov[i][7] = oa[i][1].w;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(za[i]);
+#pragma unroll
+        for (int q = 0; q < (ZBF16 ? 4 : 8); ++q) zw[i][q] = src[q];
+      }
+      if (h + 1 < H) load(h + 1);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) ss = fmaf(ov[i][c], ov[i][c], ss);
+#pragma unroll
+        for (int m = 1; m < L; m <<= 1) ss += shfl_xor_f32(ss, m);
+        const float r = rsqrtf(ss / (float)DV + A.eps);
+        uint32_t xw[4];
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+          float zz[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            zz[e] = ZBF16 ? (((c + e) & 1) ? bf16hi(zw[i][(c + e) >> 1]) : bf16lo(zw[i][(c + e) >> 1]))
+                          : __uint_as_float(zw[i][c + e]);
+          const float y0 = ov[i][c] * r * wv[c] * (zz[0] / (1.f + expf(-zz[0])));
+          const float y1 = ov[i][c + 1] * r * wv[c + 1] * (zz[1] / (1.f + expf(-zz[1])));
+          xw[c >> 1] = pack_bf16x2(y0, y1);
+        }
+        const int row = rr + RP * i;
+        if (row < RM)
+          *(uint4*)(As + row * PA + h * DV + cp) =
+              ob[i] >= 0 ? make_uint4(xw[0], xw[1], xw[2], xw[3]) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. groups of 64 columns against the resident x, one wave per group
+  constexpr int RB = RM / 32;  // 32-row blocks
+  const int nk = K / 16;       // K steps (K is a multiple of 32)
+  const int kq = (lane >> 5) * 8;
+  const int groups = (A.N + 63) / 64;
+  for (int g = wave; g < groups; g += kProjThreads / 64) {
+    // this lane's two rows of Wo (columns of y); past N the row is clamped to N - 1 and its
+    // result is not stored
+    const uint16_t* wr[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wr[j] = A.Wo + (size_t)min(g * 64 + 32 * j + (lane & 31), A.N - 1) * K + kq;
+    float16_t acc[RB][2];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i][0] = acc[i][1] = float16_t{};
+    uint4 bq[kProjAhead][2];
+#pragma unroll
+    for (int d = 0; d < kProjAhead; ++d)
+      if (d < nk) {
+        bq[d][0] = *(const uint4*)(wr[0] + 16 * d);
+        bq[d][1] = *(const uint4*)(wr[1] + 16 * d);
+      }
+    for (int k0 = 0; k0 < nk; k0 += kProjAhead) {
+#pragma unroll
+      for (int d = 0; d < kProjAhead; ++d) {
+        const int k = k0 + d;
+        if (k < nk) {
+          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, bq[d][0]);
+          const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, bq[d][1]);
+          if (k + kProjAhead < nk) {
+            bq[d][0] = *(const uint4*)(wr[0] + 16 * (k + kProjAhead));
+            bq[d][1] = *(const uint4*)(wr[1] + 16 * (k + kProjAhead));
+          }
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const bf16x8_t a =
+                __builtin_bit_cast(bf16x8_t, *(const uint4*)(As + (i * 32 + (lane & 31)) * PA + 16 * k + kq));
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // D[row][col]: lane holds col = lane % 32, rows 8*(e/4) + 4*(lane/32) + e%4
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = g * 64 + 32 * j + (lane & 31);
+      if (col >= A.N) continue;
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const long long row = m0 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (row < A.M) A.y[row * A.N + col] = acc[i][j][e];
+        }
+    }
+  }
+}
+
+template <bool ZBF16, int RM>
+hipError_t launch_output_project_dv(const OutProjArgs& A, int d_v, hipStream_t stream) {
+  const unsigned grid = (unsigned)((A.M + RM - 1) / RM);
+  const size_t lds = output_project_lds(RM, A.H * d_v);
+  const dim3 blk(kProjThreads);
+  switch (d_v) {
+    case 32: hipLaunchKernelGGL((output_project_kernel<ZBF16, 32, RM>), dim3(grid), blk, lds, stream, A); break;
+    case 64: hipLaunchKernelGGL((output_project_kernel<ZBF16, 64, RM>), dim3(grid), blk, lds, stream, A); break;
+    case 128: hipLaunchKernelGGL((output_project_kernel<ZBF16, 128, RM>), dim3(grid), blk, lds, stream, A); break;
+    case 256: hipLaunchKernelGGL((output_project_kernel<ZBF16, 256, RM>), dim3(grid), blk, lds, stream, A); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// rows per workgroup: 64 while x of 64 rows fits in LDS, else 32
+int output_project_rows(int K) { return output_project_lds(64, K) <= 160 * 1024 ? 64 : 32; }
+
 }  // namespace
+
+bool output_project_supported(int d_v, int H) {
+  return (d_v == 32 || d_v == 64 || d_v == 128 || d_v == 256) && output_project_lds(32, H * d_v) <= 160 * 1024;
+}
+
+hipError_t launch_output_project(const sdm_shape& S, const float* o, const void* z, const float* w, float eps,
+                                 const uint16_t* Wo, int d_model, float* y, hipStream_t stream) {
+  if (!output_project_supported(S.d_v, S.H)) return hipErrorInvalidValue;
+  OutProjArgs A;
+  A.o = o;
+  A.z = z;
+  A.w = w;
+  A.Wo = Wo;
+  A.y = y;
+  A.eps = eps;
+  A.H = S.H;
+  A.T = S.T;
+  A.N = d_model;
+  A.M = (long long)S.B * S.T;
+  const bool zb = S.in_dtype == SDM_BF16;
+  if (output_project_rows(S.H * S.d_v) == 64)
+    return zb ? launch_output_project_dv<true, 64>(A, S.d_v, stream) : launch_output_project_dv<false, 64>(A, S.d_v, stream);
+  return zb ? launch_output_project_dv<true, 32>(A, S.d_v, stream) : launch_output_project_dv<false, 32>(A, S.d_v, stream);
+}
 
 hipError_t launch_gates(const sdm_shape& S, const float* a, const float* b, const float* A_log, const float* dt_bias,
                         float* alpha, float* beta, hipStream_t stream) {
@@ -143,6 +410,20 @@ hipError_t launch_gates(const sdm_shape& S, const float* a, const float* b, cons
 hipError_t launch_output_gate(const sdm_shape& S, const float* o, const void* z, const float* w, float eps,
                               uint16_t* x, hipStream_t stream) {
   const long long units = (long long)S.B * S.H * S.T;
+  if (S.d_v == 32 || S.d_v == 64 || S.d_v == 128 || S.d_v == 256) {
+    const dim3 g((unsigned)((units * (S.d_v / 8) + 255) / 256));
+    const bool zb = S.in_dtype == SDM_BF16;
+#define SDM_GATE_VEC(DV)                                                                                           \
+  if (S.d_v == DV) {                                                                                               \
+    if (zb) hipLaunchKernelGGL((output_gate_vec_kernel<true, DV>), g, dim3(256), 0, stream, o, z, w, eps, x, S.H,  \
+                               S.T, units);                                                                        \
+    else hipLaunchKernelGGL((output_gate_vec_kernel<false, DV>), g, dim3(256), 0, stream, o, z, w, eps, x, S.H,    \
+                            S.T, units);                                                                           \
+  }
+    SDM_GATE_VEC(32) SDM_GATE_VEC(64) SDM_GATE_VEC(128) SDM_GATE_VEC(256)
+#undef SDM_GATE_VEC
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((units + 3) / 4));
   if (S.in_dtype == SDM_BF16)
     hipLaunchKernelGGL(output_gate_kernel<true>, grid, dim3(256), 0, stream, o, z, w, eps, x, S.H, S.T, S.d_v, units);

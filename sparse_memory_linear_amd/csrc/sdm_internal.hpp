@@ -83,6 +83,9 @@ hipError_t launch_output_gate(const sdm_shape& S, const float* o, const void* z,
                               uint16_t* x, hipStream_t stream);
 hipError_t launch_head_mix(const uint16_t* x, const uint16_t* Wo, float* y, long long M, int K, int N,
                            hipStream_t stream);
+bool output_project_supported(int d_v, int H);  // d_v and K = H d_v the fused epilogue takes
+hipError_t launch_output_project(const sdm_shape& S, const float* o, const void* z, const float* w, float eps,
+                                 const uint16_t* Wo, int d_model, float* y, hipStream_t stream);
 hipError_t launch_materialize(const sdm_shape& S, const void* M, const double* lam, const double* lrun, float* out,
                               hipStream_t stream);
 

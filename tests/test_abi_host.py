@@ -206,6 +206,19 @@ def test_epilogue_calls_validate(sdm, no_gpu):
     assert L.sdm_head_mix(p[0], p[1], p[2], 100, 64, 0, None) == -1     # no output columns
     assert L.sdm_head_mix(p[0], p[1], p[0] + 64, 100, 64, 64, None) == -1  # y overlaps x
     assert L.sdm_head_mix(p[0], p[1], p[2], 0, 64, 64, None) == 0       # nothing to do
+    assert L.sdm_head_mix(p[0], p[1], p[2], 1 << 31, 64, 64, None) == -2  # grid beyond the launch limit
+    f = ctypes.c_float
+    assert L.sdm_output_project(sp, p[0], p[1], p[2], f(-1.0), p[3], 256, p[4], None) == -1  # negative eps
+    assert L.sdm_output_project(sp, p[0], p[1], p[2], f(1e-5), p[3], 0, p[4], None) == -1    # no output columns
+    assert L.sdm_output_project(sp, p[0], p[1], p[2], f(1e-5), p[3], 256, p[0] + 64, None) == -1  # y overlaps o
+    assert L.sdm_output_project(sp, p[0], p[1], p[2], f(1e-5), p[3], 256, p[3] + 64, None) == -1  # y overlaps Wo
+    assert L.sdm_output_project(sp, p[0], p[1] + 8, p[2], f(1e-5), p[3], 256, p[4], None) == -1  # misaligned z
+    S96 = base(d_v=96)
+    assert L.sdm_output_project(ctypes.byref(S96), p[0], p[1], p[2], f(1e-5), p[3], 256, p[4], None) == -2
+    S20 = base(H=21)  # K = H*d_v = 2688: x of 32 tokens does not fit in LDS
+    assert L.sdm_output_project(ctypes.byref(S20), p[0], p[1], p[2], f(1e-5), p[3], 256, p[4], None) == -2
+    S0 = base(T=0)
+    assert L.sdm_output_project(ctypes.byref(S0), p[0], p[1], p[2], f(1e-5), p[3], 256, p[4], None) == 0
 
 
 # ----------------------------------------------------------------------------- backward

@@ -72,9 +72,47 @@ def test_head_mix(sdm, M, K, N):
     assert e < 1e-5  # exact bf16 products, float32 sums
 
 
-def test_layer_end_to_end(sdm):
-    """Gates -> forward -> output normalisation and gate -> head mixing, against the oracle's
-    chain of the same steps on the same inputs."""
+@pytest.mark.parametrize("in_dtype,B,H,T,d_v,d_model", [
+    ("bf16", 2, 3, 70, 128, 200),   # ragged row tile across the batch boundary, ragged columns
+    ("f32", 1, 4, 300, 64, 384),
+    ("bf16", 3, 2, 129, 32, 128),
+    ("bf16", 1, 2, 260, 256, 130),
+    ("bf16", 1, 10, 100, 128, 256),  # K = 1280: 32 tokens per workgroup
+    ("f32", 2, 8, 40, 256, 64),      # K = 2048
+])
+def test_output_project(sdm, in_dtype, B, H, T, d_v, d_model):
+    """Normalisation, gate and head mixing in one pass: against the oracle's chain in float64
+    and against the two separate calls on the same inputs."""
+    import torch
+    sh = W_["small"].replace(B=B, H=H, T=T, d_v=d_v, in_dtype=in_dtype, mem_dtype="f32")
+    ep = SI.make_epilogue_inputs(sh, d_model=d_model)
+    rng = np.random.default_rng(B * 1000 + T + d_v)
+    o = rng.standard_normal((B, H, T, d_v)).astype(np.float32)
+    S = lib_shape(sh)
+    od, zd, wd, Wod = to_dev(o, "f32"), to_dev(ep["z"], in_dtype), to_dev(ep["w"], "f32"), to_dev(ep["Wo"], "bf16")
+    y = torch.full((B * T, d_model), float("nan"), dtype=torch.float32, device="cuda")
+    sdm.output_project(S, od, zd, wd, 1e-5, Wod, d_model, y)
+    x = torch.empty((B, T, H, d_v), dtype=torch.bfloat16, device="cuda")
+    sdm.output_gate(S, od, zd, wd, 1e-5, x)
+    y2 = torch.empty((B * T, d_model), dtype=torch.float32, device="cuda")
+    sdm.head_mix(x, Wod, y2, B * T, H * d_v, d_model)
+    torch.cuda.synchronize()
+    got, two = y.cpu().numpy(), y2.cpu().numpy()
+    assert np.isfinite(got).all()
+    xr = O.output_gate(o.transpose(0, 2, 1, 3), SI.widen(ep["z"], in_dtype), ep["w"], 1e-5)
+    ref = O.head_mix(xr.reshape(B * T, H * d_v), SI.widen(ep["Wo"], "bf16"))
+    e, e2 = rel_err(got, ref), rel_err(got, two)
+    log(f"[output project] {in_dtype} B={B} H={H} T={T} d_v={d_v} d_model={d_model}: rel err {e:.2e} "
+        f"(vs separate calls {e2:.2e})")
+    assert e < 1e-2   # one bf16 rounding of x, float32 sums
+    assert np.array_equal(got, two)  # same bf16 x, same products and sums
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_layer_end_to_end(sdm, fused):
+    """Gates -> forward -> output normalisation and gate -> head mixing (two calls, or the
+    fused sdm_output_project), against the oracle's chain of the same steps on the same
+    inputs."""
     import torch
     sh = W_["layer_1p4b"].replace(B=1, H=2, T=96)
     d_model = 256
@@ -91,10 +129,14 @@ def test_layer_end_to_end(sdm):
     o = torch.empty((sh.B, sh.H, sh.T, sh.d_v), dtype=torch.float32, device="cuda")
     ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
     sdm.forward(S, dev["q"], dev["k"], dev["v"], al, be, dev["subkeys"], M, o, ws)
-    x = torch.empty((sh.B, sh.T, sh.H, sh.d_v), dtype=torch.bfloat16, device="cuda")
-    sdm.output_gate(S, o, to_dev(ep["z"], sh.in_dtype), to_dev(ep["w"], "f32"), 1e-5, x)
     y = torch.empty((sh.B * sh.T, d_model), dtype=torch.float32, device="cuda")
-    sdm.head_mix(x, to_dev(ep["Wo"], "bf16"), y, sh.B * sh.T, sh.H * sh.d_v, d_model)
+    if fused:
+        sdm.output_project(S, o, to_dev(ep["z"], sh.in_dtype), to_dev(ep["w"], "f32"), 1e-5, to_dev(ep["Wo"], "bf16"),
+                           d_model, y)
+    else:
+        x = torch.empty((sh.B, sh.T, sh.H, sh.d_v), dtype=torch.bfloat16, device="cuda")
+        sdm.output_gate(S, o, to_dev(ep["z"], sh.in_dtype), to_dev(ep["w"], "f32"), 1e-5, x)
+        sdm.head_mix(x, to_dev(ep["Wo"], "bf16"), y, sh.B * sh.T, sh.H * sh.d_v, d_model)
     torch.cuda.synchronize()
     # oracle chain; the gates the device computed in float32 drive both recurrences
     ga = al.cpu().numpy().astype(np.float64)
@@ -111,5 +153,5 @@ def test_layer_end_to_end(sdm):
     xr = O.output_gate(oo, SI.widen(ep["z"], sh.in_dtype), ep["w"], 1e-5)
     yr = O.head_mix(xr.reshape(sh.B * sh.T, sh.H * sh.d_v), SI.widen(ep["Wo"], "bf16"))
     e = rel_err(y.cpu().numpy(), yr)
-    log(f"[layer] end to end rel err {e:.2e} (tol {tolerance(sh)})")
+    log(f"[layer] end to end ({'fused' if fused else 'two calls'}) rel err {e:.2e} (tol {tolerance(sh)})")
     assert e < tolerance(sh)

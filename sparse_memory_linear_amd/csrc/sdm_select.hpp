@@ -39,10 +39,16 @@ __device__ __forceinline__ void stair_pairs(int kappa, int n_sel, int (&pr)[EM])
   const int lane = lane_id();
 #pragma unroll
   for (int e = 0; e < EM; ++e) pr[e] = -1;
+  // row a's length min(kappa, n_sel / (a + 1)) is computed on lane a (one division for the
+  // whole wave) and read back row by row
+  int rowlen = 0;
+  if (lane < kappa) {
+    rowlen = n_sel / (lane + 1);
+    if (rowlen > kappa) rowlen = kappa;
+  }
   int base = 0;
   for (int a = 0; a < kappa; ++a) {
-    int cnt = n_sel / (a + 1);
-    if (cnt > kappa) cnt = kappa;
+    const int cnt = __builtin_amdgcn_readlane(rowlen, a);
     if (cnt <= 0) break;
 #pragma unroll
     for (int e = 0; e < EM; ++e) {

@@ -298,12 +298,12 @@ __global__ void __launch_bounds__(CW == 1 ? kMaxWaves * 64 : 512) backward_kerne
   const rsrc_t rDR = make_rs(A.drgt + ut * R, (size_t)T * R * 4);
   auto group_sum = [](float x) {
 #pragma unroll
-    for (int m = C; m < 64; m *= 2) x += shfl_xor_f32(x, m);
+    for (int m = C; m < 64; m *= 2) x = add_xor_f32(x, m);
     return x;
   };
   auto column_sum = [](float x) {
 #pragma unroll
-    for (int m = 1; m < C; m *= 2) x += shfl_xor_f32(x, m);
+    for (int m = 1; m < C; m *= 2) x = add_xor_f32(x, m);
     return x;
   };
   auto sync = [] {

@@ -733,7 +733,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 #pragma unroll
     for (int s = LPC; s < 32; s <<= 1)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] += shfl_xor_f32(acc[c], s);
+      for (int c = 0; c < CPL; ++c) acc[c] = add_xor_f32(acc[c], s);
     // lower half: delta = beta (v - alpha * read of the write rows); new write rows
     if (hh == 0) {
       float dl[CPL];
@@ -775,7 +775,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 #pragma unroll
       for (int s = LPC; s < 32; s <<= 1)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) cr[c] += shfl_xor_f32(cr[c], s);
+        for (int c = 0; c < CPL; ++c) cr[c] = add_xor_f32(cr[c], s);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[c] += cr[c];
     }

@@ -70,9 +70,28 @@ __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
   return __uint_as_float(shfl_xor_u32(__float_as_uint(v), mask));
 }
 
+// v + (v of lane ^ mask), for mask a power of two up to 32 (fold to a constant). Within a
+// row of 16 lanes the partner's value reaches the add through its DPP operand (one fused
+// v_add_f32_dpp; every partner lies inside the row, so the zero that bound_ctrl gives an
+// invalid source never occurs); mask 4 takes a half-row mirror first. The sum equals
+// v + shfl_xor_f32(v, mask) bit for bit.
+__device__ __forceinline__ float add_xor_f32(float v, int mask) {
+  const int x = __float_as_int(v);
+  switch (mask) {
+    case 1: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    case 2: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+    case 4: {
+      const int t = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);                            // half mirror
+      return v + __int_as_float(__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, true));         // quad reverse
+    }
+    case 8: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true));  // row_ror:8
+    default: return v + shfl_xor_f32(v, mask);
+  }
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f32(v, m);
+  for (int m = 32; m >= 1; m >>= 1) v = add_xor_f32(v, m);
   return v;
 }
 

@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(256) output_gate_vec_kernel(const float* o, co
 #pragma unroll
   for (int c = 0; c < 8; ++c) ss = fmaf(ov[c], ov[c], ss);
 #pragma unroll
-  for (int m = 1; m < L; m <<= 1) ss += shfl_xor_f32(ss, m);
+  for (int m = 1; m < L; m <<= 1) ss = add_xor_f32(ss, m);
   const float r = rsqrtf(ss / (float)DV + eps);
   uint32_t xw[4];
 #pragma unroll
@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(kProjThreads) output_project_kernel(OutProjArg
 #pragma unroll
         for (int c = 0; c < 8; ++c) ss = fmaf(ov[i][c], ov[i][c], ss);
 #pragma unroll
-        for (int m = 1; m < L; m <<= 1) ss += shfl_xor_f32(ss, m);
+        for (int m = 1; m < L; m <<= 1) ss = add_xor_f32(ss, m);
         const float r = rsqrtf(ss / (float)DV + A.eps);
         uint32_t xw[4];
 #pragma unroll

@@ -30,7 +30,15 @@ Without a mode flag the recurrence runs in the form sdm_forward takes for the sh
 (sdm_forward_uses_chunkwise: the chunkwise form for a float32 table with at least 32 units,
 else the pipeline); --pipeline forces the pipelined recurrence.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--decay | --backward | --chunked | --pipeline]
+With --epilogue the step is the calls on either side of the recurrence: the gates from their
+pre-activations, the output normalisation and gate, and the head mixing (d_model =
+--d-model, default H*d_v); the fused sdm_output_project is timed beside them and checked
+equal. ``roofline`` describes the head mixing (bf16 MFMA, against 2.5 PFLOP/s).
+
+The decode workload (T = 1) times consecutive fused decode steps captured as a HIP graph.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--decay | --backward | --chunked | --pipeline | --epilogue [--d-model D]]
 """
 from __future__ import annotations
 
@@ -172,9 +180,12 @@ def main():
     ap.add_argument("--backward", action="store_true", help="training step: forward with log and backward")
     ap.add_argument("--chunked", action="store_true", help="forward with the chunkwise two-phase recurrence")
     ap.add_argument("--pipeline", action="store_true", help="forward with the pipelined recurrence")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="the steps around the recurrence: gates, output gate fused into the head mixing")
+    ap.add_argument("--d-model", type=int, default=0, help="head mixing output width (default H*d_v)")
     args = ap.parse_args()
-    if args.decay + args.backward + args.chunked + args.pipeline > 1:
-        print("--decay, --backward, --chunked and --pipeline are separate modes", file=sys.stderr)
+    if args.decay + args.backward + args.chunked + args.pipeline + args.epilogue > 1:
+        print("--decay, --backward, --chunked, --pipeline and --epilogue are separate modes", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
@@ -187,6 +198,8 @@ def main():
     sh = SI.WORKLOADS[args.workload]
     if sh.T == 1:
         return bench_decode(args, sh)
+    if args.epilogue:
+        return bench_epilogue(args, sh)
     if args.decay or args.backward or args.chunked or args.pipeline:
         args.no_cpu_baseline = True  # the oracle baseline times the default forward
     log(f"[bench] generating {sh.name} inputs")
@@ -330,6 +343,87 @@ def main():
                                 "chunkwise recurrence (prep + apply)" if args.chunked else "recurrence"),
                      "ms_per_launch": rec_ms, "bytes_per_launch": launch_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_epilogue(args, sh):
+    """The steps on either side of the recurrence at a workload's shape: gates from their
+    pre-activations, the output normalisation and gate (sdm_output_gate) and the head mixing
+    (sdm_head_mix). One step = those three calls over all B*T tokens (the faster output path
+    at every shape measured); the fused sdm_output_project, which needs no bf16 x buffer, is
+    timed beside them and checked equal bit for bit. Inputs: the seeded epilogue inputs of
+    the workload and a seeded standard normal o in place of the recurrence's output (the
+    cost does not depend on its values)."""
+    import torch
+    import sparse_memory_linear_amd as S
+
+    d_model = args.d_model or sh.H * sh.d_v
+    log(f"[bench] epilogue: {sh.name}, d_model {d_model}")
+    ep = SI.make_epilogue_inputs(sh, d_model=d_model)
+    rng = np.random.default_rng([sh.seed, 11])
+    o_host = rng.standard_normal((sh.B, sh.H, sh.T, sh.d_v), dtype=np.float32)
+
+    def dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    shape = S.make_shape(sh.B, sh.H, sh.T, sh.N, sh.d_k, sh.d_v, sh.kappa, sh.W, sh.R, sh.in_dtype, sh.mem_dtype)
+    o = dev(o_host, "f32")
+    del o_host
+    z, w, Wo = dev(ep["z"], sh.in_dtype), dev(ep["w"], "f32"), dev(ep["Wo"], "bf16")
+    a, b, A_log, dt_bias = (dev(ep[k], "f32") for k in ("a", "b", "A_log", "dt_bias"))
+    M, K = sh.B * sh.T, sh.H * sh.d_v
+    alpha = torch.empty((sh.B, sh.H, sh.T), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(alpha)
+    x = torch.empty((sh.B, sh.T, sh.H, sh.d_v), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, d_model), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y)
+    calls = {
+        "gates": lambda: S.gates(shape, a, b, A_log, dt_bias, alpha, beta),
+        "output_project": lambda: S.output_project(shape, o, z, w, 1e-5, Wo, d_model, y),
+        "output_gate": lambda: S.output_gate(shape, o, z, w, 1e-5, x),
+        "head_mix": lambda: S.head_mix(x, Wo, y2, M, K, d_model),
+    }
+    for _ in range(max(1, args.warmup)):
+        for f in calls.values():
+            f()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "fused and two-call outputs differ"
+    times = {k: [] for k in calls}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for k, f in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            times[k].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    med = {k: sorted(a_.elapsed_time(b_) for a_, b_ in v)[len(v) // 2] for k, v in times.items()}
+    step_ms = med["gates"] + med["output_gate"] + med["head_mix"]
+    ib = 2 if sh.in_dtype == "bf16" else 4
+    proj_bytes = M * K * (4 + ib) + M * d_model * 4 + d_model * K * 2
+    flops = 2.0 * M * K * d_model
+    achieved = flops / (med["head_mix"] / 1e3) / 1e12
+    log(f"[bench] epilogue: gates {med['gates']:.3f} ms, output gate {med['output_gate']:.3f} ms, head mixing "
+        f"{med['head_mix']:.3f} ms ({achieved:.0f} TFLOP/s); fused output_project {med['output_project']:.3f} ms")
+    out = {
+        "metric": "SDM layer epilogue tokens/s (gates, output gate, head mixing) on 1 MI355X",
+        "value": M / (step_ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sh.name, "B": sh.B, "H": sh.H, "T": sh.T, "d_v": sh.d_v, "d_model": d_model,
+                   "in_dtype": sh.in_dtype, "gates_ms": med["gates"], "output_gate_ms": med["output_gate"],
+                   "head_mix_ms": med["head_mix"], "output_project_ms": med["output_project"],
+                   "output_project_gbs": proj_bytes / (med["output_project"] / 1e3) / 1e9},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": achieved / 2500.0, "traffic": None, "kernel": "head_mix (bf16 MFMA)",
+                     "ms_per_launch": med["head_mix"], "flops_per_launch": flops},
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

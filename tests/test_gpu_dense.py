@@ -8,6 +8,9 @@
   out here in float64 with no slot bookkeeping.
 * kappa = s and W = R = N through the whole forward (addressing included): the result must
   equal the dense gated delta rule with softmax weights over all N product-key scores.
+
+Beside them, the other boundary of the slot lists: indices outside [0, N) are skipped and
+counted.
 """
 import numpy as np
 import pytest
@@ -174,4 +177,53 @@ def test_dense_softmax_limit(sdm, B, H, T, s, d_k, d_v):
     chunk = sdm.forward_uses_chunkwise(S)
     log(f"[dense limit] B={B} H={H} T={T} N={N} ({'chunkwise' if chunk else 'pipeline'}): "
         f"rel err o {eo:.2e}, table {em:.2e}")
+    assert eo < TOL_F32 and em < TOL_F32
+
+
+@pytest.mark.parametrize("W", [8, 6])  # 8: the pipelined recurrence; 6: the sequential path
+def test_out_of_range_slots_are_skipped_and_counted(sdm, W):
+    """Slot indices outside [0, N) in the lists passed to sdm_recurrent touch nothing and
+    carry no weight; the workspace's error word counts them. Reference: the oracle's rule
+    applied token by token to each token's valid slots only."""
+    import torch
+    B, H, T, N, d_v = 1, 2, 40, 256, 32
+    rng = np.random.default_rng(W)
+    widx = np.stack([np.stack([rng.permutation(N)[:W] for _ in range(T)]) for _ in range(B * H)]).reshape(B, H, T, W)
+    ridx = rng.integers(0, N, (B, H, T, W))
+    bad_w = rng.random((B, H, T, W)) < 0.15
+    bad_r = rng.random((B, H, T, W)) < 0.15
+    widx = np.where(bad_w, np.where(rng.random(widx.shape) < 0.5, -1, N + 3), widx).astype(np.int32)
+    ridx = np.where(bad_r, np.where(rng.random(ridx.shape) < 0.5, -7, N), ridx).astype(np.int32)
+    f = lambda a: a.astype(np.float32).astype(np.float64)
+    wgt = f(rng.dirichlet(np.ones(W), (B, H, T)))
+    rgt = f(rng.dirichlet(np.ones(W), (B, H, T)))
+    v = f(rng.standard_normal((B, H, T, d_v)))
+    alpha = f(rng.uniform(0.6, 1.0, (B, H, T)))
+    beta = f(rng.uniform(0.0, 1.0, (B, H, T)))
+    M0 = f(rng.standard_normal((B, H, N, d_v)) * 0.2)
+    sh = W_["tiny_fp32"].replace(B=B, H=H, T=T, N=N, d_k=32, d_v=d_v, kappa=4, W=W, R=W)
+    S = lib_shape(sh)
+    M = to_dev(M0, "f32")
+    o = torch.empty((B, H, T, d_v), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sdm.workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    sdm.recurrent(S, to_dev(widx, "i32"), to_dev(wgt, "f32"), to_dev(ridx, "i32"), to_dev(rgt, "f32"), to_dev(v, "f32"),
+                  to_dev(alpha, "f32"), to_dev(beta, "f32"), M, o, ws)
+    torch.cuda.synchronize()
+    n_bad = int(bad_w.sum() + bad_r.sum())
+    assert sdm.workspace_error(ws) == n_bad
+    go, gM = o.cpu().numpy(), M.cpu().numpy()
+    eo = em = 0.0
+    for b in range(B):
+        for h in range(H):
+            Mr = M0[b, h].copy()
+            outs = []
+            for t in range(T):
+                kw, kr = ~bad_w[b, h, t], ~bad_r[b, h, t]
+                ro, Mr = O.recurrence(Mr, widx[b, h, t][kw][None], wgt[b, h, t][kw][None], ridx[b, h, t][kr][None],
+                                      rgt[b, h, t][kr][None], v[b, h, t][None], alpha[b, h, t:t + 1],
+                                      beta[b, h, t:t + 1], "f32")
+                outs.append(ro[0])
+            eo = max(eo, rel_err(go[b, h], np.array(outs)))
+            em = max(em, rel_err(gM[b, h], Mr))
+    log(f"[out-of-range slots] W={W}: {n_bad} skipped and counted; rel err o {eo:.2e}, table {em:.2e}")
     assert eo < TOL_F32 and em < TOL_F32

@@ -260,11 +260,12 @@ def summarise(name: str, sh, results, tol: float, extra=None) -> dict:
 
 
 def write_record(rec: dict, fname: str = "parity_fullsize.json") -> None:
-    """Adds the workload's record to gpurun_out/<fname> at the repository root."""
+    """Adds the workload's record to <dir>/<fname>, dir = $SDM_PARITY_RECORD_DIR (else a
+    directory under the system's temporary directory)."""
     import json
     import os
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    out = os.path.join(root, "gpurun_out")
+    import tempfile
+    out = os.environ.get("SDM_PARITY_RECORD_DIR") or os.path.join(tempfile.gettempdir(), "sdm_parity_records")
     os.makedirs(out, exist_ok=True)
     path = os.path.join(out, fname)
     data = {}

@@ -10,12 +10,14 @@ checked against the oracle (one unit per task in a pool of worker processes):
   oracle's chunkwise form, and against the token-by-token rule within the tolerance;
 * decode: one step over all 64 x 16 tables, every unit checked, after a prefill of four
   sequences that is itself checked in full;
-* the backward: with the output gradient nonzero only on a window of leading tokens, every
-  gradient of a sampled unit against the oracle's backward over that window, exact zeros
-  past it, and M0 restored bit for bit by the walk back over the whole sequence.
+* the whole-table decay variant at the 8B-scale shape: bit-identical to the written-rows
+  path when no gate decays, the running log-decay and the carried state consistent;
+* the backward, with an output gradient on every token: in every unit every gradient
+  against the oracle's forward, log and reverse walk on the device's slots and weights,
+  and M0 restored bit for bit by the walk back over the whole sequence.
 
 Per-workload records (units and token-heads compared, tie counts, worst errors) are
-written to gpurun_out/parity_fullsize.json.
+written to parity_fullsize.json in $SDM_PARITY_RECORD_DIR.
 """
 import time
 
@@ -113,7 +115,7 @@ def test_fullsize_forward(sdm, name):
     o at every token and the whole final table against the oracle run on the device's slot
     lists (the oracle's own lists wherever no tie occurred), rows no token writes bit-equal
     to M0. The per-workload record (tie counts, worst errors) goes to
-    gpurun_out/parity_fullsize.json."""
+    parity_fullsize.json in $SDM_PARITY_RECORD_DIR."""
     import torch
     sh = W_[name]
     log(f"[full] {name}: generating inputs")

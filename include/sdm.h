@@ -170,8 +170,10 @@ sdm_status sdm_forward_static(const sdm_shape* shape, const void* q, const void*
  * order rather than bit for bit; the pipeline is deterministic. */
 int sdm_forward_uses_chunkwise(const sdm_shape* shape);
 
-/* One decode step: T must be 1. Same result as sdm_forward with T = 1, fused into one
- * launch; needs no workspace.
+/* One decode step: T must be 1. The rule of sdm_forward with T = 1 (the same slots; sums
+ * equal up to the order of the float32 additions), fused into one kernel launch on `stream`
+ * and nothing else (no allocation, no memory fill), so a sequence of steps may be captured
+ * into a HIP graph and replayed; needs no workspace.
  *   q, k [B,H,1,d_k]; v [B,H,1,d_v]; alpha, beta [B,H,1]; M in/out; o [B,H,1,d_v] f32. */
 sdm_status sdm_decode_step(const sdm_shape* shape, const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const void* subkeys, void* M, float* o, void* stream);

@@ -312,3 +312,35 @@ def test_decode_step_parity(sdm):
             compared += 1
     log(f"[decode] rel err {worst:.2e} over {compared} units (tol {tol})")
     assert compared > 0 and worst < tol
+
+
+@pytest.mark.parametrize("name,mem", [("decode", "bf16"), ("decode", "f32"), ("small", "f32")])
+def test_decode_step_equals_forward_T1(sdm, name, mem):
+    """State carry, decode form: one sdm_decode_step on a table equals one sdm_forward with
+    T = 1 on a copy of the same table -- the same rows written (so the same slots) and the
+    same values up to the order of the float32 sums; every other row untouched by both."""
+    import torch
+    sh = W_[name].replace(B=3, H=4, T=1, mem_dtype=mem)
+    inp = SI.make_inputs(sh)
+    dev = upload(inp, sh)
+    S1 = lib_shape(sh, T=1)
+    Md = fresh_table(sdm, S1, sh, dev)
+    Mf = Md.clone()
+    od = torch.empty((sh.B, sh.H, 1, sh.d_v), dtype=torch.float32, device="cuda")
+    of = torch.empty_like(od)
+    sdm.decode_step(S1, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], Md, od)
+    ws = torch.empty(sdm.workspace_bytes(S1), dtype=torch.uint8, device="cuda")
+    sdm.forward(S1, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], Mf, of, ws)
+    torch.cuda.synchronize()
+    assert sdm.workspace_error(ws) == 0
+    M0 = fresh_table(sdm, S1, sh, dev)
+    torch.cuda.synchronize()
+    changed_d = (Md != M0).any(-1)
+    changed_f = (Mf != M0).any(-1)
+    assert torch.equal(changed_d, changed_f), "the decode step and the forward wrote different rows"
+    tol = 1e-5 if mem == "f32" else 1e-2  # bf16 rows: one rounding of sums taken in another order
+    eo = rel_err(od.cpu().numpy(), of.cpu().numpy())
+    em = rel_err(SI.widen(from_dev(Md, mem), mem), SI.widen(from_dev(Mf, mem), mem))
+    log(f"[decode = forward T=1] {name} {mem}: rel diff o {eo:.2e}, table {em:.2e}, "
+        f"{int(changed_d.sum())} rows written")
+    assert eo < tol and em < tol

@@ -127,8 +127,8 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   const int BT = A.B * A.T;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint64_t* wbuf = wbuf_all + wave * kWave;
-  int pr[EM];
-  stair_pairs<EM>(kappa, A.n_sel, pr);
+  int pr[EM], bdiv;
+  stair_pairs<EM>(kappa, A.n_sel, pr, &bdiv);
 
   for (int half = 0; half < 2; ++half) {
     score_half<BF16>(A, head, r0, half, sc);
@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
     const int16_t* i2 = sel_i + (n * 2 + 1) * kappa;
     const float* s1 = sel_s + (n * 2 + 0) * kappa;
     const float* s2 = sel_s + (n * 2 + 1) * kappa;
-    uint64_t k = merge_token<EM>(i1, s1, i2, s2, s, kappa, A.n_sel, pr, wbuf);
+    uint64_t k = merge_token<EM>(i1, s1, i2, s2, s, kappa, A.n_sel, pr, bdiv, wbuf);
     float scv = lane < A.n_sel ? key_score(k) : -INFINITY;
     float mx = __shfl(scv, 0, kWave);
     float e = lane < A.n_sel ? expf(scv - mx) : 0.f;

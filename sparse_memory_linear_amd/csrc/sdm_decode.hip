@@ -138,6 +138,12 @@ __global__ void __launch_bounds__(kGroup * UPW) decode_kernel(DecArgs A) {
   float* sdelta = (float*)(ub + L.delta);
   int* anymatch = (int*)(ub + L.flag);
   uint64_t* wbuf = (uint64_t*)(smem + L.wbuf) + (size_t)wave * 64;
+  // the merge waves' staircase (it depends only on kappa and the list length): enumerated
+  // now, while the workgroup waits for k and q
+  int pr[EM], bdiv = 0;
+#pragma unroll
+  for (int e = 0; e < EM; ++e) pr[e] = -1;
+  const bool merger = live && lwave < 2;
 
   // 1. scores of (k half 0, k half 1, q half 0, q half 1) of every sequence against the sub-keys
   if (BF16 && (s % 32 == 0) && (hh % 16 == 0) && hh <= 16 * kMaxK16) {
@@ -196,6 +202,7 @@ __global__ void __launch_bounds__(kGroup * UPW) decode_kernel(DecArgs A) {
     };
     uint4 bufA[kMaxK16], bufB[kMaxK16];
     if (wave < items) item_load(wave, bufA);
+    if (merger) stair_pairs<EM>(kappa, lwave == 0 ? W : R, pr, &bdiv);
     if (xl) *(uint4*)(xs + (xg * 2 + xvec) * d_k + xpc * 8) = xv;
     lds_barrier();  // k and q in LDS; the first item's loads stay in flight
     for (int it = wave; it < items; it += 2 * NW) {
@@ -207,6 +214,7 @@ __global__ void __launch_bounds__(kGroup * UPW) decode_kernel(DecArgs A) {
       }
     }
   } else {
+    if (merger) stair_pairs<EM>(kappa, lwave == 0 ? W : R, pr, &bdiv);
     if (live) {
       for (int p = ltid; p < 4 * s; p += kGroup) {
         const int c = p / s, m = p % s, half = c & 1;
@@ -231,13 +239,11 @@ __global__ void __launch_bounds__(kGroup * UPW) decode_kernel(DecArgs A) {
     select_half<ES>(sc + lwave * (s + 1), 0, s, kappa, wbuf, sel_i + lwave * kappa, sel_s + lwave * kappa);
   lds_barrier();
   // 3. kappa x kappa merge and softmax: the group's wave 0 for the key (W), wave 1 for the query (R)
-  if (live && lwave < 2) {
+  if (merger) {
     const int n_sel = lwave == 0 ? W : R;
     const int base = lwave * 2;
-    int pr[EM];
-    stair_pairs<EM>(kappa, n_sel, pr);
     const uint64_t key = merge_token<EM>(sel_i + base * kappa, sel_s + base * kappa, sel_i + (base + 1) * kappa,
-                                         sel_s + (base + 1) * kappa, s, kappa, n_sel, pr, wbuf);
+                                         sel_s + (base + 1) * kappa, s, kappa, n_sel, pr, bdiv, wbuf);
     const float scv = lane < n_sel ? key_score(key) : -INFINITY;
     const float mx = __shfl(scv, 0, kWave);
     const float e = lane < n_sel ? expf(scv - mx) : 0.f;

@@ -33,19 +33,19 @@ __device__ void select_half(const float* row, int swz, int s, int kappa, uint64_
 // ---------------------------------------------------------------- merge
 // Rank pairs (a, b) of the staircase {(a, b): (a+1)(b+1) <= n_sel, a, b < kappa}, enumerated
 // row by row: this lane's pairs p = lane + 64 e, packed a << 8 | b, or -1 past the end.
-// Depends only on (kappa, n_sel): computed once per wave, outside the token loop.
+// *bdiv receives n_sel / (lane + 1) (the first rank b past row `lane`), which merge_token
+// takes. Depends only on (kappa, n_sel): computed once per wave, outside the token loop.
 template <int EM>
-__device__ __forceinline__ void stair_pairs(int kappa, int n_sel, int (&pr)[EM]) {
+__device__ __forceinline__ void stair_pairs(int kappa, int n_sel, int (&pr)[EM], int* bdiv) {
   const int lane = lane_id();
 #pragma unroll
   for (int e = 0; e < EM; ++e) pr[e] = -1;
   // row a's length min(kappa, n_sel / (a + 1)) is computed on lane a (one division for the
   // whole wave) and read back row by row
+  const int q = n_sel / (lane + 1);
+  *bdiv = q;
   int rowlen = 0;
-  if (lane < kappa) {
-    rowlen = n_sel / (lane + 1);
-    if (rowlen > kappa) rowlen = kappa;
-  }
+  if (lane < kappa) rowlen = q < kappa ? q : kappa;
   int base = 0;
   for (int a = 0; a < kappa; ++a) {
     const int cnt = __builtin_amdgcn_readlane(rowlen, a);
@@ -69,7 +69,7 @@ __device__ __forceinline__ uint64_t cand_key(const int16_t* i1, const float* s1,
 // Top n_sel of the kappa x kappa candidates for one token: lanes < n_sel get their key.
 template <int EM>
 __device__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2, int s,
-                                int kappa, int n_sel, const int (&pr)[EM], uint64_t* wbuf) {
+                                int kappa, int n_sel, const int (&pr)[EM], int bdiv, uint64_t* wbuf) {
   const int lane = lane_id();
   // 1. exact top n_sel of the staircase pairs (every pair outside it is dominated by at
   //    least n_sel pairs inside it up to float32 rounding ties, which step 2 catches)
@@ -87,10 +87,7 @@ __device__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_
   //    tie would need an equal score); otherwise fall back to the exact extraction.
   const float tau_score = key_score(tau);
   bool viol = false;
-  if (lane < kappa) {
-    const int b = n_sel / (lane + 1);
-    if (b < kappa && s1[lane] + s2[b] >= tau_score) viol = true;
-  }
+  if (lane < kappa && bdiv < kappa && s1[lane] + s2[bdiv] >= tau_score) viol = true;
   const int all = kappa * kappa;
   if (ballot(viol) == 0ull) return top;
   // 3. exact extraction over all kappa^2 pairs, largest first

@@ -469,12 +469,20 @@ def bench_decode(args, sh):
     bank = SI.make_decode_bank(sh, 3 * n + args.warmup)  # warmup, eager steps, graph warm-up, timed graph
     P = max(1, min(16, len(os.sched_getaffinity(0))))
     cpu = None
-    # before the GPU is touched: prefill tokens and the oracle baseline in forked workers
     _oracle_decode.params, _oracle_decode.bank = params, bank
-    with mp.get_context("fork").Pool(P) as pool:
-        log(f"[bench] decode: prefill tokens of {sh.B} sequences in {P} workers")
-        pre = dict(pool.map(_prefill_tokens, [(sh.name, b) for b in range(sh.B)]))
-        if not args.no_cpu_baseline:
+    if args.no_cpu_baseline:
+        # no worker processes: a run under a profiler whose preloaded library has already
+        # initialised the GPU must not fork
+        pre = {}
+        for b in range(sh.B):
+            pre[b] = _prefill_tokens((sh.name, b))[1]
+            if b % 16 == 15:
+                log(f"[bench] decode: prefill tokens of {b + 1}/{sh.B} sequences")
+    else:
+        # before the GPU is touched: prefill tokens and the oracle baseline in forked workers
+        with mp.get_context("fork").Pool(P) as pool:
+            log(f"[bench] decode: prefill tokens of {sh.B} sequences in {P} workers")
+            pre = dict(pool.map(_prefill_tokens, [(sh.name, b) for b in range(sh.B)]))
             dt = _oracle_decode((sh.name, 0, 0, 2)) / 2
             steps = int(max(2, min(n, 15.0 / max(dt, 1e-6))))
             units = [(b % sh.B, b % sh.H) for b in range(P)]

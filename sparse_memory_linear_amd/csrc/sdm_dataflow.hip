@@ -243,6 +243,9 @@ __device__ __forceinline__ void buf_store(u4 d, __amdgpu_buffer_rsrc_t rs, uint3
 __device__ __forceinline__ int lds_ld(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// A word every lane reads at the same address, as a wave-uniform value: the loops and
+// branches that depend on it stay scalar, and so does the token counter they advance.
+__device__ __forceinline__ int lds_ld_u(const int* p) { return __builtin_amdgcn_readfirstlane(lds_ld(p)); }
 __device__ __forceinline__ void lds_st(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -292,7 +295,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
 
   const int T = A.T, W = A.W, R = A.R, E = A.E, S = A.S, smask = A.S - 1, win = A.win, rmask = A.RS - 1;
   const int SM = A.SM, mmask = A.SM - 1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane / LPC, l = lane % LPC;
   // XCD-aware placement: all column blocks of a unit go to the same XCD (workgroups are
   // dealt to the 8 XCDs round-robin), so they share its L2 for rows and per-token inputs.
@@ -474,20 +477,20 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
           const int t0 = (gw + i * kGatherWaves) * GB;
           const int tl = t0 + GB < T ? t0 + GB : T;
           if (!ready(tl) && !aborted) {
-            m_seen = lds_ld(&ctrl[kMetaDone]);
-            wm_seen = lds_ld(&ctrl[kWm]);
-            s_seen = lds_ld(&ctrl[kStoreIssued]);
+            m_seen = lds_ld_u(&ctrl[kMetaDone]);
+            wm_seen = lds_ld_u(&ctrl[kWm]);
+            s_seen = lds_ld_u(&ctrl[kStoreIssued]);
             if (!ready(tl)) {
               // blocked: first write out every own step still in flight, oldest first
 #pragma unroll
               for (int j = 1; j < GD; ++j)
                 if (i - GD + j >= 0) complete(i - GD + j, data[(sidx + j) % GD]);
               while (true) {
-                m_seen = lds_ld(&ctrl[kMetaDone]);
-                wm_seen = lds_ld(&ctrl[kWm]);
-                s_seen = lds_ld(&ctrl[kStoreIssued]);
+                m_seen = lds_ld_u(&ctrl[kMetaDone]);
+                wm_seen = lds_ld_u(&ctrl[kWm]);
+                s_seen = lds_ld_u(&ctrl[kStoreIssued]);
                 if (ready(tl)) break;
-                if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+                if (--budget <= 0 || lds_ld_u(&ctrl[kAbort])) {
                   aborted = true;
                   break;
                 }
@@ -527,7 +530,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
           if (lane == 0) lds_st(&ctrl[kWm], t0);
           drained = true;
         }
-        if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+        if (--budget <= 0 || lds_ld_u(&ctrl[kAbort])) {
           give_up();
           return;
         }
@@ -621,8 +624,8 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     const int sl = t & smask, rl = t & rmask;
     {
       long long budget = kSpinBudget;
-      while (lds_ld(&g_tok[sl]) != t) {
-        if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+      while (lds_ld_u(&g_tok[sl]) != t) {
+        if (--budget <= 0 || lds_ld_u(&ctrl[kAbort])) {
           aborted = true;
           break;
         }
@@ -691,7 +694,7 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
           }
         }
         if (ballot(wait) == 0ull) break;
-        if (--budget <= 0 || lds_ld(&ctrl[kAbort])) {
+        if (--budget <= 0 || lds_ld_u(&ctrl[kAbort])) {
           aborted = true;
           break;
         }

@@ -126,6 +126,39 @@ __device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t key) {
   return key;
 }
 
+// Bitonic sort of one float per lane, descending (scores only: used for thresholds).
+__device__ __forceinline__ float wave_sort_desc_f32(float s) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float other = shfl_xor_f32(s, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      s = ((s > other) == take_max) ? s : other;
+    }
+  }
+  return s;
+}
+// The same sort moving a 32-bit payload with each score. Equal scores are left in no
+// particular order, and two equal scores that meet may leave with the same payload: the
+// caller checks the sorted scores for equal neighbours before it trusts the payloads.
+__device__ __forceinline__ void wave_sort_desc_f32_payload(float& s, uint32_t& p) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float os = shfl_xor_f32(s, j);
+      const uint32_t op = shfl_xor_u32(p, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+      const bool keep = (s > os) == take_max;
+      s = keep ? s : os;
+      p = keep ? p : op;
+    }
+  }
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -142,47 +175,63 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// Exact top-`count` (count <= 64) of E keys per lane (E*64 candidates; key 0 = empty),
-// returned one per lane in rank order: lane i < count holds the i-th largest key, lanes
-// >= count hold 0. `buf` is 64 words of LDS private to the calling wave.
+// Exact top-`count` (count <= 64) of E (score, index) pairs per lane, ranked by score
+// descending, then index ascending; a score of -inf marks an absent entry, and at least
+// `count` lanes must hold a finite score. Lane i < count receives the pair of rank i.
+// `buf` is 64 words of LDS private to the calling wave.
 //
-// Fast path: the count-th largest lane maximum (score word only) is a lower bound of the
-// count-th largest key; if at most 64 keys reach it they are compacted and sorted.
-// Otherwise the keys are extracted one by one (exact, slower).
+// The count-th largest lane maximum tau bounds the answer from below: every pair of the
+// top `count` scores at least tau (otherwise `count` lane maxima would beat it), so the
+// pairs scoring >= tau hold the answer. When at most 64 do, they are compacted and sorted
+// on their float scores alone, each carrying its index; if two sorted neighbours up to
+// rank `count` score equal, their index order is not known and the candidates are sorted
+// again on exact 64-bit keys (score, complemented index). More than 64 candidates take the
+// exact extraction, one rank at a time. Only the candidates ever get a 64-bit key.
 template <int E>
-__device__ uint64_t wave_topk(const uint64_t (&keys)[E], int count, uint64_t* buf) {
+__device__ void wave_topk_f32(const float (&sc)[E], const uint32_t (&ix)[E], int count, uint64_t* buf,
+                              float* out_s, uint32_t* out_i) {
   const int lane = lane_id();
-  uint32_t lmax = (uint32_t)(keys[0] >> 32);  // score words only
+  float lmax = sc[0];
 #pragma unroll
-  for (int e = 1; e < E; ++e) lmax = max(lmax, (uint32_t)(keys[e] >> 32));
-  uint32_t sorted_hi = wave_sort_desc_u32(lmax);
-  uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)sorted_hi, count - 1);
+  for (int e = 1; e < E; ++e) lmax = fmaxf(lmax, sc[e]);
+  const float tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sort_desc_f32(lmax)), count - 1));
   uint64_t masks[E];
   int total = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    bool p = keys[e] != 0 && (uint32_t)(keys[e] >> 32) >= tau;
-    masks[e] = ballot(p);
+    masks[e] = ballot(sc[e] >= tau);
     total += popc64(masks[e]);
   }
-  if (total <= kWave) {
+  if (tau > -INFINITY && total <= kWave) {
     int base = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if ((masks[e] >> lane) & 1ull) buf[base + mbcnt(masks[e])] = keys[e];
+      if ((masks[e] >> lane) & 1ull)
+        buf[base + mbcnt(masks[e])] = ((uint64_t)ix[e] << 32) | (uint64_t)__float_as_uint(sc[e]);
       base += popc64(masks[e]);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    uint64_t mine = lane < total ? buf[lane] : 0ull;
+    const uint64_t mine = lane < total ? buf[lane] : (0xFFFFFFFFull << 32) | (uint64_t)__float_as_uint(-INFINITY);
     __builtin_amdgcn_wave_barrier();
-    uint64_t s = wave_sort_desc_u64(mine);
-    return lane < count ? s : 0ull;
+    float s = __uint_as_float((uint32_t)mine);
+    uint32_t p = (uint32_t)(mine >> 32);
+    wave_sort_desc_f32_payload(s, p);
+    const float next = __shfl_down(s, 1, kWave);
+    if (ballot(lane < count && lane < kWave - 1 && s == next) == 0ull) {
+      *out_s = s;
+      *out_i = p;
+      return;
+    }
+    const uint64_t key = wave_sort_desc_u64(lane < total ? rank_key(__uint_as_float((uint32_t)mine), (uint32_t)(mine >> 32)) : 0ull);
+    *out_s = key_score(key);
+    *out_i = key_index(key);
+    return;
   }
-  // exact slow path: repeated wave-wide maximum extraction
+  // exact slow path: repeated wave-wide maximum extraction on 64-bit keys
   uint64_t work[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) work[e] = keys[e];
+  for (int e = 0; e < E; ++e) work[e] = sc[e] > -INFINITY ? rank_key(sc[e], ix[e]) : 0ull;
   uint64_t out = 0;
   for (int i = 0; i < count; ++i) {
     uint64_t m = work[0];
@@ -194,7 +243,8 @@ __device__ uint64_t wave_topk(const uint64_t (&keys)[E], int count, uint64_t* bu
     for (int e = 0; e < E; ++e)
       if (work[e] == g) work[e] = 0;  // keys are unique (index in the low word)
   }
-  return out;
+  *out_s = key_score(out);
+  *out_i = key_index(out);
 }
 
 }  // namespace sdm

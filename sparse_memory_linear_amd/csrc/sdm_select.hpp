@@ -17,16 +17,22 @@ template <int E>
 __device__ void select_half(const float* row, int swz, int s, int kappa, uint64_t* wbuf, int16_t* out_idx,
                             float* out_sc) {
   const int lane = lane_id();
-  uint64_t keys[E];
+  // i ^ swz = (lane ^ swz) + 64 e for i = lane + 64 e, since swz < 32
+  const float* rp = row + (lane ^ swz);
+  float sc[E];
+  uint32_t ix[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    int i = lane + kWave * e;
-    keys[e] = i < s ? rank_key(row[i ^ swz], (uint32_t)i) : 0ull;
+    const int i = lane + kWave * e;
+    sc[e] = i < s ? rp[kWave * e] : -INFINITY;
+    ix[e] = (uint32_t)i;
   }
-  uint64_t k = wave_topk<E>(keys, kappa, wbuf);
+  float ts;
+  uint32_t ti;
+  wave_topk_f32<E>(sc, ix, kappa, wbuf, &ts, &ti);
   if (lane < kappa) {
-    out_idx[lane] = (int16_t)key_index(k);
-    out_sc[lane] = key_score(k);
+    out_idx[lane] = (int16_t)ti;
+    out_sc[lane] = ts;
   }
 }
 
@@ -73,19 +79,23 @@ __device__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_
   const int lane = lane_id();
   // 1. exact top n_sel of the staircase pairs (every pair outside it is dominated by at
   //    least n_sel pairs inside it up to float32 rounding ties, which step 2 catches)
-  uint64_t keys[EM];
+  float sc[EM];
+  uint32_t ix[EM];
 #pragma unroll
-  for (int e = 0; e < EM; ++e)
-    keys[e] = pr[e] >= 0 ? cand_key(i1, s1, i2, s2, pr[e] >> 8, pr[e] & 255, s) : 0ull;
-  uint64_t top = wave_topk<EM>(keys, n_sel, wbuf);
-  const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, n_sel - 1);
-  const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), n_sel - 1);
-  const uint64_t tau = ((uint64_t)thi << 32) | tlo;
+  for (int e = 0; e < EM; ++e) {
+    const int a = pr[e] >> 8, b = pr[e] & 255;
+    sc[e] = pr[e] >= 0 ? s1[a] + s2[b] : -INFINITY;
+    ix[e] = pr[e] >= 0 ? (uint32_t)i1[a] * (uint32_t)s + (uint32_t)i2[b] : 0xFFFFFFFFu;
+  }
+  float ts;
+  uint32_t ti;
+  wave_topk_f32<EM>(sc, ix, n_sel, wbuf, &ts, &ti);
+  const uint64_t top = lane < n_sel ? rank_key(ts, ti) : 0ull;
   // 2. a pair (a, b) outside the staircase has b >= n_sel/(a+1), so its score is at most that
   //    of the boundary pair (a, n_sel/(a+1)) of its row. If no boundary pair reaches the
   //    n_sel-th score, nothing outside the staircase can rank above it (a float32 rounding
   //    tie would need an equal score); otherwise fall back to the exact extraction.
-  const float tau_score = key_score(tau);
+  const float tau_score = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ts), n_sel - 1));
   bool viol = false;
   if (lane < kappa && bdiv < kappa && s1[lane] + s2[bdiv] >= tau_score) viol = true;
   const int all = kappa * kappa;

@@ -45,7 +45,8 @@ namespace sdm {
 
 namespace {
 
-constexpr int kDepBlk = 64;        // tokens per deps workgroup
+constexpr int kDepBlk = 128;       // tokens per deps workgroup (window offsets of entries stay below 256)
+constexpr int kDepThreads = 512;
 constexpr int kMaxHashBits = 15;   // deps hash table: at most 32768 entries, at most half full
 constexpr int kDepFilterWords = 2048;  // 64K-bit filter of the slots in the deps hash table
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
@@ -84,7 +85,7 @@ __device__ __forceinline__ uint32_t dep_hash(uint32_t slot, int bits) { return (
 __device__ __forceinline__ uint32_t dep_filter_bit(uint32_t slot) { return (slot * 0x9E3779B1u) >> 16; }  // 16 bits
 
 // hash entry = slot << 14 | window offset << 6 | writer position
-__global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
+__global__ void __launch_bounds__(kDepThreads) deps_kernel(DepArgs A) {
   extern __shared__ uint32_t table[];  // 2^bits entries, then the filter
   uint32_t* filt = table + (1 << A.bits);  // kDepFilterWords: a slot whose bit is clear is not in the table
   const int bits = A.bits;
@@ -94,24 +95,24 @@ __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
   const int wlo = t0 - A.win > 0 ? t0 - A.win : 0;
   const int whi = t0 + kDepBlk < A.T ? t0 + kDepBlk : A.T;
   const int W = A.W, R = A.R, per = W + R;
-  for (int i = threadIdx.x; i < (1 << bits); i += 256) table[i] = kEmpty;
-  for (int i = threadIdx.x; i < kDepFilterWords; i += 256) filt[i] = 0u;
+  for (int i = threadIdx.x; i < (1 << bits); i += kDepThreads) table[i] = kEmpty;
+  for (int i = threadIdx.x; i < kDepFilterWords; i += kDepThreads) filt[i] = 0u;
   __syncthreads();
   const int32_t* wi = A.widx + (size_t)u * A.T * W;
   const int32_t* ri = A.ridx + (size_t)u * A.T * R;
   // eight entries per thread at a time: their slot loads are in flight together
   constexpr int kB = 8;
   const int nins = (whi - wlo) * W;
-  for (int e0 = threadIdx.x; e0 < nins; e0 += 256 * kB) {
+  for (int e0 = threadIdx.x; e0 < nins; e0 += kDepThreads * kB) {
     int32_t sl[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int e = e0 + 256 * b, k = e / W, j = e - k * W;
+      const int e = e0 + kDepThreads * b, k = e / W, j = e - k * W;
       sl[b] = e < nins ? wi[(size_t)(wlo + k) * W + j] : -1;
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int e = e0 + 256 * b, k = e / W, j = e - k * W;
+      const int e = e0 + kDepThreads * b, k = e / W, j = e - k * W;
       const int32_t slot = sl[b];
       if (slot < 0 || slot >= A.N) continue;
       const uint32_t ent = ((uint32_t)slot << 14) | ((uint32_t)k << 6) | (uint32_t)j;
@@ -124,16 +125,16 @@ __global__ void __launch_bounds__(256) deps_kernel(DepArgs A) {
   __syncthreads();
   uint32_t* out = A.pk + ((size_t)u * A.T + t0) * per;
   const int nlook = (whi - t0) * per;
-  for (int e0 = threadIdx.x; e0 < nlook; e0 += 256 * kB) {
+  for (int e0 = threadIdx.x; e0 < nlook; e0 += kDepThreads * kB) {
     int32_t sl[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int e = e0 + 256 * b, kk = e / per, p = e - kk * per, t = t0 + kk;
+      const int e = e0 + kDepThreads * b, kk = e / per, p = e - kk * per, t = t0 + kk;
       sl[b] = e < nlook ? (p >= W ? ri[(size_t)t * R + (p - W)] : wi[(size_t)t * W + p]) : -1;
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int e = e0 + 256 * b;
+      const int e = e0 + kDepThreads * b;
       if (e >= nlook) continue;
       const int kk = e / per, p = e - kk * per;
       const int t = t0 + kk, kt = t - wlo;
@@ -995,7 +996,7 @@ hipError_t launch_dataflow(const sdm_shape& S, const int32_t* widx, const float*
   // at most half full: writers of one block and its window
   D.bits = 10;
   while (D.bits < kMaxHashBits && (1 << D.bits) < 2 * (kDepBlk + c.win) * S.W) ++D.bits;
-  hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(256), ((size_t)4 << D.bits) + kDepFilterWords * 4, stream, D);
+  hipLaunchKernelGGL(deps_kernel, dim3((S.T + kDepBlk - 1) / kDepBlk, U), dim3(kDepThreads), ((size_t)4 << D.bits) + kDepFilterWords * 4, stream, D);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float* fac = nullptr;

@@ -121,7 +121,9 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   float* sc = (float*)smem;                                     // [32][s+1]
   float* sel_s = sc + kTok * stride;                             // [32][2][kappa]
   int16_t* sel_i = (int16_t*)(sel_s + kTok * 2 * kappa);          // [32][2][kappa]
-  uint64_t* wbuf_all = (uint64_t*)(((uintptr_t)(sel_i + kTok * 2 * kappa) + 15) & ~(uintptr_t)15);
+  // an offset from smem (not an integer-cast address), so that the compiler keeps LDS accesses
+  const size_t wofs = ((size_t)((unsigned char*)(sel_i + kTok * 2 * kappa) - smem) + 15) & ~(size_t)15;
+  uint64_t* wbuf_all = (uint64_t*)(smem + wofs);
   const int head = blockIdx.y;
   const int r0 = blockIdx.x * kTok;
   const int BT = A.B * A.T;

@@ -188,7 +188,7 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
 // again on exact 64-bit keys (score, complemented index). More than 64 candidates take the
 // exact extraction, one rank at a time. Only the candidates ever get a 64-bit key.
 template <int E>
-__device__ void wave_topk_f32(const float (&sc)[E], const uint32_t (&ix)[E], int count, uint64_t* buf,
+__device__ __forceinline__ void wave_topk_f32(const float (&sc)[E], const uint32_t (&ix)[E], int count, uint64_t* buf,
                               float* out_s, uint32_t* out_i) {
   const int lane = lane_id();
   float lmax = sc[0];
@@ -206,8 +206,7 @@ __device__ void wave_topk_f32(const float (&sc)[E], const uint32_t (&ix)[E], int
     int base = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if ((masks[e] >> lane) & 1ull)
-        buf[base + mbcnt(masks[e])] = ((uint64_t)ix[e] << 32) | (uint64_t)__float_as_uint(sc[e]);
+      if (sc[e] >= tau) buf[base + mbcnt(masks[e])] = ((uint64_t)ix[e] << 32) | (uint64_t)__float_as_uint(sc[e]);
       base += popc64(masks[e]);
     }
     __builtin_amdgcn_wave_barrier();

@@ -14,7 +14,7 @@ namespace sdm {
 // Top-kappa sub-keys of one token-half: lanes < kappa receive (index, score) in rank order.
 // Score i of the row sits at row[i ^ swz] (swz < 32 permutes within aligned groups of 32).
 template <int E>
-__device__ void select_half(const float* row, int swz, int s, int kappa, uint64_t* wbuf, int16_t* out_idx,
+__device__ __forceinline__ void select_half(const float* row, int swz, int s, int kappa, uint64_t* wbuf, int16_t* out_idx,
                             float* out_sc) {
   const int lane = lane_id();
   // i ^ swz = (lane ^ swz) + 64 e for i = lane + 64 e, since swz < 32
@@ -74,7 +74,7 @@ __device__ __forceinline__ uint64_t cand_key(const int16_t* i1, const float* s1,
 
 // Top n_sel of the kappa x kappa candidates for one token: lanes < n_sel get their key.
 template <int EM>
-__device__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2, int s,
+__device__ __forceinline__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2, int s,
                                 int kappa, int n_sel, const int (&pr)[EM], int bdiv, uint64_t* wbuf) {
   const int lane = lane_id();
   // 1. exact top n_sel of the staircase pairs (every pair outside it is dominated by at

@@ -186,11 +186,28 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
 // on their float scores alone, each carrying its index; if two sorted neighbours up to
 // rank `count` score equal, their index order is not known and the candidates are sorted
 // again on exact 64-bit keys (score, complemented index). More than 64 candidates take the
-// exact extraction, one rank at a time. Only the candidates ever get a 64-bit key.
+// exact extraction, one rank at a time. Only the candidates ever get a 64-bit key. With one
+// entry per lane the lanes are sorted directly, with the same tie check.
 template <int E>
 __device__ __forceinline__ void wave_topk_f32(const float (&sc)[E], const uint32_t (&ix)[E], int count, uint64_t* buf,
                               float* out_s, uint32_t* out_i) {
   const int lane = lane_id();
+  if constexpr (E == 1) {
+    // one entry per lane: no threshold and no compaction, the lanes themselves are sorted
+    float s = sc[0];
+    uint32_t p = ix[0];
+    wave_sort_desc_f32_payload(s, p);
+    const float next = __shfl_down(s, 1, kWave);
+    if (ballot(lane < count && lane < kWave - 1 && s == next) == 0ull) {
+      *out_s = s;
+      *out_i = p;
+      return;
+    }
+    const uint64_t key = wave_sort_desc_u64(sc[0] > -INFINITY ? rank_key(sc[0], ix[0]) : 0ull);
+    *out_s = key_score(key);
+    *out_i = key_index(key);
+    return;
+  }
   float lmax = sc[0];
 #pragma unroll
   for (int e = 1; e < E; ++e) lmax = fmaxf(lmax, sc[e]);

@@ -51,14 +51,16 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
 
 // ---------------------------------------------------------------- scoring
 // Scores of half `half` for the 32 tokens rows r0..r0+31 of head `head` into sc[32][s+1].
-template <bool BF16>
+// NK: K steps of 16 the fragment arrays hold (h <= 16 NK); a kernel built for half widths up
+// to 64 keeps 32 fewer registers live through the scoring.
+template <bool BF16, int NK>
 __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float* sc) {
   const int s = A.s, h = A.h, d_k = 2 * h;
   const int BT = A.B * A.T;
   const int stride = score_stride(s);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const bool use_mfma = BF16 && (s % 32 == 0) && (h % 16 == 0) && h <= 16 * kMaxK16;
+  const bool use_mfma = BF16 && (s % 32 == 0) && (h % 16 == 0) && h <= 16 * NK;
   if (use_mfma) {
     // v_mfma_f32_32x32x16_bf16: lane l carries k = 8 (l / 32) .. +7 of row (or column) l % 32
     // of both operands; bf16 products are exact and summed in float32
@@ -71,19 +73,19 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
     const int kq = (lane >> 5) * 8;
     const int nk = h / 16;
     // this lane's token fragments for every k step, loaded once for all sub-key tiles
-    uint4 xf[kMaxK16];
+    uint4 xf[NK];
 #pragma unroll
-    for (int k = 0; k < kMaxK16; ++k)
+    for (int k = 0; k < NK; ++k)
       if (k < nk) xf[k] = *(const uint4*)(xrow + 16 * k + kq);
     for (int st = wave; st < s / 32; st += kWaves) {
       const uint16_t* crow = C + (size_t)(st * 32 + (lane & 31)) * h;
-      uint4 cf[kMaxK16];
+      uint4 cf[NK];
 #pragma unroll
-      for (int k = 0; k < kMaxK16; ++k)
+      for (int k = 0; k < NK; ++k)
         if (k < nk) cf[k] = *(const uint4*)(crow + 16 * k + kq);
       float16_t acc = {};
 #pragma unroll
-      for (int k = 0; k < kMaxK16; ++k)
+      for (int k = 0; k < NK; ++k)
         if (k < nk)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cf[k]),
                                                         __builtin_bit_cast(bf16x8_t, xf[k]), acc, 0, 0, 0);
@@ -113,7 +115,7 @@ __device__ void score_half(const AddrArgs& A, int head, int r0, int half, float*
 }
 
 // ---------------------------------------------------------------- kernel
-template <bool BF16, int ES, int EM>
+template <bool BF16, int ES, int EM, int NK>
 __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int s = A.s, kappa = A.kappa;
@@ -133,7 +135,7 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   stair_pairs<EM>(kappa, A.n_sel, pr, &bdiv);
 
   for (int half = 0; half < 2; ++half) {
-    score_half<BF16>(A, head, r0, half, sc);
+    score_half<BF16, NK>(A, head, r0, half, sc);
     __syncthreads();
     for (int n = wave; n < kTok; n += kWaves) {
       if (r0 + n >= BT) continue;
@@ -173,24 +175,32 @@ int stair_count_of(int kappa, int n_sel) {
   return c;
 }
 
-template <bool BF16, int ES>
+template <bool BF16, int ES, int NK>
 hipError_t launch_em(const AddrArgs& A, size_t lds, hipStream_t st) {
   dim3 grid((A.B * A.T + kTok - 1) / kTok, A.H);
   int em = (A.stair_count + kWave - 1) / kWave;
-  if (em <= 1) hipLaunchKernelGGL((address_kernel<BF16, ES, 1>), grid, dim3(kThreads), lds, st, A);
-  else if (em <= 2) hipLaunchKernelGGL((address_kernel<BF16, ES, 2>), grid, dim3(kThreads), lds, st, A);
-  else if (em <= 4) hipLaunchKernelGGL((address_kernel<BF16, ES, 4>), grid, dim3(kThreads), lds, st, A);
-  else hipLaunchKernelGGL((address_kernel<BF16, ES, 8>), grid, dim3(kThreads), lds, st, A);
+  if (em <= 1) hipLaunchKernelGGL((address_kernel<BF16, ES, 1, NK>), grid, dim3(kThreads), lds, st, A);
+  else if (em <= 2) hipLaunchKernelGGL((address_kernel<BF16, ES, 2, NK>), grid, dim3(kThreads), lds, st, A);
+  else if (em <= 4) hipLaunchKernelGGL((address_kernel<BF16, ES, 4, NK>), grid, dim3(kThreads), lds, st, A);
+  else hipLaunchKernelGGL((address_kernel<BF16, ES, 8, NK>), grid, dim3(kThreads), lds, st, A);
   return hipGetLastError();
+}
+
+template <bool BF16, int ES>
+hipError_t launch_nk(const AddrArgs& A, size_t lds, hipStream_t st) {
+  if constexpr (BF16) {
+    if (A.h <= 64) return launch_em<BF16, ES, 4>(A, lds, st);
+  }
+  return launch_em<BF16, ES, kMaxK16>(A, lds, st);
 }
 
 template <bool BF16>
 hipError_t launch_es(const AddrArgs& A, size_t lds, hipStream_t st) {
   int es = (A.s + kWave - 1) / kWave;
-  if (es <= 1) return launch_em<BF16, 1>(A, lds, st);
-  if (es <= 2) return launch_em<BF16, 2>(A, lds, st);
-  if (es <= 4) return launch_em<BF16, 4>(A, lds, st);
-  return launch_em<BF16, 8>(A, lds, st);
+  if (es <= 1) return launch_nk<BF16, 1>(A, lds, st);
+  if (es <= 2) return launch_nk<BF16, 2>(A, lds, st);
+  if (es <= 4) return launch_nk<BF16, 4>(A, lds, st);
+  return launch_nk<BF16, 8>(A, lds, st);
 }
 
 }  // namespace

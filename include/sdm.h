@@ -107,6 +107,21 @@ sdm_status sdm_init_from_M0(const sdm_shape* shape, const void* M0, void* M, voi
 sdm_status sdm_address(const sdm_shape* shape, const void* x, const void* subkeys, int32_t n_sel,
                        int32_t* idx, float* weight, float* score, void* stream);
 
+/* sdm_address that also carries out slice `part` of `nparts` of sdm_init_from_M0 in the
+ * same kernel launch (PL §3 "Learned initial state"; the addressing is bound by its vector
+ * ALU and leaves the memory pipe idle, so the copy rides on it). The initialisation is split
+ * into nparts equal ranges of the 16-byte chunks of one head-major copy of M0; once calls
+ * with part = 0 .. nparts-1 have all completed, M[b,h] = M0[h] bit for bit for every b,
+ * exactly as after sdm_init_from_M0. idx, weight and score are those of sdm_address bit for
+ * bit. With B*T = 0 only the copy slice runs.
+ *   M0 [H, N, d_v] mem_dtype (read); M [B, H, N, d_v] mem_dtype (written, this slice only)
+ *   1 <= nparts <= 64 and 0 <= part < nparts, else SDM_ERR_INVALID_ARG. M must be 16-byte
+ *   aligned and overlap none of M0, x, subkeys, idx, weight, score (SDM_ERR_INVALID_ARG);
+ *   every other argument and error as for sdm_address. */
+sdm_status sdm_address_init(const sdm_shape* shape, const void* x, const void* subkeys, int32_t n_sel,
+                            int32_t* idx, float* weight, float* score, const void* M0, void* M,
+                            int32_t part, int32_t nparts, void* stream);
+
 /* The sparse gated-delta recurrence with caller-supplied slots and weights (PL §2 "Gated
  * DeltaNet", PL §3 "Sparse memory updates" / "Sparse retrieval"). For each unit, tokens
  * t = 0..T-1 in order:

@@ -64,6 +64,8 @@ _SIGS = {
     "sdm_workspace_bytes": (ctypes.c_size_t, [_SP]),
     "sdm_init_from_M0": (ctypes.c_int, [_SP, _P, _P, _P]),
     "sdm_address": (ctypes.c_int, [_SP, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "sdm_address_init": (ctypes.c_int, [_SP, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                        ctypes.c_int32, _P]),
     "sdm_recurrent": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sdm_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "sdm_forward_static": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -163,6 +165,13 @@ def init_from_M0(shape: Shape, M0, M, stream=None):
 def address(shape: Shape, x, subkeys, n_sel: int, idx, weight, score=None, stream=None):
     _check(lib().sdm_address(ctypes.byref(shape), _ptr(x), _ptr(subkeys), int(n_sel), _ptr(idx), _ptr(weight),
                              _ptr(score), _stream(stream)), "sdm_address")
+
+
+def address_init(shape: Shape, x, subkeys, n_sel: int, idx, weight, M0, M, part: int, nparts: int, score=None,
+                 stream=None):
+    _check(lib().sdm_address_init(ctypes.byref(shape), _ptr(x), _ptr(subkeys), int(n_sel), _ptr(idx),
+                                  _ptr(weight), _ptr(score), _ptr(M0), _ptr(M), int(part), int(nparts),
+                                  _stream(stream)), "sdm_address_init")
 
 
 def recurrent(shape: Shape, widx, wgt, ridx, rgt, v, alpha, beta, M, o, ws, stream=None):

@@ -26,6 +26,7 @@ constexpr int kMaxK16 = 8;    // MFMA scoring for half widths up to 128 (8 steps
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct AddrArgs {
   const void* x;        // [B,H,T,d_k] in dtype
@@ -35,7 +36,38 @@ struct AddrArgs {
   float* score;         // [B,H,T,n_sel] or null
   int B, H, T, s, h, kappa, n_sel;
   int stair_count;      // number of (a, b) rank pairs with (a+1)(b+1) <= n_sel, a,b < kappa
+  // optional slice [c0, c1) of the table initialisation M[b] = M0 (16-byte chunks of one
+  // head-major copy of M0, written to each of the cB copies in M); null cM0 = none
+  const u32x4* cM0;
+  u32x4* cM;
+  size_t chunks, c0, c1;
+  int cB;
 };
+
+// The table initialisation rides on the addressing kernel, whose vector ALU is the bound while
+// its memory pipe idles: each workgroup copies a share of the slice when it starts,
+// kCopyUnroll chunks per thread in flight. (Holding the loaded chunks in registers across
+// the first scoring pass, to hide their latency behind it, made the kernel spill.)
+constexpr int kCopyUnroll = 8;
+__device__ __forceinline__ void copy_share(const AddrArgs& A) {
+  const size_t G = (size_t)gridDim.x * gridDim.y;
+  const size_t g = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const size_t step = G * kThreads * kCopyUnroll;
+  for (size_t base = A.c0 + g * kThreads * kCopyUnroll + threadIdx.x; base < A.c1; base += step) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      if (i < A.c1) v[u] = __builtin_nontemporal_load(&A.cM0[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      if (i < A.c1)
+        for (int b = 0; b < A.cB; ++b) __builtin_nontemporal_store(v[u], &A.cM[(size_t)b * A.chunks + i]);
+    }
+  }
+}
 
 // Score tile [32 tokens][s]. The MFMA layout writes one token per lane; to keep those writes
 // in different LDS banks, score m of token n sits at n * s + (m ^ n) when s is a multiple of
@@ -130,6 +162,7 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   const int r0 = blockIdx.x * kTok;
   const int BT = A.B * A.T;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (A.cM0) copy_share(A);
   uint64_t* wbuf = wbuf_all + wave * kWave;
   int pr[EM], bdiv;
   stair_pairs<EM>(kappa, A.n_sel, pr, &bdiv);
@@ -212,8 +245,23 @@ size_t address_lds_bytes(int s, int kappa) {
 }
 
 hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys, int n_sel, int32_t* idx,
-                          float* weight, float* score, hipStream_t stream) {
+                          float* weight, float* score, hipStream_t stream, const InitPart* init) {
   AddrArgs A;
+  A.cM0 = nullptr;
+  A.cM = nullptr;
+  A.chunks = A.c0 = A.c1 = 0;
+  A.cB = 0;
+  if (init) {
+    // slice `part` of `nparts` of the 16-byte chunks of one head-major copy of M0
+    A.chunks = (size_t)S.H * (size_t)S.N * (size_t)S.d_v * dtype_size(S.mem_dtype) / 16;
+    A.c0 = A.chunks * (size_t)init->part / (size_t)init->nparts;
+    A.c1 = A.chunks * ((size_t)init->part + 1) / (size_t)init->nparts;
+    A.cB = S.B;
+    if (A.c1 > A.c0 && S.B > 0) {
+      A.cM0 = (const u32x4*)init->M0;
+      A.cM = (u32x4*)init->M;
+    }
+  }
   A.x = x;
   A.subkeys = subkeys;
   A.idx = idx;
@@ -227,7 +275,7 @@ hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys
   A.kappa = S.kappa;
   A.n_sel = n_sel;
   A.stair_count = stair_count_of(S.kappa, n_sel);
-  if (S.B * S.T == 0) return hipSuccess;
+  if (S.B * S.T == 0) return A.cM0 ? launch_init_part(S, init->M0, init->M, A.c0, A.c1, stream) : hipSuccess;
   size_t lds = address_lds_bytes(A.s, A.kappa);
   if (S.in_dtype == SDM_BF16) return launch_es<true>(A, lds, stream);
   return launch_es<false>(A, lds, stream);

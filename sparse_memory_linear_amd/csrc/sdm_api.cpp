@@ -323,8 +323,9 @@ sdm_status sdm_init_from_M0(const sdm_shape* S, const void* M0, void* M, void* s
   return hip_status(launch_init(*S, M0, M, (hipStream_t)stream));
 }
 
-sdm_status sdm_address(const sdm_shape* S, const void* x, const void* subkeys, int32_t n_sel, int32_t* idx,
-                       float* weight, float* score, void* stream) {
+namespace {
+sdm_status address_checks(const sdm_shape* S, const void* x, const void* subkeys, int32_t n_sel, int32_t* idx,
+                          float* weight, float* score) {
   sdm_status st = check_shape(S, true);
   if (st != SDM_OK) return st;
   if (n_sel < 1 || (int64_t)n_sel > (int64_t)S->kappa * S->kappa) return SDM_ERR_INVALID_ARG;
@@ -337,8 +338,35 @@ sdm_status sdm_address(const sdm_shape* S, const void* x, const void* subkeys, i
   if (overlaps(idx, ob, weight, ob) || (score && (overlaps(score, ob, idx, ob) || overlaps(score, ob, weight, ob))) ||
       overlaps(idx, ob, x, xb) || overlaps(weight, ob, x, xb))
     return SDM_ERR_INVALID_ARG;
+  return SDM_OK;
+}
+}  // namespace
+
+sdm_status sdm_address(const sdm_shape* S, const void* x, const void* subkeys, int32_t n_sel, int32_t* idx,
+                       float* weight, float* score, void* stream) {
+  sdm_status st = address_checks(S, x, subkeys, n_sel, idx, weight, score);
+  if (st != SDM_OK) return st;
   if (S->T == 0) return SDM_OK;
   return hip_status(launch_address(*S, x, subkeys, n_sel, idx, weight, score, (hipStream_t)stream));
+}
+
+sdm_status sdm_address_init(const sdm_shape* S, const void* x, const void* subkeys, int32_t n_sel, int32_t* idx,
+                            float* weight, float* score, const void* M0, void* M, int32_t part, int32_t nparts,
+                            void* stream) {
+  sdm_status st = address_checks(S, x, subkeys, n_sel, idx, weight, score);
+  if (st != SDM_OK) return st;
+  if (nparts < 1 || nparts > 64 || part < 0 || part >= nparts) return SDM_ERR_INVALID_ARG;
+  if (!M0 || !M || !aligned16(M0) || !aligned16(M)) return SDM_ERR_INVALID_ARG;
+  const size_t head_bytes = (size_t)S->H * (size_t)S->N * S->d_v * dtype_size(S->mem_dtype);
+  const size_t mb = head_bytes * S->B;
+  const size_t ob = tensor_bytes(*S, n_sel, 4);
+  const size_t xb = tensor_bytes(*S, S->d_k, dtype_size(S->in_dtype));
+  const size_t cb = (size_t)S->H * 2 * (size_t)isqrt64(S->N) * (S->d_k / 2) * dtype_size(S->in_dtype);
+  if (overlaps(M0, head_bytes, M, mb) || overlaps(M, mb, x, xb) || overlaps(M, mb, subkeys, cb) ||
+      overlaps(M, mb, idx, ob) || overlaps(M, mb, weight, ob) || (score && overlaps(M, mb, score, ob)))
+    return SDM_ERR_INVALID_ARG;
+  const InitPart ip{M0, M, part, nparts};
+  return hip_status(launch_address(*S, x, subkeys, n_sel, idx, weight, score, (hipStream_t)stream, &ip));
 }
 
 sdm_status sdm_recurrent(const sdm_shape* S, const int32_t* widx, const float* wgt, const int32_t* ridx,

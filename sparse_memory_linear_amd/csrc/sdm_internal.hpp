@@ -40,9 +40,18 @@ struct DecayState {
 
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t stream);
 size_t address_lds_bytes(int s, int kappa);
+// Slice `part` of `nparts` of the table initialisation M[b, h] = M0[h] (16-byte chunks of one
+// head-major copy of M0, split into nparts equal ranges), carried out by an addressing call.
+struct InitPart {
+  const void* M0;
+  void* M;
+  int part, nparts;
+};
 hipError_t launch_address(const sdm_shape& S, const void* x, const void* subkeys, int n_sel, int32_t* idx,
-                          float* weight, float* score, hipStream_t stream);
+                          float* weight, float* score, hipStream_t stream, const InitPart* init = nullptr);
 hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t stream);
+// chunks [c0, c1) of the initialisation (of H*N*rowbytes/16 chunks per copy)
+hipError_t launch_init_part(const sdm_shape& S, const void* M0, void* M, size_t c0, size_t c1, hipStream_t stream);
 hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,
                             const float* rgt, const void* v, const float* alpha, const float* beta, void* M, float* o,
                             void* ws, const WsLayout& L, const DecayState* dk, hipStream_t stream,

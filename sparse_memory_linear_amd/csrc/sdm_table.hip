@@ -18,10 +18,11 @@ namespace {
 // Each thread moves 16-byte chunks: one read of M0[h], B writes (one per sequence).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// chunks = H * N * rowbytes / 16 (one head-major copy of M0); M holds B such copies.
+// chunks = H * N * rowbytes / 16 (one head-major copy of M0); M holds B such copies. The
+// kernel moves chunks [c0, c1).
 __global__ void __launch_bounds__(256) init_kernel(const u32x4* __restrict__ M0, u32x4* __restrict__ M, int B,
-                                                   size_t chunks) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (size_t)gridDim.x * blockDim.x) {
+                                                   size_t chunks, size_t c0, size_t c1) {
+  for (size_t i = c0 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < c1; i += (size_t)gridDim.x * blockDim.x) {
     u32x4 v = __builtin_nontemporal_load(&M0[i]);
     for (int b = 0; b < B; ++b) __builtin_nontemporal_store(v, &M[(size_t)b * chunks + i]);
   }
@@ -175,15 +176,20 @@ hipError_t launch_zero(void* p, size_t n_words, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t stream) {
+hipError_t launch_init_part(const sdm_shape& S, const void* M0, void* M, size_t c0, size_t c1, hipStream_t stream) {
   const size_t rowbytes = (size_t)S.d_v * dtype_size(S.mem_dtype);
   const size_t chunks = (size_t)S.H * (size_t)S.N * rowbytes / 16;
-  if (chunks == 0) return hipSuccess;
-  size_t blocks = (chunks + 255) / 256;
+  if (c1 > chunks) c1 = chunks;
+  if (c1 <= c0 || S.B == 0) return hipSuccess;
+  size_t blocks = (c1 - c0 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(init_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const u32x4*)M0, (u32x4*)M, S.B,
-                     chunks);
+                     chunks, c0, c1);
   return hipGetLastError();
+}
+
+hipError_t launch_init(const sdm_shape& S, const void* M0, void* M, hipStream_t stream) {
+  return launch_init_part(S, M0, M, 0, ~(size_t)0, stream);
 }
 
 hipError_t launch_recurrent(const sdm_shape& S, const int32_t* widx, const float* wgt, const int32_t* ridx,

@@ -102,6 +102,27 @@ def test_null_and_misaligned_pointers(sdm, no_gpu):
     assert L.sdm_recurrent(sp, *args, FAKE + 10 * (1 << 36), 1 << 30, None) == -1
 
 
+def test_address_init_validates(sdm, no_gpu):
+    L = sdm.lib()
+    S = base()
+    sp = ctypes.byref(S)
+    x, c, idx, w, M0, M = (FAKE + i * (1 << 36) for i in range(6))
+    # part and nparts out of range
+    for part, nparts in ((0, 0), (-1, 2), (2, 2), (0, 65)):
+        assert L.sdm_address_init(sp, x, c, 16, idx, w, None, M0, M, part, nparts, None) == -1
+    # null or misaligned tables
+    assert L.sdm_address_init(sp, x, c, 16, idx, w, None, None, M, 0, 1, None) == -1
+    assert L.sdm_address_init(sp, x, c, 16, idx, w, None, M0, M + 8, 0, 1, None) == -1
+    # M0 inside M, M over the slot outputs, the query or the sub-keys
+    assert L.sdm_address_init(sp, x, c, 16, idx, w, None, M + 4096, M, 0, 1, None) == -1
+    assert L.sdm_address_init(sp, x, c, 16, M + 4096, w, None, M0, M, 0, 1, None) == -1
+    assert L.sdm_address_init(sp, M + 1024, c, 16, idx, w, None, M0, M, 0, 1, None) == -1
+    assert L.sdm_address_init(sp, x, M + 2048, 16, idx, w, None, M0, M, 0, 1, None) == -1
+    # the addressing checks of sdm_address still apply
+    assert L.sdm_address_init(sp, x, c, 0, idx, w, None, M0, M, 0, 1, None) == -1
+    assert L.sdm_address_init(sp, x, c, 16, None, w, None, M0, M, 0, 1, None) == -1
+
+
 def test_workspace_too_small(sdm, no_gpu):
     L = sdm.lib()
     S = base()

@@ -114,6 +114,42 @@ def test_address_parity(sdm, name):
     log(f"[address] {name}: tie positions {total_ties}")
 
 
+# ----------------------------------------------------------------------------- addressing + init
+@pytest.mark.parametrize("name,nparts", [("tiny_fp32", 1), ("small_T256", 2), ("layer_1p4b_T100", 3),
+                                         ("layer_8b_T300", 2)])
+def test_address_init_equals_separate_calls(sdm, name, nparts):
+    """sdm_address_init: slot lists, weights and scores bit-identical to sdm_address, and once
+    every part has run the table is M0 in every sequence, bit for bit (M starts as a byte
+    pattern no copy of M0 holds)."""
+    import torch
+    sh = CASES[name]
+    log(f"[address_init] {name} nparts={nparts}")
+    inp = SI.make_inputs(sh)
+    dev = upload(inp, sh)
+    S = lib_shape(sh)
+    M = empty_mem((sh.B, sh.H, sh.N, sh.d_v), sh.mem_dtype)
+    M.view(torch.uint8).fill_(0xA5)
+    for part in range(nparts):
+        which, n_sel = (("k", sh.W), ("q", sh.R))[part % 2]
+        outs = []
+        for fused in (False, True):
+            idx = torch.empty((sh.B, sh.H, sh.T, n_sel), dtype=torch.int32, device="cuda")
+            wgt = torch.empty((sh.B, sh.H, sh.T, n_sel), dtype=torch.float32, device="cuda")
+            sc = torch.empty_like(wgt)
+            if fused:
+                sdm.address_init(S, dev[which], dev["subkeys"], n_sel, idx, wgt, dev["M0"], M, part, nparts, score=sc)
+            else:
+                sdm.address(S, dev[which], dev["subkeys"], n_sel, idx, wgt, sc)
+            outs.append((idx, wgt, sc))
+        torch.cuda.synchronize()
+        for a, b in zip(*outs):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name} part {part}: outputs differ"
+    torch.cuda.synchronize()
+    got = from_dev(M, sh.mem_dtype)
+    for b in range(sh.B):
+        assert np.array_equal(got[b], inp["M0"]), f"{name}: sequence {b} differs from M0 after {nparts} parts"
+
+
 # ----------------------------------------------------------------------------- recurrence
 @pytest.mark.parametrize("name", list(CASES))
 def test_recurrent_parity(sdm, name):

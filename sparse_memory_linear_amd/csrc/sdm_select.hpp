@@ -28,35 +28,59 @@ __device__ __forceinline__ uint64_t rank_key(float score, uint32_t index) {
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
 __device__ __forceinline__ float key_score(uint64_t k) { return from_ordered_u32((uint32_t)(k >> 32)); }
 
-// Bitonic sort of one key per lane across the wave, descending (lane 0 = largest). At each
-// step a lane keeps the larger of its key and its partner's when it is the lower lane of a
-// descending block or the upper lane of an ascending one, else the smaller: one compare,
-// folded with that lane pattern, and one select per word. Equal keys are interchangeable.
+// The value of lane (lane ^ m) for the partners a descending bitonic sort of the wave uses:
+// m = 2^i (the steps inside a stage) and m = 2^i - 1 (the mirror that opens stage 2^i), with
+// DPP, ds_swizzle and v_permlane32_swap. `m` must fold to a constant.
+__device__ __forceinline__ uint32_t xchg_u32(uint32_t v, int m) {
+  switch (m) {
+    case 3: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+    case 7: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    case 15: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row_mirror
+    case 31: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x7C1F);              // xor 31 in 32 lanes
+    case 63: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)shfl_xor_u32(v, 32), 0x7C1F);
+    default: return shfl_xor_u32(v, m);
+  }
+}
+__device__ __forceinline__ uint64_t xchg_u64(uint64_t v, int m) {
+  return ((uint64_t)xchg_u32((uint32_t)(v >> 32), m) << 32) | xchg_u32((uint32_t)v, m);
+}
+__device__ __forceinline__ float xchg_f32(float v, int m) { return __uint_as_float(xchg_u32(__float_as_uint(v), m)); }
+
+// Bitonic sort of one value per lane across the wave, descending (lane 0 = largest). Stage k
+// (k = 2, 4, ..., 64) opens by comparing each lane with its mirror in its block of k lanes
+// (lane ^ (k - 1)), which merges the two sorted halves of the block into two bitonic halves,
+// every value of the lower above every value of the upper; steps j = k/4 .. 1 (lane ^ j)
+// then sort those halves. Every block is sorted in the same direction, so at each step the
+// lower lane of a pair keeps the larger value: the lane pattern depends on one lane bit (six
+// patterns in all, where a direction that alternates between blocks needs 21). Equal values
+// are interchangeable. `step` performs one compare-exchange with partner lane ^ m, the lower
+// lane being the one whose bit `bit` is clear.
+template <typename Step>
+__device__ __forceinline__ void bitonic_desc(Step step) {
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+    step(k - 1, k >> 1);
+#pragma unroll
+    for (int j = k >> 2; j > 0; j >>= 1) step(j, j);
+  }
+}
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t key) {
   const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t other = shfl_xor_u64(key, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      key = ((key > other) == take_max) ? key : other;
-    }
-  }
+  bitonic_desc([&](int m, int bit) {
+    const uint64_t other = xchg_u64(key, m);
+    const bool lower = (lane & bit) == 0;
+    key = ((key > other) == lower) ? key : other;
+  });
   return key;
 }
-// Bitonic sort of one float per lane, descending (scores only: used for thresholds).
+// Scores only: used for thresholds.
 __device__ __forceinline__ float wave_sort_desc_f32(float s) {
   const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float other = shfl_xor_f32(s, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      s = ((s > other) == take_max) ? s : other;
-    }
-  }
+  bitonic_desc([&](int m, int bit) {
+    const float other = xchg_f32(s, m);
+    const bool lower = (lane & bit) == 0;
+    s = ((s > other) == lower) ? s : other;
+  });
   return s;
 }
 // The same sort moving a 32-bit payload with each score. Equal scores are left in no
@@ -64,18 +88,13 @@ __device__ __forceinline__ float wave_sort_desc_f32(float s) {
 // caller checks the sorted scores for equal neighbours before it trusts the payloads.
 __device__ __forceinline__ void wave_sort_desc_f32_payload(float& s, uint32_t& p) {
   const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float os = shfl_xor_f32(s, j);
-      const uint32_t op = shfl_xor_u32(p, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      const bool keep = (s > os) == take_max;
-      s = keep ? s : os;
-      p = keep ? p : op;
-    }
-  }
+  bitonic_desc([&](int m, int bit) {
+    const float os = xchg_f32(s, m);
+    const uint32_t op = xchg_u32(p, m);
+    const bool keep = (s > os) == ((lane & bit) == 0);
+    s = keep ? s : os;
+    p = keep ? p : op;
+  });
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {

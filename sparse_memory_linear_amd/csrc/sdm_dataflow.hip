@@ -344,6 +344,22 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
     const int nb = (T + tpb - 1) / tpb;
     const size_t vrow = (size_t)A.d_v * sizeof(InT) / 4;         // words per token of v
     const size_t vcol = (size_t)cb * CPR * sizeof(InT) / 4;      // first word of this block
+    // Each lane's sources for batch 0 and their per-batch strides (elements): the wave gates
+    // the whole pipeline, so a batch advances one pointer per array instead of recomputing
+    // 64-bit addresses. Lane q/4 carries words q..q+3 of the batch's packed words and weights
+    // (token q / E, position q % E); lane l carries word l % vw of token l / vw's v columns
+    // and gates.
+    const int q4 = lane * 4, ttq = q4 / E, eq = q4 - ttq * E;
+    const bool lq = q4 < tpb * E;
+    const int ttv = lane / vw, kv = lane - ttv * vw;
+    const bool lv = lane < tpb * vw;
+    const uint32_t* pk_src = A.pk + (ut0 + ttq) * E + eq;
+    const float* wt_src = eq < W ? A.wgt + (ut0 + ttq) * W + eq : A.rgt + (ut0 + ttq) * R + (eq - W);
+    const uint32_t* v_src = kv < vw2 ? (const uint32_t*)A.v + (ut0 + ttv) * vrow + vcol + kv
+                                     : (const uint32_t*)(kv == vw2 ? A.alpha : A.beta) + ut0 + ttv;
+    const float* fac_src = A.fac ? A.fac + (ut0 + ttq) * E + eq : nullptr;
+    const size_t pk_step = (size_t)E * tpb, wt_step = (size_t)(eq < W ? W : R) * tpb;
+    const size_t v_step = (kv < vw2 ? vrow : (size_t)1) * tpb;
     int published = 0, s_seen = 0;
     long long budget = kSpinBudget;
     for (int b = 0; b < nb; ++b) {
@@ -368,29 +384,19 @@ __global__ void __launch_bounds__(kWaves * 64) pipe_kernel(PipeArgs A) {
       }
       const int sl0 = tb & mmask;
       {
-        const int q = lane * 4, tt = q / E;
-        if (q < tpb * E && tb + tt < T)
-          __builtin_amdgcn_global_load_lds(A.pk + (ut0 + tb) * E + q, (void*)(pk_r + (size_t)sl0 * E), 16, 0, 0);
-      }
-      {
-        const int q = lane * 4, tt = q / E, e = q - tt * E;
-        const size_t t = ut0 + tb + tt;
-        const float* src = e < W ? A.wgt + t * W + e : A.rgt + t * R + (e - W);
-        if (q < tpb * E && tb + tt < T)
-          __builtin_amdgcn_global_load_lds(src, (void*)(wt_r + (size_t)sl0 * E), 16, 0, 0);
-      }
-      {
-        const int tt = lane / vw, k = lane - tt * vw;
-        const size_t t = ut0 + tb + tt;
-        const uint32_t* src = k < vw2 ? (const uint32_t*)A.v + t * vrow + vcol + k
-                                      : (const uint32_t*)(k == vw2 ? A.alpha : A.beta) + t;
-        if (lane < tpb * vw && tb + tt < T)
-          __builtin_amdgcn_global_load_lds(src, (void*)(vab_r + (size_t)sl0 * vw), 4, 0, 0);
-      }
-      if (A.fac) {
-        const int q = lane * 4, tt = q / E;
-        if (q < tpb * E && tb + tt < T)
-          __builtin_amdgcn_global_load_lds(A.fac + (ut0 + tb) * E + q, (void*)(fac_r + (size_t)sl0 * E), 16, 0, 0);
+        // every token of a full batch is valid; only the last batch checks them (a batch
+        // always issues its 3 or 4 loads: its first token is valid)
+        const bool full = tb + tpb <= T;
+        const bool okq = lq && (full || tb + ttq < T);
+        const bool okv = lv && (full || tb + ttv < T);
+        if (okq) __builtin_amdgcn_global_load_lds(pk_src, (void*)(pk_r + (size_t)sl0 * E), 16, 0, 0);
+        if (okq) __builtin_amdgcn_global_load_lds(wt_src, (void*)(wt_r + (size_t)sl0 * E), 16, 0, 0);
+        if (okv) __builtin_amdgcn_global_load_lds(v_src, (void*)(vab_r + (size_t)sl0 * vw), 4, 0, 0);
+        if (A.fac && okq) __builtin_amdgcn_global_load_lds(fac_src, (void*)(fac_r + (size_t)sl0 * E), 16, 0, 0);
+        pk_src += pk_step;
+        wt_src += wt_step;
+        v_src += v_step;
+        if (A.fac) fac_src += pk_step;
       }
       if (b >= kMetaDepth) {
         // exactly 3 (4 with decay factors) loads per batch: the batch kMetaDepth back is complete

@@ -167,24 +167,35 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
   int pr[EM], bdiv;
   stair_pairs<EM>(kappa, A.n_sel, pr, &bdiv);
 
+  // Two tokens per wave pass (their selections interleaved) where the score rows can hold the
+  // candidate buffers: a token's row is dead once its scores are in registers, and rows of
+  // at least 512 bytes at a stride of s floats keep them 8-byte aligned. Rows past the end
+  // of the tokens hold scores of a clamped row and are selected but not written out.
+  const bool pair = ES >= 2 && s % 32 == 0;
+  auto rowbuf = [&](int n) { return (uint64_t*)(sc + n * stride); };
   for (int half = 0; half < 2; ++half) {
     score_half<BF16, NK>(A, head, r0, half, sc);
     __syncthreads();
-    for (int n = wave; n < kTok; n += kWaves) {
-      if (r0 + n >= BT) continue;
-      select_half<ES>(sc + n * stride, score_swz(s, n), s, kappa, wbuf, sel_i + (n * 2 + half) * kappa,
-                      sel_s + (n * 2 + half) * kappa);
+    if (pair) {
+      for (int n = wave; n < kTok; n += 2 * kWaves) {
+        const int m = n + kWaves;
+        select_half_x2<ES>(sc + n * stride, score_swz(s, n), sc + m * stride, score_swz(s, m), s, kappa, rowbuf(n),
+                           rowbuf(m), sel_i + (n * 2 + half) * kappa, sel_s + (n * 2 + half) * kappa,
+                           sel_i + (m * 2 + half) * kappa, sel_s + (m * 2 + half) * kappa);
+      }
+    } else {
+      for (int n = wave; n < kTok; n += kWaves) {
+        if (r0 + n >= BT) continue;
+        select_half<ES>(sc + n * stride, score_swz(s, n), s, kappa, wbuf, sel_i + (n * 2 + half) * kappa,
+                        sel_s + (n * 2 + half) * kappa);
+      }
     }
     __syncthreads();
   }
-  for (int n = wave; n < kTok; n += kWaves) {
+  // softmax over a token's selected scores; idx, weight and score out
+  auto emit = [&](int n, uint64_t k) {
     const int r = r0 + n;
-    if (r >= BT) continue;
-    const int16_t* i1 = sel_i + (n * 2 + 0) * kappa;
-    const int16_t* i2 = sel_i + (n * 2 + 1) * kappa;
-    const float* s1 = sel_s + (n * 2 + 0) * kappa;
-    const float* s2 = sel_s + (n * 2 + 1) * kappa;
-    uint64_t k = merge_token<EM>(i1, s1, i2, s2, s, kappa, A.n_sel, pr, bdiv, wbuf);
+    if (r >= BT) return;
     float scv = lane < A.n_sel ? key_score(k) : -INFINITY;
     float mx = __shfl(scv, 0, kWave);
     float e = lane < A.n_sel ? expf(scv - mx) : 0.f;
@@ -195,6 +206,23 @@ __global__ void __launch_bounds__(kThreads, 4) address_kernel(AddrArgs A) {
       A.idx[o + lane] = (int32_t)key_index(k);
       A.weight[o + lane] = e / tot;
       if (A.score) A.score[o + lane] = scv;
+    }
+  };
+  auto sel = [&](int n, int h) { return sel_i + (n * 2 + h) * kappa; };
+  auto sco = [&](int n, int h) { return sel_s + (n * 2 + h) * kappa; };
+  if (pair) {
+    for (int n = wave; n < kTok; n += 2 * kWaves) {
+      const int m = n + kWaves;
+      uint64_t ka, kb;
+      merge_token_x2<EM>(sel(n, 0), sco(n, 0), sel(n, 1), sco(n, 1), sel(m, 0), sco(m, 0), sel(m, 1), sco(m, 1), s,
+                         kappa, A.n_sel, pr, bdiv, rowbuf(n), rowbuf(m), &ka, &kb);
+      emit(n, ka);
+      emit(m, kb);
+    }
+  } else {
+    for (int n = wave; n < kTok; n += kWaves) {
+      if (r0 + n >= BT) continue;
+      emit(n, merge_token<EM>(sel(n, 0), sco(n, 0), sel(n, 1), sco(n, 1), s, kappa, A.n_sel, pr, bdiv, wbuf));
     }
   }
 }

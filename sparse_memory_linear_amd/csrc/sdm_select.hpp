@@ -97,6 +97,31 @@ __device__ __forceinline__ void wave_sort_desc_f32_payload(float& s, uint32_t& p
   });
 }
 
+// Two independent sorts in one pass: each step exchanges and compares both, so one chain's
+// dependent instructions fill the other's latency.
+__device__ __forceinline__ void wave_sort_desc_f32x2(float& a, float& b) {
+  const int lane = lane_id();
+  bitonic_desc([&](int m, int bit) {
+    const float oa = xchg_f32(a, m), ob = xchg_f32(b, m);
+    const bool lower = (lane & bit) == 0;
+    a = ((a > oa) == lower) ? a : oa;
+    b = ((b > ob) == lower) ? b : ob;
+  });
+}
+__device__ __forceinline__ void wave_sort_desc_f32_payload2(float& s0, uint32_t& p0, float& s1, uint32_t& p1) {
+  const int lane = lane_id();
+  bitonic_desc([&](int m, int bit) {
+    const float o0 = xchg_f32(s0, m), o1 = xchg_f32(s1, m);
+    const uint32_t q0 = xchg_u32(p0, m), q1 = xchg_u32(p1, m);
+    const bool lower = (lane & bit) == 0;
+    const bool k0 = (s0 > o0) == lower, k1 = (s1 > o1) == lower;
+    s0 = k0 ? s0 : o0;
+    p0 = k0 ? p0 : q0;
+    s1 = k1 ? s1 : o1;
+    p1 = k1 ? p1 : q1;
+  });
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -195,6 +220,78 @@ __device__ __forceinline__ void wave_topk_f32(const float (&sc)[E], const uint32
 }
 
 
+// Two independent top-`count` selections (as wave_topk_f32) in one wave, their threshold
+// sorts, compactions and candidate sorts interleaved. Results equal two calls of
+// wave_topk_f32; a selection whose candidates do not fit the fast path is redone by it.
+// bufa and bufb are 64 words of LDS each, private to the calling wave.
+template <int E>
+__device__ __forceinline__ void wave_topk_f32_x2(const float (&sa)[E], const uint32_t (&ia)[E], const float (&sb)[E],
+                                                 const uint32_t (&ib)[E], int count, uint64_t* bufa, uint64_t* bufb,
+                                                 float* oa_s, uint32_t* oa_i, float* ob_s, uint32_t* ob_i) {
+  const int lane = lane_id();
+  const uint64_t none = (0xFFFFFFFFull << 32) | (uint64_t)__float_as_uint(-INFINITY);
+  uint64_t ma, mb;  // this lane's candidate of each selection, (index << 32) | score bits
+  int na, nb;       // candidates of each selection
+  if constexpr (E == 1) {
+    ma = sa[0] > -INFINITY ? ((uint64_t)ia[0] << 32) | __float_as_uint(sa[0]) : none;
+    mb = sb[0] > -INFINITY ? ((uint64_t)ib[0] << 32) | __float_as_uint(sb[0]) : none;
+    na = nb = kWave;
+  } else {
+    float xa = sa[0], xb = sb[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) {
+      xa = fmaxf(xa, sa[e]);
+      xb = fmaxf(xb, sb[e]);
+    }
+    wave_sort_desc_f32x2(xa, xb);
+    const float ta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xa), count - 1));
+    const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xb), count - 1));
+    // compaction, optimistic: positions past 64 are not written, and such a selection is
+    // redone below
+    na = nb = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ca = sa[e] >= ta, cb = sb[e] >= tb;
+      const uint64_t ka = ballot(ca), kb = ballot(cb);
+      const int qa = na + mbcnt(ka), qb = nb + mbcnt(kb);
+      if (ca && qa < kWave) bufa[qa] = ((uint64_t)ia[e] << 32) | (uint64_t)__float_as_uint(sa[e]);
+      if (cb && qb < kWave) bufb[qb] = ((uint64_t)ib[e] << 32) | (uint64_t)__float_as_uint(sb[e]);
+      na += popc64(ka);
+      nb += popc64(kb);
+    }
+    if (!(ta > -INFINITY && na <= kWave && tb > -INFINITY && nb <= kWave)) {
+      wave_topk_f32<E>(sa, ia, count, bufa, oa_s, oa_i);
+      wave_topk_f32<E>(sb, ib, count, bufb, ob_s, ob_i);
+      return;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    ma = lane < na ? bufa[lane] : none;
+    mb = lane < nb ? bufb[lane] : none;
+    __builtin_amdgcn_wave_barrier();
+  }
+  float s0 = __uint_as_float((uint32_t)ma), s1 = __uint_as_float((uint32_t)mb);
+  uint32_t p0 = (uint32_t)(ma >> 32), p1 = (uint32_t)(mb >> 32);
+  wave_sort_desc_f32_payload2(s0, p0, s1, p1);
+  const float n0 = __shfl_down(s0, 1, kWave), n1 = __shfl_down(s1, 1, kWave);
+  const bool ok = lane < count && lane < kWave - 1;
+  *oa_s = s0;
+  *oa_i = p0;
+  *ob_s = s1;
+  *ob_i = p1;
+  // equal neighbours up to rank `count`: that selection's order is redone on exact keys
+  if (ballot(ok && s0 == n0)) {
+    const uint64_t key = wave_sort_desc_u64(ma != none ? rank_key(__uint_as_float((uint32_t)ma), (uint32_t)(ma >> 32)) : 0ull);
+    *oa_s = key_score(key);
+    *oa_i = key_index(key);
+  }
+  if (ballot(ok && s1 == n1)) {
+    const uint64_t key = wave_sort_desc_u64(mb != none ? rank_key(__uint_as_float((uint32_t)mb), (uint32_t)(mb >> 32)) : 0ull);
+    *ob_s = key_score(key);
+    *ob_i = key_index(key);
+  }
+}
+
 // ---------------------------------------------------------------- per-half selection
 // Top-kappa sub-keys of one token-half: lanes < kappa receive (index, score) in rank order.
 // Score i of the row sits at row[i ^ swz] (swz < 32 permutes within aligned groups of 32).
@@ -218,6 +315,34 @@ __device__ __forceinline__ void select_half(const float* row, int swz, int s, in
   if (lane < kappa) {
     out_idx[lane] = (int16_t)ti;
     out_sc[lane] = ts;
+  }
+}
+
+// Two token-halves in one wave (as two select_half calls), their selections interleaved.
+template <int E>
+__device__ __forceinline__ void select_half_x2(const float* rowa, int swza, const float* rowb, int swzb, int s, int kappa,
+                                               uint64_t* bufa, uint64_t* bufb, int16_t* oia, float* osa, int16_t* oib,
+                                               float* osb) {
+  const int lane = lane_id();
+  const float* ra = rowa + (lane ^ swza);
+  const float* rb = rowb + (lane ^ swzb);
+  float sa[E], sb[E];
+  uint32_t ix[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + kWave * e;
+    sa[e] = i < s ? ra[kWave * e] : -INFINITY;
+    sb[e] = i < s ? rb[kWave * e] : -INFINITY;
+    ix[e] = (uint32_t)i;
+  }
+  float ta, tb;
+  uint32_t ja, jb;
+  wave_topk_f32_x2<E>(sa, ix, sb, ix, kappa, bufa, bufb, &ta, &ja, &tb, &jb);
+  if (lane < kappa) {
+    oia[lane] = (int16_t)ja;
+    osa[lane] = ta;
+    oib[lane] = (int16_t)jb;
+    osb[lane] = tb;
   }
 }
 
@@ -257,6 +382,25 @@ __device__ __forceinline__ uint64_t cand_key(const int16_t* i1, const float* s1,
   return rank_key(sc, slot);
 }
 
+// Exact top n_sel of all kappa^2 pairs, extracted largest first: lanes < n_sel get their key.
+__device__ __forceinline__ uint64_t merge_exact(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2,
+                                                int s, int kappa, int n_sel) {
+  const int lane = lane_id();
+  const int all = kappa * kappa;
+  uint64_t out = 0ull, prev = ~0ull;
+  for (int i = 0; i < n_sel; ++i) {
+    uint64_t m = 0ull;
+    for (int p = lane; p < all; p += kWave) {
+      uint64_t k = cand_key(i1, s1, i2, s2, p / kappa, p % kappa, s);
+      if (k < prev && k > m) m = k;
+    }
+    uint64_t g = wave_max_u64(m);
+    if (lane == i) out = g;
+    prev = g;
+  }
+  return out;
+}
+
 // Top n_sel of the kappa x kappa candidates for one token: lanes < n_sel get their key.
 template <int EM>
 __device__ __forceinline__ uint64_t merge_token(const int16_t* i1, const float* s1, const int16_t* i2, const float* s2, int s,
@@ -283,21 +427,38 @@ __device__ __forceinline__ uint64_t merge_token(const int16_t* i1, const float* 
   const float tau_score = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ts), n_sel - 1));
   bool viol = false;
   if (lane < kappa && bdiv < kappa && s1[lane] + s2[bdiv] >= tau_score) viol = true;
-  const int all = kappa * kappa;
   if (ballot(viol) == 0ull) return top;
-  // 3. exact extraction over all kappa^2 pairs, largest first
-  uint64_t out = 0ull, prev = ~0ull;
-  for (int i = 0; i < n_sel; ++i) {
-    uint64_t m = 0ull;
-    for (int p = lane; p < all; p += kWave) {
-      uint64_t k = cand_key(i1, s1, i2, s2, p / kappa, p % kappa, s);
-      if (k < prev && k > m) m = k;
-    }
-    uint64_t g = wave_max_u64(m);
-    if (lane == i) out = g;
-    prev = g;
+  return merge_exact(i1, s1, i2, s2, s, kappa, n_sel);
+}
+
+// Two tokens' merges in one wave (as two merge_token calls), their selections interleaved.
+template <int EM>
+__device__ __forceinline__ void merge_token_x2(const int16_t* i1a, const float* s1a, const int16_t* i2a,
+                                               const float* s2a, const int16_t* i1b, const float* s1b,
+                                               const int16_t* i2b, const float* s2b, int s, int kappa, int n_sel,
+                                               const int (&pr)[EM], int bdiv, uint64_t* bufa, uint64_t* bufb,
+                                               uint64_t* ka, uint64_t* kb) {
+  const int lane = lane_id();
+  float sa[EM], sb[EM];
+  uint32_t xa[EM], xb[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    const int a = pr[e] >> 8, b = pr[e] & 255;
+    sa[e] = pr[e] >= 0 ? s1a[a] + s2a[b] : -INFINITY;
+    sb[e] = pr[e] >= 0 ? s1b[a] + s2b[b] : -INFINITY;
+    xa[e] = pr[e] >= 0 ? (uint32_t)i1a[a] * (uint32_t)s + (uint32_t)i2a[b] : 0xFFFFFFFFu;
+    xb[e] = pr[e] >= 0 ? (uint32_t)i1b[a] * (uint32_t)s + (uint32_t)i2b[b] : 0xFFFFFFFFu;
   }
-  return out;
+  float ta, tb;
+  uint32_t ja, jb;
+  wave_topk_f32_x2<EM>(sa, xa, sb, xb, n_sel, bufa, bufb, &ta, &ja, &tb, &jb);
+  *ka = lane < n_sel ? rank_key(ta, ja) : 0ull;
+  *kb = lane < n_sel ? rank_key(tb, jb) : 0ull;
+  const float tua = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ta), n_sel - 1));
+  const float tub = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tb), n_sel - 1));
+  const bool row = lane < kappa && bdiv < kappa;
+  if (ballot(row && s1a[lane] + s2a[bdiv] >= tua)) *ka = merge_exact(i1a, s1a, i2a, s2a, s, kappa, n_sel);
+  if (ballot(row && s1b[lane] + s2b[bdiv] >= tub)) *kb = merge_exact(i1b, s1b, i2b, s2b, s, kappa, n_sel);
 }
 
 }  // namespace sdm
